@@ -1,0 +1,144 @@
+/*
+ * libattn.h -- C ABI of libattn, multi-head scaled-dot-product self-attention
+ * (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For a GPT-2 style packed input qkv of shape (B, T, 3C)
+ * split into NH heads of size hs = C/NH, every head (b, h) and query row t
+ * attends to the key set U(t) = {0..t} (causal) or {0..T-1} (non-causal):
+ *
+ *     s[t,j]   = q_t . k_j                              (unscaled dot product)
+ *     att[t,j] = exp(scale*s[t,j]) / sum_{j' in U(t)} exp(scale*s[t,j'])
+ *     out_t    = sum_{j in U(t)} att[t,j] v_j,         scale = 1/sqrt(hs)
+ *
+ * This is Scores = Q K^T / sqrt(d_k), a softmax per row and a product with V
+ * ("Umakini wa kujitegemea, kerneli za CUDA na FlashAttention", section 1),
+ * with the causal row set, the packed layout and the unscaled preatt of the
+ * CPU references attention_forward_cpu / attention_backward_cpu in llm.c
+ * dev/cuda/attention_backward.cu.  The fused entry points never form the
+ * T x T matrices: they tile Q, K, V through on-chip memory with a running
+ * (online) softmax and keep only a per-row log-sum-exp, which the backward
+ * uses to recompute the probabilities (the FlashAttention part of the same
+ * page).  The backward is the analytic one of attention_backward_cpu, with
+ * the closed-form softmax gradient of softmax_autoregressive_backward_kernel7
+ * in attention_backward.cu:
+ *
+ *     dpreatt[t,j] = scale * att[t,j] * (datt[t,j] - D[t]),
+ *     D[t] = sum_j att[t,j] datt[t,j] = dout_t . out_t,  datt[t,j] = dout_t . v_j
+ *     dq_t = sum_j dpreatt[t,j] k_j,  dk_j = sum_t dpreatt[t,j] q_t,
+ *     dv_j = sum_t att[t,j] dout_t.
+ *
+ * Layouts (all row-major, contiguous, element strides implied by the shape):
+ *     qkv, dqkv   (B, T, 3C): q at [b,t,h*hs+i], k at [b,t,C+h*hs+i],
+ *                             v at [b,t,2C+h*hs+i]
+ *     out, dout   (B, T, C) : [b,t,h*hs+i]
+ *     lse         (B, NH, T): float, natural log, scaled domain:
+ *                             lse = log sum_{j in U(t)} exp(scale*s[t,j])
+ *     preatt, att, datt, dpreatt (B, NH, T, T): float
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer on the current HIP
+ * device, 16-byte aligned, owned by the caller; libattn never frees it.
+ * bf16 tensors are passed as uint16_t bit patterns (bfloat16, round to
+ * nearest even on output).  Outputs are overwritten (=), never accumulated.
+ * An output may not overlap any input or another output.
+ *
+ * Streams.  Calls enqueue work on the calling thread's libattn stream
+ * (attn_set_stream; default: the null stream) and return without waiting.
+ * Results are deterministic: no atomics, fixed reduction order.
+ *
+ * Workspace.  attn_backward* needs B*NH*T floats of scratch for D; libattn
+ * keeps one grow-only buffer per device, allocated with hipMalloc on first
+ * need, and frees it in attn_release().  With the environment variable
+ * ATTN_TEST_FAIL_ALLOC=1 that allocation fails (ATTN_EHIP) before any HIP
+ * call, so callers can test their error handling on any host.
+ *
+ * Errors.  Every int-returning call returns ATTN_OK or a negative status and
+ * records a message for attn_last_error().  Argument checks run before any
+ * HIP call, so ATTN_EINVAL / ATTN_EUNSUPPORTED never touch the device.
+ * libattn never prints and never exits.
+ */
+#ifndef LIBATTN_H
+#define LIBATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+/* null pointer, B/T/NH < 1, C < NH, C % NH != 0, causal not 0/1, misaligned
+ * or overlapping buffers, or a tensor too large for 32-bit in-batch offsets
+ * (T*3C >= 2^31, or T*T >= 2^31 for the materialised calls) */
+#define ATTN_EINVAL (-1)
+/* head size hs = C/NH not in {16, 32, 64, 128} */
+#define ATTN_EUNSUPPORTED (-2)
+/* a HIP call (workspace allocation, kernel launch) failed */
+#define ATTN_EHIP (-3)
+
+/*
+ * Fused forward, fp32.  Writes out (B,T,C) and lse (B,NH,T).
+ * causal = 1 masks keys j > t; causal = 0 attends to every key.
+ */
+int attn_forward(float* out, float* lse, const float* qkv,
+                 int B, int T, int C, int NH, int causal);
+
+/*
+ * Fused backward, fp32.  Reads dout (B,T,C), qkv, and the forward's out and
+ * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  Runs a D = rowsum(dout*out)
+ * pre-pass, a dK/dV kernel and a dQ kernel, all recomputing the
+ * probabilities from lse.
+ */
+int attn_backward(float* dqkv, const float* dout, const float* qkv,
+                  const float* out, const float* lse,
+                  int B, int T, int C, int NH, int causal);
+
+/*
+ * Fused forward and backward with bfloat16 inputs and outputs and fp32
+ * accumulation (the mixed-precision scheme of "LLM Systems 10 & 11:
+ * Accelerating Transformer Training and Inference", section 1: low-precision
+ * operands, higher-precision accumulation).  lse stays fp32.  Probabilities
+ * and dS are rounded to bf16 only as matrix-core operands.
+ */
+int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv,
+                      int B, int T, int C, int NH, int causal);
+int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                       const uint16_t* out, const float* lse,
+                       int B, int T, int C, int NH, int causal);
+
+/*
+ * Materialised forward, fp32, as the pages' reference does it: writes the
+ * full unscaled preatt = q.k (B,NH,T,T) including masked entries, att
+ * (B,NH,T,T) with masked entries exactly 0, and out (B,T,C).
+ * (llm.c attention_backward.cu: attention_forward_cpu and the
+ * permute / sgemm / softmax / sgemm / unpermute GPU sequence.)
+ */
+int attn_forward_materialized(float* out, float* preatt, float* att, const float* qkv,
+                              int B, int T, int C, int NH, int causal);
+
+/*
+ * Materialised backward, fp32, from the forward's att: writes datt = dout.v
+ * (dense, every (t,j)), dpreatt (exactly 0 on masked entries) and dqkv.
+ * (llm.c attention_backward.cu: attention_backward_cpu and
+ * softmax_autoregressive_backward_kernel7.)
+ */
+int attn_backward_materialized(float* dqkv, float* dpreatt, float* datt,
+                               const float* dout, const float* qkv, const float* att,
+                               int B, int T, int C, int NH, int causal);
+
+/* Set the HIP stream (a hipStream_t, or NULL for the null stream) used by
+ * the calling thread's subsequent calls.  Always returns ATTN_OK. */
+int attn_set_stream(void* hip_stream);
+
+/* Message describing the calling thread's last non-OK status ("" if none).
+ * The string stays valid until the thread's next libattn call. */
+const char* attn_last_error(void);
+
+/* Free the backward workspace on every device it was allocated on.  Must
+ * not race with work still queued that uses it (synchronise first). */
+void attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_H */

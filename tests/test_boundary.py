@@ -1,0 +1,148 @@
+"""The C ABI of libattn on a host without a GPU: the library loads, exports
+every entry point its header declares, and rejects bad arguments with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_causal_head_attn_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_header_compiles_as_c():
+    src = '#include "libattn.h"\nint main(void){return attn_set_stream(0);}\n'
+    res = subprocess.run(["gcc", "-fsyntax-only", "-std=c99", "-Wall", "-Werror",
+                          "-I", os.path.dirname(HEADER), "-x", "c", "-"],
+                         input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+# Fake, aligned, non-overlapping addresses: argument checks never dereference
+# them, and every case below is rejected before any HIP call.
+BASE = 1 << 40
+STEP = 1 << 36
+
+
+def ptrs(n):
+    return [ctypes.c_void_p(BASE + i * STEP) for i in range(n)]
+
+
+def call(name, nptr, B, T, C, NH, causal, override=None):
+    lib = la.load()
+    p = ptrs(nptr)
+    if override:
+        for i, v in override.items():
+            p[i] = ctypes.c_void_p(v)
+    rc = getattr(lib, name)(*p, B, T, C, NH, causal)
+    return rc, lib.attn_last_error().decode()
+
+
+ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_forward_bf16", 3),
+         ("attn_backward_bf16", 5), ("attn_forward_materialized", 4),
+         ("attn_backward_materialized", 6)]
+
+
+@pytest.mark.parametrize("name,nptr", ENTRY)
+@pytest.mark.parametrize("dims,code", [
+    ((0, 64, 64, 4, 1), la.ATTN_EINVAL),       # B < 1
+    ((1, 0, 64, 4, 1), la.ATTN_EINVAL),        # T < 1
+    ((1, 64, 64, 0, 1), la.ATTN_EINVAL),       # NH < 1
+    ((1, 64, 3, 4, 1), la.ATTN_EINVAL),        # C < NH
+    ((1, 64, 66, 4, 1), la.ATTN_EINVAL),       # C % NH != 0
+    ((1, 64, 64, 4, 2), la.ATTN_EINVAL),       # causal not 0/1
+    ((1, 64, 64, 4, -1), la.ATTN_EINVAL),
+    ((1, 64, 96, 4, 1), la.ATTN_EUNSUPPORTED),  # hs = 24
+    ((1, 64, 256, 1, 1), la.ATTN_EUNSUPPORTED),  # hs = 256
+    ((1, 64, 8, 1, 0), la.ATTN_EUNSUPPORTED),    # hs = 8
+])
+def test_bad_dimensions(name, nptr, dims, code):
+    rc, msg = call(name, nptr, *dims)
+    assert rc == code, msg
+    assert msg
+
+
+@pytest.mark.parametrize("name,nptr", ENTRY)
+def test_null_pointers(name, nptr):
+    for i in range(nptr):
+        rc, msg = call(name, nptr, 1, 64, 64, 4, 1, override={i: 0})
+        assert rc == la.ATTN_EINVAL and "NULL" in msg
+
+
+@pytest.mark.parametrize("name,nptr", ENTRY)
+def test_misaligned_pointer(name, nptr):
+    rc, msg = call(name, nptr, 1, 64, 64, 4, 1, override={0: BASE + 4})
+    assert rc == la.ATTN_EINVAL and "aligned" in msg
+
+
+@pytest.mark.parametrize("name,nptr", ENTRY)
+def test_output_overlapping_input(name, nptr):
+    # put the last argument (an input) 16 bytes into the first (an output)
+    rc, msg = call(name, nptr, 1, 64, 64, 4, 1, override={nptr - 1: BASE + 16})
+    assert rc == la.ATTN_EINVAL and "overlaps" in msg
+
+
+def test_too_large_for_32bit_offsets():
+    rc, msg = call("attn_forward", 3, 1, 1 << 20, 1024, 16, 1)
+    assert rc == la.ATTN_EINVAL and "32-bit" in msg
+    rc, msg = call("attn_forward_materialized", 4, 1, 1 << 16, 64, 4, 1)
+    assert rc == la.ATTN_EINVAL and "T*T" in msg
+
+
+def test_forced_workspace_failure():
+    """ATTN_TEST_FAIL_ALLOC=1 makes the backward's workspace allocation fail
+    with ATTN_EHIP before any HIP call (run in a child process so the
+    environment variable is read fresh)."""
+    code = (
+        "import ctypes, transformer_causal_head_attn_amd as la\n"
+        "lib = la.load()\n"
+        "p = [ctypes.c_void_p((1 << 40) + i * (1 << 36)) for i in range(5)]\n"
+        "rc = lib.attn_backward(*p, 1, 64, 64, 4, 1)\n"
+        "print(rc, lib.attn_last_error().decode())\n"
+    )
+    env = dict(os.environ, ATTN_TEST_FAIL_ALLOC="1", PYTHONPATH=ROOT)
+    res = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=120)
+    assert res.returncode == 0, res.stderr
+    rc, msg = res.stdout.split(" ", 1)
+    assert int(rc) == la.ATTN_EHIP and "forced" in msg
+
+
+def test_last_error_cleared_by_success():
+    lib = la.load()
+    call("attn_forward", 3, 0, 1, 1, 1, 1)
+    assert la.attn_last_error()
+    assert lib.attn_set_stream(None) == la.ATTN_OK
+    assert la.attn_last_error() == ""
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 64, 192)
+    with pytest.raises(ValueError):
+        la.forward(x, 4, True)

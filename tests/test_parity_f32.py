@@ -1,0 +1,150 @@
+"""fp32 fused path against the fp64 oracle, element by element
+(|gpu - oracle| <= 1e-5 + 1e-4 |oracle|), plus GPU-only invariants."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_close, gpu_fwd_bwd, head_view
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import transformer_causal_head_attn_amd as m
+    m.load()
+    return m
+
+
+def _case(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("key", [1, 2])
+def test_workload_full_compare(la, oracle_mod, key):
+    w = WORKLOADS[key]
+    _case(f"f32 workload {key}: {w.label()}")
+    qkv, dout = workload_inputs(w)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
+    ro, rl = oracle_mod.forward(qkv, w.NH, w.causal)
+    rd = oracle_mod.backward(qkv, dout, w.NH, w.causal)
+    assert_close(out, ro, "f32", "out")
+    assert_close(lse, rl, "f32", "lse")
+    assert_close(dqkv, rd, "f32", "dqkv")
+
+
+SHAPES = [
+    # B, T, C, NH  (hs = C/NH) -- ragged tails, several tiles, every head size
+    (1, 1, 64, 4),
+    (2, 2, 64, 1),
+    (1, 63, 128, 4),
+    (2, 65, 128, 2),
+    (1, 100, 96, 3),
+    (1, 129, 512, 4),
+    (3, 200, 64, 4),
+    (1, 333, 256, 2),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ragged_shapes(la, oracle_mod, shape, causal):
+    B, T, C, NH = shape
+    _case(f"f32 ragged B{B} T{T} C{C} NH{NH} causal={causal}")
+    qkv, dout = make_inputs(B, T, C, "f32", seed=100 + T)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, NH, causal)
+    ro, rl = oracle_mod.forward(qkv, NH, causal)
+    rd = oracle_mod.backward(qkv, dout, NH, causal)
+    assert_close(out, ro, "f32", "out")
+    assert_close(lse, rl, "f32", "lse")
+    assert_close(dqkv, rd, "f32", "dqkv")
+
+
+def test_gpt2_layer_sampled_heads(la, oracle_mod):
+    """The benchmark's workload (B8 T1024 C768 NH12, causal, fp32) in the
+    benchmark's launch configuration; the oracle runs on 4 sampled heads and
+    every element of those heads is compared."""
+    w = WORKLOADS[3]
+    _case(f"f32 workload 3 sampled heads: {w.label()}")
+    qkv, dout = workload_inputs(w)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
+    for b, h in [(0, 0), (3, 7), (5, 11), (7, 4)]:
+        qs = oracle_mod.head_slice(qkv, b, h, w.NH, packed=True)
+        ds = oracle_mod.head_slice(dout, b, h, w.NH, packed=False)
+        ro, rl = oracle_mod.forward(qs, 1, True)
+        rd = oracle_mod.backward(qs, ds, 1, True)
+        assert_close(head_view(out, b, h, w.NH, False), ro, "f32", f"out head {(b, h)}")
+        assert_close(lse[b:b + 1, h:h + 1].numpy(), rl, "f32", f"lse head {(b, h)}")
+        assert_close(head_view(dqkv, b, h, w.NH, True), rd, "f32", f"dqkv head {(b, h)}")
+
+
+def test_deterministic(la):
+    """Two runs on the same inputs are bitwise identical (no atomics)."""
+    qkv, dout = make_inputs(2, 300, 256, "f32", seed=5)
+    a = gpu_fwd_bwd(la, qkv, dout, 4, True)
+    b = gpu_fwd_bwd(la, qkv, dout, 4, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_causality(la):
+    """Changing k and v at positions >= t0 leaves out, lse and dq of rows
+    < t0 bitwise unchanged (masked probabilities are exactly 0)."""
+    B, T, C, NH = 2, 250, 256, 4
+    t0 = 97
+    qkv, dout = make_inputs(B, T, C, "f32", seed=6)
+    o1, l1, d1 = gpu_fwd_bwd(la, qkv, dout, NH, True)
+    qkv2 = qkv.clone()
+    qkv2[:, t0:, C:] = 1000.0 * torch.randn_like(qkv2[:, t0:, C:])
+    o2, l2, d2 = gpu_fwd_bwd(la, qkv2, dout, NH, True)
+    assert torch.equal(o1[:, :t0], o2[:, :t0])
+    assert torch.equal(l1[:, :, :t0], l2[:, :, :t0])
+    assert torch.equal(d1[:, :t0, :C], d2[:, :t0, :C])
+
+
+def test_first_row_and_single_token_exact(la):
+    """Causal row 0 sees only key 0, so out_0 = v_0 exactly; with T = 1
+    out = v exactly."""
+    B, T, C, NH = 2, 130, 128, 2
+    qkv, dout = make_inputs(B, T, C, "f32", seed=7)
+    out, _, _ = gpu_fwd_bwd(la, qkv, dout, NH, True)
+    assert torch.equal(out[:, 0], qkv[:, 0, 2 * C:])
+    qkv1, dout1 = make_inputs(3, 1, C, "f32", seed=8)
+    for causal in (True, False):
+        out1, _, _ = gpu_fwd_bwd(la, qkv1, dout1, NH, causal)
+        assert torch.equal(out1, qkv1[:, :, 2 * C:])
+
+
+def test_outputs_fully_overwritten(la, oracle_mod):
+    """Outputs are written with '=': NaN-filled output buffers come back
+    fully defined."""
+    B, T, C, NH = 1, 70, 64, 4
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=9)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    out = torch.full((B, T, C), float("nan"), device="cuda")
+    lse = torch.full((B, NH, T), float("nan"), device="cuda")
+    la.attn_forward(out, lse, qkv, B, T, C, NH, 1)
+    dqkv = torch.full((B, T, 3 * C), float("nan"), device="cuda")
+    la.attn_backward(dqkv, dout, qkv, out, lse, B, T, C, NH, 1)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.forward(qkv_c, NH, True)
+    assert_close(out, ro, "f32", "out")
+    assert_close(dqkv, oracle_mod.backward(qkv_c, dout_c, NH, True), "f32", "dqkv")
+
+
+def test_respects_torch_stream(la, oracle_mod):
+    """Work is enqueued on torch's current stream."""
+    B, T, C, NH = 2, 128, 128, 2
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=10)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qkv = qkv_c.to("cuda", non_blocking=False)
+        out, lse = la.forward(qkv, NH, True)
+    s.synchronize()
+    ro, _ = oracle_mod.forward(qkv_c, NH, True)
+    assert_close(out, ro, "f32", "out")

@@ -1,0 +1,14 @@
+"""libattn: multi-head scaled-dot-product self-attention, forward and
+backward, on AMD Instinct MI355X (gfx950) with hand-written HIP kernels.
+
+The compute lives in ``libattn.so`` (C ABI: ``include/libattn.h``); this
+package only builds it and marshals torch tensors into its calls.  Importing
+the package does not load the library; the first call does, and fails loudly
+if it cannot.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_OK, EXPORTS, LIB_PATH, AttnError,
+    attn_backward, attn_backward_bf16, attn_backward_materialized, attn_forward,
+    attn_forward_bf16, attn_forward_materialized, attn_last_error, attn_release,
+    attn_set_stream, backward, backward_materialized, forward, forward_materialized, load,
+)

@@ -1,0 +1,206 @@
+"""ctypes binding of libattn's C ABI (argument marshalling only).
+
+Every function named like an entry point of ``include/libattn.h`` takes torch
+tensors where the C call takes device pointers, checks that they are
+contiguous CUDA (HIP) tensors of the right dtype and size, passes
+``data_ptr()`` and torch's current stream, and raises ``AttnError`` on a
+non-zero status.  All arithmetic runs in the HIP kernels of libattn.so; there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_EHIP = -3
+
+EXPORTS = (
+    "attn_forward", "attn_backward", "attn_forward_bf16", "attn_backward_bf16",
+    "attn_forward_materialized", "attn_backward_materialized",
+    "attn_set_stream", "attn_last_error", "attn_release",
+)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libattn.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(p)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        for name, nptr in (("attn_forward", 3), ("attn_forward_bf16", 3),
+                           ("attn_backward", 5), ("attn_backward_bf16", 5),
+                           ("attn_forward_materialized", 4),
+                           ("attn_backward_materialized", 6)):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * nptr + [i] * 5
+            fn.restype = i
+        lib.attn_set_stream.argtypes = [vp]
+        lib.attn_set_stream.restype = i
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_release.argtypes = []
+        lib.attn_release.restype = None
+        _lib = lib
+        return lib
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    lib.attn_set_stream(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    rc = getattr(lib, name)(*args)
+    if rc != ATTN_OK:
+        raise AttnError(name, rc, lib.attn_last_error().decode())
+
+
+def _dims(B, T, C, NH, causal):
+    return [int(B), int(T), int(C), int(NH), int(causal)]
+
+
+# ------------------------------------------------------- C ABI, one to one --
+
+def attn_forward(out, lse, qkv, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_forward", _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(qkv, "qkv", f, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def attn_backward(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_backward", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_forward_bf16(out, lse, qkv, B, T, C, NH, causal) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_forward_bf16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(qkv, "qkv", h, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_bf16(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_backward_bf16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
+          _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_forward_materialized(out, preatt, att, qkv, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    M = B * NH * T * T
+    _call("attn_forward_materialized", _check(out, "out", f, B * T * C),
+          _check(preatt, "preatt", f, M), _check(att, "att", f, M),
+          _check(qkv, "qkv", f, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_materialized(dqkv, dpreatt, datt, dout, qkv, att, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    M = B * NH * T * T
+    _call("attn_backward_materialized", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dpreatt, "dpreatt", f, M), _check(datt, "datt", f, M),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(att, "att", f, M), *_dims(B, T, C, NH, causal))
+
+
+def attn_set_stream(stream) -> None:
+    """Set the calling thread's libattn stream (a torch.cuda.Stream, a raw
+    hipStream_t integer, or None for the null stream).  The functions above
+    set torch's current stream before every call anyway."""
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    load().attn_set_stream(ctypes.c_void_p(stream or 0))
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def attn_release() -> None:
+    load().attn_release()
+
+
+# ---------------------------------------------------- allocating helpers --
+
+def _shape(qkv: torch.Tensor, NH: int):
+    if qkv.dim() != 3 or qkv.shape[2] % 3:
+        raise ValueError(f"qkv must be (B, T, 3C), got {tuple(qkv.shape)}")
+    B, T, C3 = qkv.shape
+    return B, T, C3 // 3
+
+
+def forward(qkv: torch.Tensor, NH: int, causal: bool = True):
+    """Allocate (out, lse) with torch and run the fused forward (fp32 or
+    bf16 by qkv's dtype)."""
+    B, T, C = _shape(qkv, NH)
+    out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
+    fn = attn_forward_bf16 if qkv.dtype == torch.bfloat16 else attn_forward
+    fn(out, lse, qkv, B, T, C, NH, int(causal))
+    return out, lse
+
+
+def backward(dout, qkv, out, lse, NH: int, causal: bool = True):
+    """Allocate dqkv with torch and run the fused backward."""
+    B, T, C = _shape(qkv, NH)
+    dqkv = torch.empty_like(qkv)
+    fn = attn_backward_bf16 if qkv.dtype == torch.bfloat16 else attn_backward
+    fn(dqkv, dout, qkv, out, lse, B, T, C, NH, int(causal))
+    return dqkv
+
+
+def forward_materialized(qkv: torch.Tensor, NH: int, causal: bool = True):
+    B, T, C = _shape(qkv, NH)
+    out = torch.empty((B, T, C), dtype=torch.float32, device=qkv.device)
+    pre = torch.empty((B, NH, T, T), dtype=torch.float32, device=qkv.device)
+    att = torch.empty_like(pre)
+    attn_forward_materialized(out, pre, att, qkv, B, T, C, NH, int(causal))
+    return out, pre, att
+
+
+def backward_materialized(dout, qkv, att, NH: int, causal: bool = True):
+    B, T, C = _shape(qkv, NH)
+    dqkv = torch.empty_like(qkv)
+    dpre = torch.empty_like(att)
+    datt = torch.empty_like(att)
+    attn_backward_materialized(dqkv, dpre, datt, dout, qkv, att, B, T, C, NH, int(causal))
+    return dqkv, dpre, datt

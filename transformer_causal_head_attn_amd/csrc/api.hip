@@ -1,0 +1,256 @@
+// api.hip -- the C ABI of libattn: argument checks, per-thread stream and
+// error state, the per-device backward workspace, and dispatch to the
+// kernel launchers.  Declarations and semantics: include/libattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/libattn.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local hipStream_t g_stream = nullptr;
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+// A byte range [p, p + n) of one tensor argument.
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Checks shared by every entry point.  `outs` must not overlap each other or
+// any of `ins`.  `mat` adds the T*T limit of the materialised calls.
+int check_args(int B, int T, int C, int NH, int causal, const Span* outs, int nout,
+               const Span* ins, int nin, bool mat) {
+    for (int i = 0; i < nout; ++i)
+        if (!outs[i].p) return fail(ATTN_EINVAL, "%s is NULL", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if (!ins[i].p) return fail(ATTN_EINVAL, "%s is NULL", ins[i].name);
+    if (B < 1 || T < 1 || NH < 1)
+        return fail(ATTN_EINVAL, "B, T and NH must be >= 1 (got B=%d T=%d NH=%d)", B, T, NH);
+    if (C < NH || C % NH != 0)
+        return fail(ATTN_EINVAL, "C=%d must be a positive multiple of NH=%d", C, NH);
+    if (causal != 0 && causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+    if ((long long)T * 3 * C >= (1LL << 31))
+        return fail(ATTN_EINVAL, "T*3C = %lld exceeds the 32-bit in-batch offset range",
+                    (long long)T * 3 * C);
+    if (mat && (long long)T * T >= (1LL << 31))
+        return fail(ATTN_EINVAL, "T*T = %lld exceeds the 32-bit offset range", (long long)T * T);
+    if ((long long)B * NH * (long long)((T + 63) / 64) >= (1LL << 31))
+        return fail(ATTN_EINVAL, "too many tiles for one launch");
+    for (int i = 0; i < nout; ++i)
+        if ((uintptr_t)outs[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if ((uintptr_t)ins[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", ins[i].name);
+    for (int i = 0; i < nout; ++i) {
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(ATTN_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(ATTN_EINVAL, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    }
+    const int hs = C / NH;
+    if (hs != 16 && hs != 32 && hs != 64 && hs != 128)
+        return fail(ATTN_EUNSUPPORTED, "head size C/NH = %d is not one of 16, 32, 64, 128", hs);
+    return ATTN_OK;
+}
+
+attn::Shape shape_of(int B, int T, int C, int NH, int causal) {
+    attn::Shape s;
+    s.B = B;
+    s.T = T;
+    s.C = C;
+    s.NH = NH;
+    s.hs = C / NH;
+    s.causal = causal;
+    return s;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---- per-device grow-only workspace (D for the backward) ----
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+void* g_ws_ptr[kMaxDevices] = {};
+size_t g_ws_bytes[kMaxDevices] = {};
+
+int workspace(size_t bytes, float** out) {
+    // ATTN_TEST_FAIL_ALLOC=1 makes the allocation fail before any HIP call,
+    // so the error path can be exercised on a host without a GPU.
+    const char* forced = getenv("ATTN_TEST_FAIL_ALLOC");
+    if (forced && forced[0] == '1') return fail(ATTN_EHIP, "workspace allocation failed (forced)");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EHIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (g_ws_bytes[dev] < bytes) {
+        if (g_ws_ptr[dev]) {
+            // the old buffer may still be read by queued work on any stream
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail(ATTN_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(g_ws_ptr[dev]);
+            g_ws_ptr[dev] = nullptr;
+            g_ws_bytes[dev] = 0;
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return fail(ATTN_EHIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+        g_ws_ptr[dev] = p;
+        g_ws_bytes[dev] = bytes;
+    }
+    *out = (float*)g_ws_ptr[dev];
+    return ATTN_OK;
+}
+
+size_t nbytes(long long elems, size_t elem) { return (size_t)elems * elem; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_set_stream(void* hip_stream) {
+    g_stream = (hipStream_t)hip_stream;
+    return ok();
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+void attn_release(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (!g_ws_ptr[d]) continue;
+        if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws_ptr[d]);
+        g_ws_ptr[d] = nullptr;
+        g_ws_bytes[d] = 0;
+    }
+    if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+int attn_forward(float* out, float* lse, const float* qkv, int B, int T, int C, int NH,
+                 int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, 4), "out"}, {lse, nbytes(BT * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 4), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    return launched(attn::launch_fwd_f32(out, lse, qkv, shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_forward launch");
+}
+
+int attn_backward(float* dqkv, const float* dout, const float* qkv, const float* out,
+                  const float* lse, int B, int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {out, nbytes(BT * C, 4), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    float* D = nullptr;
+    rc = workspace(nbytes(BT * NH, 4), &D);
+    if (rc) return rc;
+    return launched(attn::launch_bwd_f32(dqkv, dout, qkv, out, lse, D,
+                                         shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_backward launch");
+}
+
+int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C, int NH,
+                      int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, 2), "out"}, {lse, nbytes(BT * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 2), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    return launched(attn::launch_fwd_bf16(out, lse, qkv, shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_forward_bf16 launch");
+}
+
+int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                       const uint16_t* out, const float* lse, int B, int T, int C, int NH,
+                       int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {out, nbytes(BT * C, 2), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    float* D = nullptr;
+    rc = workspace(nbytes(BT * NH, 4), &D);
+    if (rc) return rc;
+    return launched(attn::launch_bwd_bf16(dqkv, dout, qkv, out, lse, D,
+                                          shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_backward_bf16 launch");
+}
+
+int attn_forward_materialized(float* out, float* preatt, float* att, const float* qkv, int B,
+                              int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const long long M = (long long)B * NH * T * T;
+    const Span outs[] = {{out, nbytes(BT * C, 4), "out"},
+                         {preatt, nbytes(M, 4), "preatt"},
+                         {att, nbytes(M, 4), "att"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 4), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 3, ins, 1, true);
+    if (rc) return rc;
+    return launched(attn::launch_fwd_materialized(out, preatt, att, qkv,
+                                                  shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_forward_materialized launch");
+}
+
+int attn_backward_materialized(float* dqkv, float* dpreatt, float* datt, const float* dout,
+                               const float* qkv, const float* att, int B, int T, int C, int NH,
+                               int causal) {
+    const long long BT = (long long)B * T;
+    const long long M = (long long)B * NH * T * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"},
+                         {dpreatt, nbytes(M, 4), "dpreatt"},
+                         {datt, nbytes(M, 4), "datt"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {att, nbytes(M, 4), "att"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 3, ins, 3, true);
+    if (rc) return rc;
+    float* D = nullptr;
+    rc = workspace(nbytes((long long)B * NH * T, 4), &D);
+    if (rc) return rc;
+    return launched(attn::launch_bwd_materialized(dqkv, dpreatt, datt, dout, qkv, att, D,
+                                                  shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_backward_materialized launch");
+}
+
+}  // extern "C"

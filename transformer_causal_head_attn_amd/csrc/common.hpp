@@ -1,0 +1,86 @@
+// common.hpp -- shared device helpers and internal launcher declarations
+// for libattn (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Problem description handed from the C ABI to the launchers.
+struct Shape {
+    int B, T, C, NH, hs;
+    int causal;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Wave64 lane exchange across the four 16-lane groups (xor 16, xor 32).
+__device__ __forceinline__ float xor_lanes(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+// Maximum / sum over the four lanes l, l^16, l^32, l^48 that share l % 16.
+__device__ __forceinline__ float group4_max(float x) {
+    x = fmaxf(x, xor_lanes(x, 16));
+    x = fmaxf(x, xor_lanes(x, 32));
+    return x;
+}
+__device__ __forceinline__ float group4_sum(float x) {
+    x += xor_lanes(x, 16);
+    x += xor_lanes(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// D += A * B on the fp32 matrix cores, one 16x16 output block per wave.
+// Lane l supplies A[l%16][l/16] and B[l/16][l%16] (K = 4); the result
+// register i of lane l is D[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// D += A * B with bf16 operands (K = 32), fp32 accumulate.  Lane l supplies
+// eight k-entries of row l%16 of A and eight of column l%16 of B; entry e of
+// lane group g = l/16 stands for k = 8g + e.  Only the pairing of A's and B's
+// k-slots matters for the sum, so any k numbering shared by both operands
+// gives the same product.  The result layout is that of mfma_f32.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 <-> fp32 (round to nearest even; NaN kept quiet).
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+    return __uint_as_float(((uint32_t)u) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_fwd_f32(float* out, float* lse, const float* qkv, const Shape& s, hipStream_t st);
+hipError_t launch_bwd_f32(float* dqkv, const float* dout, const float* qkv, const float* out,
+                          const float* lse, float* Dws, const Shape& s, hipStream_t st);
+hipError_t launch_fwd_bf16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
+                           hipStream_t st);
+hipError_t launch_bwd_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                           const uint16_t* out, const float* lse, float* Dws, const Shape& s,
+                           hipStream_t st);
+hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
+                                   const Shape& s, hipStream_t st);
+hipError_t launch_bwd_materialized(float* dqkv, float* dpreatt, float* datt, const float* dout,
+                                   const float* qkv, const float* att, float* Dws, const Shape& s,
+                                   hipStream_t st);
+
+}  // namespace attn

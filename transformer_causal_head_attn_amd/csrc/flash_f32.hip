@@ -1,0 +1,503 @@
+// flash_f32.hip -- fused fp32 attention forward and backward for gfx950.
+//
+// Method: multi-head self-attention softmax(Q K^T / sqrt(hs)) V per head
+// ("Umakini wa kujitegemea, kerneli za CUDA na FlashAttention", section 1),
+// computed tile by tile with a running row maximum and normaliser so the
+// T x T score matrix never leaves the chip, keeping only the per-row
+// log-sum-exp for the backward, which recomputes the probabilities (the
+// FlashAttention part of that page).  The backward is the analytic gradient
+// of attention_backward_cpu in llm.c dev/cuda/attention_backward.cu with
+// the closed-form softmax step of its softmax_autoregressive_backward_kernel7
+// (dS = P * (dP - D), D = rowsum(P * dP) = rowsum(dO * O)).
+//
+// gfx950 mapping (wave64, v_mfma_f32_16x16x4_f32):
+//  * a workgroup is 4 waves; each wave owns 16 rows of the 64-row tile it
+//    keeps in registers (Q rows in the forward and dQ kernels, K/V rows in
+//    the dK/dV kernel) and streams the other operand through LDS in 64-row
+//    tiles read straight from the packed (B,T,3C) tensor (no permute pass);
+//  * products are arranged so that the score block lands with one query per
+//    lane column (S^T = K Q^T in the forward / dQ kernel): a lane then holds
+//    16 scores of its own row, row statistics need only an in-lane reduction
+//    plus two cross-lane exchanges (xor 16, xor 32), and the probabilities
+//    feed the next product (O^T = V^T P^T) straight from the accumulator
+//    registers;
+//  * the contraction index k of every Q.K product is numbered
+//    k = (hs/4)*g + s for lane group g and step s, so each lane's operand
+//    values are contiguous and move with 16-byte loads;
+//  * causal work skips every key tile beyond the diagonal; workgroups are
+//    issued heaviest tile first so the causal tail does not idle CUs, and
+//    consecutive workgroup ids walk the heads so that all tiles of a head
+//    land on one XCD (one L2) whenever B*NH is a multiple of 8.
+#include "common.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kTile = 64;      // rows per Q tile and per K/V tile
+constexpr int kThreads = 256;  // 4 waves
+
+struct Lane {
+    int tid, w, l, r16, g;
+    __device__ Lane() {
+        tid = threadIdx.x;
+        w = tid >> 6;
+        l = tid & 63;
+        r16 = l & 15;
+        g = l >> 4;
+    }
+};
+
+// Copy a kTile x HS fp32 tile (rows row0.., row stride `ld` floats) from
+// global memory into LDS (row stride LDK), zero-filling rows >= T.
+template <int HS, int LDK>
+__device__ __forceinline__ void load_tile_f32(float* lds, const float* base, size_t ld,
+                                              int row0, int T, int tid) {
+    constexpr int C4 = HS / 4;
+#pragma unroll
+    for (int e = tid; e < kTile * C4; e += kThreads) {
+        const int row = e / C4, c4 = e % C4;
+        const int j = row0 + row;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < T) v = *reinterpret_cast<const float4*>(base + (size_t)j * ld + 4 * c4);
+        *reinterpret_cast<float4*>(lds + row * LDK + 4 * c4) = v;
+    }
+}
+
+// Load this lane's HS/4 contiguous values of one row (k = (HS/4)*g + s).
+template <int HS>
+__device__ __forceinline__ void load_row_part(float (&r)[HS / 4], const float* rowp, bool valid,
+                                              int g) {
+    constexpr int KS = HS / 4;
+#pragma unroll
+    for (int c = 0; c < KS / 4; ++c) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) v = *reinterpret_cast<const float4*>(rowp + KS * g + 4 * c);
+        r[4 * c + 0] = v.x;
+        r[4 * c + 1] = v.y;
+        r[4 * c + 2] = v.z;
+        r[4 * c + 3] = v.w;
+    }
+}
+
+// Map a linear workgroup id to (tile, bh): tiles in decreasing order of work
+// for causal problems, heads fastest.
+__device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_first_high,
+                                              int& tile, int& bh) {
+    const int bid = blockIdx.x;
+    const int rank = bid / BH;
+    bh = bid - rank * BH;
+    tile = heavy_first_high ? (ntiles - 1 - rank) : rank;
+}
+
+// ------------------------------------------------------------------ forward
+template <int HS>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(float* __restrict__ out,
+                                                           float* __restrict__ lse,
+                                                           const float* __restrict__ qkv, int T,
+                                                           int C, int NH, int causal,
+                                                           float scale_log2) {
+    constexpr int LDK = HS + 4;
+    constexpr int KS = HS / 4;
+    constexpr int NB = kTile / 16;   // 16-key blocks per tile
+    constexpr int MB = HS / 16;      // 16-column blocks of O
+    __shared__ float Ks[kTile * LDK];
+    __shared__ float Vs[kTile * LDK];
+
+    const Lane L;
+    const int nqt = (T + kTile - 1) / kTile;
+    const int BH = gridDim.x / nqt;
+    int qt, bh;
+    tile_of_block(BH, nqt, causal != 0, qt, bh);
+    const int b = bh / NH, h = bh - (bh / NH) * NH;
+    const size_t C3 = 3 * (size_t)C;
+    const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
+    const float* kbase = qbase + C;
+    const float* vbase = qbase + 2 * (size_t)C;
+
+    const int qrow = qt * kTile + 16 * L.w + L.r16;
+    float qreg[KS];
+    load_row_part<HS>(qreg, qbase + (size_t)qrow * C3, qrow < T, L.g);
+
+    float m = -INFINITY;   // running max of scale*log2(e)*s (log2 domain)
+    float lsum = 0.f;      // this lane's share of the running normaliser
+    f32x4 o[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nkt = causal ? (qt + 1) : nqt;
+    for (int kt = 0; kt < nkt; ++kt) {
+        __syncthreads();
+        load_tile_f32<HS, LDK>(Ks, kbase, C3, kt * kTile, T, L.tid);
+        load_tile_f32<HS, LDK>(Vs, vbase, C3, kt * kTile, T, L.tid);
+        __syncthreads();
+
+        // S^T blocks: s[n][i] = S[qrow][kt*64 + 16n + 4g + i]
+        f32x4 s[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const float* kr = Ks + (16 * n + L.r16) * LDK + KS * L.g;
+#pragma unroll
+            for (int c = 0; c < KS / 4; ++c) {
+                const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
+                acc = mfma_f32(kk.x, qreg[4 * c + 0], acc);
+                acc = mfma_f32(kk.y, qreg[4 * c + 1], acc);
+                acc = mfma_f32(kk.z, qreg[4 * c + 2], acc);
+                acc = mfma_f32(kk.w, qreg[4 * c + 3], acc);
+            }
+            s[n] = acc;
+        }
+
+        // scale, mask (only the last tile holds the diagonal and the tail)
+        const bool edge = (kt == nkt - 1);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = s[n][i] * scale_log2;
+                if (edge) {
+                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
+                    if (kv >= T || (causal && kv > qrow)) x = -INFINITY;
+                }
+                s[n][i] = x;
+                mloc = fmaxf(mloc, x);
+            }
+        }
+        mloc = group4_max(mloc);
+        const float mnew = fmaxf(m, mloc);
+        const float alpha = fast_exp2(m - mnew);   // m = -inf on the first tile -> 0
+        m = mnew;
+        float psum = 0.f;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[n][i] - mnew);
+                s[n][i] = p;
+                psum += p;
+            }
+        }
+        lsum = lsum * alpha + psum;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+
+        // O^T += V^T P^T: o[mb][i'] = O[qrow][16mb + 4g + i']
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* vr = Vs + (16 * n + 4 * L.g + i) * LDK + L.r16;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) o[mb] = mfma_f32(vr[16 * mb], s[n][i], o[mb]);
+            }
+        }
+    }
+
+    const float ltot = group4_sum(lsum);
+    if (qrow < T) {
+        const float inv = 1.0f / ltot;
+        float* orow = out + ((size_t)b * T + qrow) * C + (size_t)h * HS;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const f32x4 v = o[mb] * inv;
+            *reinterpret_cast<float4*>(orow + 16 * mb + 4 * L.g) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (L.g == 0) lse[(size_t)bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+    }
+}
+
+// ------------------------------------------------------ backward pre-pass
+// D[b,h,t] = sum_i dout[b,t,h*hs+i] * out[b,t,h*hs+i], one group of HS/4
+// lanes per (b,t,h) row, rows in memory order.
+template <int HS>
+__global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict__ D,
+                                                               const float* __restrict__ dout,
+                                                               const float* __restrict__ out,
+                                                               int T, int NH, long long rows) {
+    constexpr int G = HS / 4;
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long row = gid / G;
+    const int part = (int)(gid - row * G);
+    float acc = 0.f;
+    if (row < rows) {
+        const float4 a = *reinterpret_cast<const float4*>(dout + row * HS + 4 * part);
+        const float4 c = *reinterpret_cast<const float4*>(out + row * HS + 4 * part);
+        acc = a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+    }
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && part == 0) {
+        const long long bt = row / NH;
+        const int h = (int)(row - bt * NH);
+        const long long b = bt / T;
+        const int t = (int)(bt - b * T);
+        D[((size_t)b * NH + h) * T + t] = acc;
+    }
+}
+
+// ----------------------------------------------------- backward dK / dV
+// One workgroup per (64-row K/V tile, head); loops over the Q tiles that see
+// it.  Per Q tile: S = Q K^T, P = exp(scale*S - lse), dV^T += dO^T P,
+// dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS (scale applied at the end).
+template <int HS>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
+    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
+    int causal, float scale, float scale_log2) {
+    constexpr int LDK = HS + 4;
+    constexpr int KS = HS / 4;
+    constexpr int NB = kTile / 16;
+    constexpr int MB = HS / 16;
+    __shared__ float Qs[kTile * LDK];
+    __shared__ float dOs[kTile * LDK];
+    __shared__ float Ls[kTile];
+    __shared__ float Dl[kTile];
+
+    const Lane L;
+    const int nt = (T + kTile - 1) / kTile;
+    const int BH = gridDim.x / nt;
+    int kt, bh;
+    tile_of_block(BH, nt, false, kt, bh);   // kt = 0 has the most Q tiles
+    const int b = bh / NH, h = bh - (bh / NH) * NH;
+    const size_t C3 = 3 * (size_t)C;
+    const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
+    const float* kbase = qbase + C;
+    const float* vbase = qbase + 2 * (size_t)C;
+    const float* dobase = dout + (size_t)b * T * C + (size_t)h * HS;
+    const float* lrow = lse + (size_t)bh * T;
+    const float* drow = Dws + (size_t)bh * T;
+
+    const int kvrow = kt * kTile + 16 * L.w + L.r16;
+    float kreg[KS], vreg[KS];
+    load_row_part<HS>(kreg, kbase + (size_t)kvrow * C3, kvrow < T, L.g);
+    load_row_part<HS>(vreg, vbase + (size_t)kvrow * C3, kvrow < T, L.g);
+
+    f32x4 dk[MB], dv[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        dk[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int qt0 = causal ? kt : 0;
+    for (int qt = qt0; qt < nt; ++qt) {
+        __syncthreads();
+        load_tile_f32<HS, LDK>(Qs, qbase, C3, qt * kTile, T, L.tid);
+        load_tile_f32<HS, LDK>(dOs, dobase, (size_t)C, qt * kTile, T, L.tid);
+        if (L.tid < kTile) {
+            const int q = qt * kTile + L.tid;
+            Ls[L.tid] = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
+            Dl[L.tid] = (q < T) ? drow[q] : 0.f;
+        }
+        __syncthreads();
+        const bool diag = causal && (qt == kt);
+
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            // s[i] = S[q = qt*64 + 16n + 4g + i][kvrow], dp likewise
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            const float* qr = Qs + (16 * n + L.r16) * LDK + KS * L.g;
+            const float* dr = dOs + (16 * n + L.r16) * LDK + KS * L.g;
+#pragma unroll
+            for (int c = 0; c < KS / 4; ++c) {
+                const float4 qa = *reinterpret_cast<const float4*>(qr + 4 * c);
+                const float4 da = *reinterpret_cast<const float4*>(dr + 4 * c);
+                s = mfma_f32(qa.x, kreg[4 * c + 0], s);
+                dp = mfma_f32(da.x, vreg[4 * c + 0], dp);
+                s = mfma_f32(qa.y, kreg[4 * c + 1], s);
+                dp = mfma_f32(da.y, vreg[4 * c + 1], dp);
+                s = mfma_f32(qa.z, kreg[4 * c + 2], s);
+                dp = mfma_f32(da.z, vreg[4 * c + 2], dp);
+                s = mfma_f32(qa.w, kreg[4 * c + 3], s);
+                dp = mfma_f32(da.w, vreg[4 * c + 3], dp);
+            }
+            float p[4], ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ql = 16 * n + 4 * L.g + i;
+                float pv = fast_exp2(s[i] * scale_log2 - Ls[ql]);
+                if (diag && (qt * kTile + ql < kvrow)) pv = 0.f;
+                p[i] = pv;
+                ds[i] = pv * (dp[i] - Dl[ql]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ql = 16 * n + 4 * L.g + i;
+                const float* dor = dOs + ql * LDK + L.r16;
+                const float* qrr = Qs + ql * LDK + L.r16;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    dv[mb] = mfma_f32(dor[16 * mb], p[i], dv[mb]);
+                    dk[mb] = mfma_f32(qrr[16 * mb], ds[i], dk[mb]);
+                }
+            }
+        }
+    }
+
+    if (kvrow < T) {
+        float* dkrow = dqkv + ((size_t)b * T + kvrow) * C3 + C + (size_t)h * HS;
+        float* dvrow = dkrow + C;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const f32x4 a = dk[mb] * scale;
+            const f32x4 v = dv[mb];
+            *reinterpret_cast<float4*>(dkrow + 16 * mb + 4 * L.g) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4*>(dvrow + 16 * mb + 4 * L.g) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// ----------------------------------------------------------- backward dQ
+// One workgroup per (64-row Q tile, head); loops over the key tiles it sees.
+// Per K/V tile: S^T = K Q^T, P, dP^T = V dO^T, dS = P * (dP - D),
+// dQ^T += K^T dS^T (scale applied at the end).
+template <int HS>
+__global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(
+    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
+    int causal, float scale, float scale_log2) {
+    constexpr int LDK = HS + 4;
+    constexpr int KS = HS / 4;
+    constexpr int NB = kTile / 16;
+    constexpr int MB = HS / 16;
+    __shared__ float Ks[kTile * LDK];
+    __shared__ float Vs[kTile * LDK];
+
+    const Lane L;
+    const int nt = (T + kTile - 1) / kTile;
+    const int BH = gridDim.x / nt;
+    int qt, bh;
+    tile_of_block(BH, nt, causal != 0, qt, bh);
+    const int b = bh / NH, h = bh - (bh / NH) * NH;
+    const size_t C3 = 3 * (size_t)C;
+    const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
+    const float* kbase = qbase + C;
+    const float* vbase = qbase + 2 * (size_t)C;
+    const float* dobase = dout + (size_t)b * T * C + (size_t)h * HS;
+
+    const int qrow = qt * kTile + 16 * L.w + L.r16;
+    const bool qvalid = qrow < T;
+    float qreg[KS], doreg[KS];
+    load_row_part<HS>(qreg, qbase + (size_t)qrow * C3, qvalid, L.g);
+    load_row_part<HS>(doreg, dobase + (size_t)qrow * C, qvalid, L.g);
+    const float l2 = qvalid ? lse[(size_t)bh * T + qrow] * kLog2e : INFINITY;
+    const float Dq = qvalid ? Dws[(size_t)bh * T + qrow] : 0.f;
+
+    f32x4 dq[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dq[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nkt = causal ? (qt + 1) : nt;
+    for (int kt = 0; kt < nkt; ++kt) {
+        __syncthreads();
+        load_tile_f32<HS, LDK>(Ks, kbase, C3, kt * kTile, T, L.tid);
+        load_tile_f32<HS, LDK>(Vs, vbase, C3, kt * kTile, T, L.tid);
+        __syncthreads();
+        const bool edge = (kt == nkt - 1);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            // s[i] = S[qrow][kv = kt*64 + 16n + 4g + i], dp likewise
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            const float* kr = Ks + (16 * n + L.r16) * LDK + KS * L.g;
+            const float* vr = Vs + (16 * n + L.r16) * LDK + KS * L.g;
+#pragma unroll
+            for (int c = 0; c < KS / 4; ++c) {
+                const float4 ka = *reinterpret_cast<const float4*>(kr + 4 * c);
+                const float4 va = *reinterpret_cast<const float4*>(vr + 4 * c);
+                s = mfma_f32(ka.x, qreg[4 * c + 0], s);
+                dp = mfma_f32(va.x, doreg[4 * c + 0], dp);
+                s = mfma_f32(ka.y, qreg[4 * c + 1], s);
+                dp = mfma_f32(va.y, doreg[4 * c + 1], dp);
+                s = mfma_f32(ka.z, qreg[4 * c + 2], s);
+                dp = mfma_f32(va.z, doreg[4 * c + 2], dp);
+                s = mfma_f32(ka.w, qreg[4 * c + 3], s);
+                dp = mfma_f32(va.w, doreg[4 * c + 3], dp);
+            }
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float pv = fast_exp2(s[i] * scale_log2 - l2);
+                if (edge) {
+                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
+                    if (kv >= T || (causal && kv > qrow)) pv = 0.f;
+                }
+                ds[i] = pv * (dp[i] - Dq);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* kr2 = Ks + (16 * n + 4 * L.g + i) * LDK + L.r16;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) dq[mb] = mfma_f32(kr2[16 * mb], ds[i], dq[mb]);
+            }
+        }
+    }
+
+    if (qvalid) {
+        float* dqrow = dqkv + ((size_t)b * T + qrow) * C3 + (size_t)h * HS;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const f32x4 a = dq[mb] * scale;
+            *reinterpret_cast<float4*>(dqrow + 16 * mb + 4 * L.g) = make_float4(a[0], a[1], a[2], a[3]);
+        }
+    }
+}
+
+template <int HS>
+hipError_t fwd_f32_hs(float* out, float* lse, const float* qkv, const Shape& s, hipStream_t st) {
+    const int nqt = (s.T + kTile - 1) / kTile;
+    const unsigned grid = (unsigned)(nqt * s.B * s.NH);
+    const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
+    hipLaunchKernelGGL(fwd_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, out, lse, qkv, s.T,
+                       s.C, s.NH, s.causal, scale_log2);
+    return hipGetLastError();
+}
+
+template <int HS>
+hipError_t bwd_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* out,
+                      const float* lse, float* Dws, const Shape& s, hipStream_t st) {
+    const long long rows = (long long)s.B * s.T * s.NH;
+    const long long pre_threads = rows * (HS / 4);
+    const unsigned pre_grid = (unsigned)((pre_threads + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(prepass_f32_kernel<HS>, dim3(pre_grid), dim3(kThreads), 0, st, Dws, dout,
+                       out, s.T, s.NH, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nt = (s.T + kTile - 1) / kTile;
+    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const float scale = (float)(1.0 / sqrt((double)HS));
+    const float scale_log2 = scale * kLog2e;
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
+                       lse, Dws, s.T, s.C, s.NH, s.causal, scale, scale_log2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
+                       lse, Dws, s.T, s.C, s.NH, s.causal, scale, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(float* out, float* lse, const float* qkv, const Shape& s,
+                          hipStream_t st) {
+    switch (s.hs) {
+        case 16: return fwd_f32_hs<16>(out, lse, qkv, s, st);
+        case 32: return fwd_f32_hs<32>(out, lse, qkv, s, st);
+        case 64: return fwd_f32_hs<64>(out, lse, qkv, s, st);
+        case 128: return fwd_f32_hs<128>(out, lse, qkv, s, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_f32(float* dqkv, const float* dout, const float* qkv, const float* out,
+                          const float* lse, float* Dws, const Shape& s, hipStream_t st) {
+    switch (s.hs) {
+        case 16: return bwd_f32_hs<16>(dqkv, dout, qkv, out, lse, Dws, s, st);
+        case 32: return bwd_f32_hs<32>(dqkv, dout, qkv, out, lse, Dws, s, st);
+        case 64: return bwd_f32_hs<64>(dqkv, dout, qkv, out, lse, Dws, s, st);
+        case 128: return bwd_f32_hs<128>(dqkv, dout, qkv, out, lse, Dws, s, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn
