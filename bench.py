@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention path on one MI355X.
+
+One step = one forward (attn_forward) plus one backward (pre-pass, dK/dV
+kernel, dQ kernel) over the workload's synthetic batch, inputs resident in
+device memory.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16]
+
+value = useful fwd+bwd TFLOP/s = (4 + 10) * hs * pairs * B * NH / step time,
+pairs = T(T+1)/2 for causal (masked pairs are not counted; the backward's
+recomputation of the scores is counted, as one of its five contractions).
+Each kernel is timed with HIP events recorded on the stream it runs on
+(torch's current stream, which the binding hands to libattn).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd causal TFLOP/s and % MFMA peak, B8 T1024 C768 NH12"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "transformer_causal_head_attn_amd", "csrc")
+KERNEL_SOURCE = {"f32": "flash_f32.hip", "bf16": "flash_bf16.hip"}
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=3)
+    p.add_argument("--dtype", choices=["f32", "bf16"], default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=15.0,
+                   help="CPU seconds the oracle baseline may spend on its sample")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the secondary measurements (other dtype)")
+    return p.parse_args()
+
+
+def kernel_flops(w):
+    """Algorithmic flops of each kernel for one launch: 2*hs per unmasked
+    (query, key) pair per contraction it performs."""
+    u = 2 * w.hs * w.pairs * w.B * w.NH
+    return {"fwd": 2 * u,       # S = Q K^T, O = P V
+            "prepass": 0,
+            "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
+            "dq": 3 * u}        # S, dP, dQ = dS K
+
+
+def prepass_bytes(w, esize):
+    return 2 * w.B * w.T * w.C * esize + w.B * w.NH * w.T * 4
+
+
+def source_sha(dtype):
+    with open(os.path.join(CSRC, KERNEL_SOURCE[dtype]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, dtype, workload_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel, if its kernel source is unchanged since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{dtype}_workload{workload_key}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    fetch = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    write = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (sha and fetch and write) or sha.group(1) != source_sha(dtype):
+        return None
+    return float(fetch.group(1)) + float(write.group(1))
+
+
+def run_gpu(la, torch, w, dtype, steps, warmup):
+    from workloads import workload_inputs
+    qkv_c, dout_c = workload_inputs(w, dtype)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    B, T, C, NH = w.B, w.T, w.C, w.NH
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty((B, T, C), dtype=tdt, device="cuda")
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+    dqkv = torch.empty_like(qkv)
+    D = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+    sfx = "_bf16" if dtype == "bf16" else ""
+    fwd = getattr(la, "attn_forward" + sfx)
+    pre = getattr(la, "attn_backward_preprocess" + sfx)
+    dkdv = getattr(la, "attn_backward_dkdv" + sfx)
+    dq = getattr(la, "attn_backward_dq" + sfx)
+    c = int(w.causal)
+    stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
+              ("prepass", lambda: pre(D, dout, out, B, T, C, NH)),
+              ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c)),
+              ("dq", lambda: dq(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
+
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record()
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = {}
+    for i, (name, _) in enumerate(stages):
+        per_kernel[name] = sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps
+    total_ms = ev[0][0].elapsed_time(ev[-1][-1]) / steps
+    return total_ms, wall * 1e3 / steps, per_kernel
+
+
+def cpu_baseline(w, dtype, budget_s):
+    """The fp64 oracle, as it stands, on the first heads of the same
+    workload in (b, h) order until the CPU budget is spent."""
+    import oracle
+    from workloads import workload_inputs
+    qkv, dout = workload_inputs(w, dtype)
+    heads = [(b, h) for b in range(w.B) for h in range(w.NH)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        qs = oracle.head_slice(qkv, b, h, w.NH, packed=True)
+        ds = oracle.head_slice(dout, b, h, w.NH, packed=False)
+        oracle.forward(qs, 1, w.causal)
+        oracle.backward(qs, ds, 1, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 14 * w.hs * w.pairs * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (first in (b,h) order) of the same workload, "
+                      f"fp64 forward+backward, {dt:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    import transformer_causal_head_attn_amd as la
+    from workloads import WORKLOADS
+
+    la.load()
+    w = WORKLOADS[args.workload]
+    dtype = args.dtype or w.dtype
+    total_ms, wall_ms, per_kernel = run_gpu(la, torch, w, dtype, args.steps, args.warmup)
+    flops = w.flops_fwd + w.flops_bwd
+    value = flops / (total_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+
+    kf = kernel_flops(w)
+    esize = 2 if dtype == "bf16" else 4
+    kernels = {}
+    for name, ms in per_kernel.items():
+        rec = {"ms": round(ms, 5)}
+        if kf[name]:
+            rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
+            rec["frac_peak"] = round(rec["tflops"] / peak, 4)
+        else:
+            rec["gbs"] = round(prepass_bytes(w, esize) / (ms * 1e-3) / 1e9, 1)
+            rec["frac_hbm"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = rec
+    dom = max(per_kernel, key=per_kernel.get)
+    achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dom, dtype, w.key),
+                "algorithmic_flops_per_launch": kf[dom]}
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) qkv and dout, no dataset)",
+        "config": {"workload": f"{w.name} {w.label()}", "B": w.B, "T": w.T, "C": w.C,
+                   "NH": w.NH, "hs": w.hs, "causal": w.causal},
+        "frac_mfma_peak": round(value / peak, 4),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+
+    if not args.no_extra:
+        other = "bf16" if dtype == "f32" else "f32"
+        o_total, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
+        o_val = flops / (o_total * 1e-3) / 1e12
+        line["same_workload_" + other] = {
+            "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
+            "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
+            "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_budget_s)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

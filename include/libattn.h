@@ -93,6 +93,26 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   int B, int T, int C, int NH, int causal);
 
 /*
+ * The three stages of attn_backward, for callers that want to time, order or
+ * overlap them, or to own the D buffer (these calls allocate nothing):
+ *   attn_backward_preprocess: D (B,NH,T) fp32 = rowsum over each head's hs
+ *       columns of dout * out (D[t] = sum_j att[t,j] datt[t,j], the row term
+ *       of the closed-form softmax gradient);
+ *   attn_backward_dkdv: writes only the dk and dv thirds of dqkv;
+ *   attn_backward_dq: writes only the dq third of dqkv.
+ * dkdv and dq read D and lse; they may run in either order after the
+ * pre-pass.  Running all three equals attn_backward.
+ */
+int attn_backward_preprocess(float* D, const float* dout, const float* out,
+                             int B, int T, int C, int NH);
+int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv,
+                       const float* lse, const float* D,
+                       int B, int T, int C, int NH, int causal);
+int attn_backward_dq(float* dqkv, const float* dout, const float* qkv,
+                     const float* lse, const float* D,
+                     int B, int T, int C, int NH, int causal);
+
+/*
  * Fused forward and backward with bfloat16 inputs and outputs and fp32
  * accumulation (the mixed-precision scheme of "LLM Systems 10 & 11:
  * Accelerating Transformer Training and Inference", section 1: low-precision
@@ -104,6 +124,15 @@ int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv,
 int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                        const uint16_t* out, const float* lse,
                        int B, int T, int C, int NH, int causal);
+/* bf16 versions of the three backward stages (D stays fp32). */
+int attn_backward_preprocess_bf16(float* D, const uint16_t* dout, const uint16_t* out,
+                                  int B, int T, int C, int NH);
+int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                            const float* lse, const float* D,
+                            int B, int T, int C, int NH, int causal);
+int attn_backward_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                          const float* lse, const float* D,
+                          int B, int T, int C, int NH, int causal);
 
 /*
  * Materialised forward, fp32, as the pages' reference does it: writes the

@@ -65,7 +65,10 @@ def call(name, nptr, B, T, C, NH, causal, override=None):
 
 ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_forward_bf16", 3),
          ("attn_backward_bf16", 5), ("attn_forward_materialized", 4),
-         ("attn_backward_materialized", 6)]
+         ("attn_backward_materialized", 6),
+         ("attn_backward_dkdv", 5), ("attn_backward_dq", 5),
+         ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 5)]
+STAGE0 = [("attn_backward_preprocess", 3), ("attn_backward_preprocess_bf16", 3)]
 
 
 @pytest.mark.parametrize("name,nptr", ENTRY)
@@ -105,6 +108,20 @@ def test_output_overlapping_input(name, nptr):
     # put the last argument (an input) 16 bytes into the first (an output)
     rc, msg = call(name, nptr, 1, 64, 64, 4, 1, override={nptr - 1: BASE + 16})
     assert rc == la.ATTN_EINVAL and "overlaps" in msg
+
+
+@pytest.mark.parametrize("name,nptr", STAGE0)
+def test_preprocess_arguments(name, nptr):
+    lib = la.load()
+    p = ptrs(nptr)
+    assert getattr(lib, name)(*p, 1, 64, 64, 0) == la.ATTN_EINVAL
+    assert getattr(lib, name)(*p, 1, 64, 66, 4) == la.ATTN_EINVAL
+    assert getattr(lib, name)(*p, 1, 64, 96, 4) == la.ATTN_EUNSUPPORTED
+    p[0] = ctypes.c_void_p(0)
+    assert getattr(lib, name)(*p, 1, 64, 64, 4) == la.ATTN_EINVAL
+    p = ptrs(nptr)
+    p[2] = ctypes.c_void_p(BASE + 16)   # out overlaps the D output
+    assert getattr(lib, name)(*p, 1, 64, 64, 4) == la.ATTN_EINVAL
 
 
 def test_too_large_for_32bit_offsets():

@@ -24,7 +24,10 @@ ATTN_EUNSUPPORTED = -2
 ATTN_EHIP = -3
 
 EXPORTS = (
-    "attn_forward", "attn_backward", "attn_forward_bf16", "attn_backward_bf16",
+    "attn_forward", "attn_backward",
+    "attn_backward_preprocess", "attn_backward_dkdv", "attn_backward_dq",
+    "attn_forward_bf16", "attn_backward_bf16",
+    "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
     "attn_forward_materialized", "attn_backward_materialized",
     "attn_set_stream", "attn_last_error", "attn_release",
 )
@@ -55,9 +58,15 @@ def load(path: str | None = None):
         for name, nptr in (("attn_forward", 3), ("attn_forward_bf16", 3),
                            ("attn_backward", 5), ("attn_backward_bf16", 5),
                            ("attn_forward_materialized", 4),
-                           ("attn_backward_materialized", 6)):
+                           ("attn_backward_materialized", 6),
+                           ("attn_backward_dkdv", 5), ("attn_backward_dq", 5),
+                           ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 5)):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * nptr + [i] * 5
+            fn.restype = i
+        for name in ("attn_backward_preprocess", "attn_backward_preprocess_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 3 + [i] * 4
             fn.restype = i
         lib.attn_set_stream.argtypes = [vp]
         lib.attn_set_stream.restype = i
@@ -111,6 +120,29 @@ def attn_backward(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
           *_dims(B, T, C, NH, causal))
 
 
+def attn_backward_preprocess(D, dout, out, B, T, C, NH) -> None:
+    f = torch.float32
+    _call("attn_backward_preprocess", _check(D, "D", f, B * NH * T),
+          _check(dout, "dout", f, B * T * C), _check(out, "out", f, B * T * C),
+          int(B), int(T), int(C), int(NH))
+
+
+def attn_backward_dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_backward_dkdv", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_dq(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_backward_dq", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
 def attn_forward_bf16(out, lse, qkv, B, T, C, NH, causal) -> None:
     h, f = torch.bfloat16, torch.float32
     _call("attn_forward_bf16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
@@ -122,6 +154,29 @@ def attn_backward_bf16(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
     _call("attn_backward_bf16", _check(dqkv, "dqkv", h, B * T * 3 * C),
           _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
           _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_preprocess_bf16(D, dout, out, B, T, C, NH) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_backward_preprocess_bf16", _check(D, "D", f, B * NH * T),
+          _check(dout, "dout", h, B * T * C), _check(out, "out", h, B * T * C),
+          int(B), int(T), int(C), int(NH))
+
+
+def attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_backward_dkdv_bf16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_dq_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_backward_dq_bf16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
           *_dims(B, T, C, NH, causal))
 
 

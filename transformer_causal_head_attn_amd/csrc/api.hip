@@ -182,9 +182,52 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
     float* D = nullptr;
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
-    return launched(attn::launch_bwd_f32(dqkv, dout, qkv, out, lse, D,
-                                         shape_of(B, T, C, NH, causal), g_stream),
-                    "attn_backward launch");
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dq_f32(dqkv, dout, qkv, lse, D, s, g_stream);
+    return launched(e, "attn_backward launch");
+}
+
+int attn_backward_preprocess(float* D, const float* dout, const float* out, int B, int T, int C,
+                             int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{D, nbytes(BT * NH, 4), "D"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"}, {out, nbytes(BT * C, 4), "out"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 1, ins, 2, false);
+    if (rc) return rc;
+    return launched(attn::launch_prepass_f32(D, dout, out, shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_backward_preprocess launch");
+}
+
+int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                       const float* D, int B, int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
+                                          g_stream),
+                    "attn_backward_dkdv launch");
+}
+
+int attn_backward_dq(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                     const float* D, int B, int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dq_f32(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
+                                        g_stream),
+                    "attn_backward_dq launch");
 }
 
 int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C, int NH,
@@ -212,9 +255,54 @@ int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv
     float* D = nullptr;
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
-    return launched(attn::launch_bwd_bf16(dqkv, dout, qkv, out, lse, D,
-                                          shape_of(B, T, C, NH, causal), g_stream),
-                    "attn_backward_bf16 launch");
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    hipError_t e = attn::launch_prepass_bf16(D, dout, out, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dq_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
+    return launched(e, "attn_backward_bf16 launch");
+}
+
+int attn_backward_preprocess_bf16(float* D, const uint16_t* dout, const uint16_t* out, int B,
+                                  int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{D, nbytes(BT * NH, 4), "D"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"}, {out, nbytes(BT * C, 2), "out"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 1, ins, 2, false);
+    if (rc) return rc;
+    return launched(attn::launch_prepass_bf16(D, dout, out, shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_backward_preprocess_bf16 launch");
+}
+
+int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                            const float* lse, const float* D, int B, int T, int C, int NH,
+                            int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
+                                           g_stream),
+                    "attn_backward_dkdv_bf16 launch");
+}
+
+int attn_backward_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                          const float* lse, const float* D, int B, int T, int C, int NH,
+                          int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dq_bf16(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
+                                         g_stream),
+                    "attn_backward_dq_bf16 launch");
 }
 
 int attn_forward_materialized(float* out, float* preatt, float* att, const float* qkv, int B,

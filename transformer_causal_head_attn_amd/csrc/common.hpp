@@ -69,14 +69,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---- launchers (return hipSuccess or the launch error) ----
+// fp32 fused path
 hipError_t launch_fwd_f32(float* out, float* lse, const float* qkv, const Shape& s, hipStream_t st);
-hipError_t launch_bwd_f32(float* dqkv, const float* dout, const float* qkv, const float* out,
-                          const float* lse, float* Dws, const Shape& s, hipStream_t st);
+hipError_t launch_prepass_f32(float* D, const float* dout, const float* out, const Shape& s,
+                              hipStream_t st);
+hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                           const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                         const float* D, const Shape& s, hipStream_t st);
+// bf16 fused path (bf16 tensors as raw 16-bit patterns)
 hipError_t launch_fwd_bf16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                            hipStream_t st);
-hipError_t launch_bwd_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                           const uint16_t* out, const float* lse, float* Dws, const Shape& s,
-                           hipStream_t st);
+hipError_t launch_prepass_bf16(float* D, const uint16_t* dout, const uint16_t* out,
+                               const Shape& s, hipStream_t st);
+hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                            const float* lse, const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                          const float* lse, const float* D, const Shape& s, hipStream_t st);
+// materialised fp32 path
 hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
                                    const Shape& s, hipStream_t st);
 hipError_t launch_bwd_materialized(float* dqkv, float* dpreatt, float* datt, const float* dout,

@@ -454,50 +454,69 @@ hipError_t fwd_f32_hs(float* out, float* lse, const float* qkv, const Shape& s, 
 }
 
 template <int HS>
-hipError_t bwd_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* out,
-                      const float* lse, float* Dws, const Shape& s, hipStream_t st) {
+hipError_t prepass_f32_hs(float* D, const float* dout, const float* out, const Shape& s,
+                          hipStream_t st) {
     const long long rows = (long long)s.B * s.T * s.NH;
-    const long long pre_threads = rows * (HS / 4);
-    const unsigned pre_grid = (unsigned)((pre_threads + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(prepass_f32_kernel<HS>, dim3(pre_grid), dim3(kThreads), 0, st, Dws, dout,
-                       out, s.T, s.NH, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const long long threads = rows * (HS / 4);
+    const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(prepass_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, D, dout, out,
+                       s.T, s.NH, rows);
+    return hipGetLastError();
+}
+
+template <int HS>
+hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                       const float* D, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    const float scale_log2 = scale * kLog2e;
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, Dws, s.T, s.C, s.NH, s.causal, scale, scale_log2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <int HS>
+hipError_t dq_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                     const float* D, const Shape& s, hipStream_t st) {
+    const int nt = (s.T + kTile - 1) / kTile;
+    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, Dws, s.T, s.C, s.NH, s.causal, scale, scale_log2);
+                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
     return hipGetLastError();
 }
 
 }  // namespace
 
+#define ATTN_DISPATCH_HS(fn, ...)                         \
+    switch (s.hs) {                                       \
+        case 16: return fn<16>(__VA_ARGS__);              \
+        case 32: return fn<32>(__VA_ARGS__);              \
+        case 64: return fn<64>(__VA_ARGS__);              \
+        case 128: return fn<128>(__VA_ARGS__);            \
+        default: return hipErrorInvalidValue;             \
+    }
+
 hipError_t launch_fwd_f32(float* out, float* lse, const float* qkv, const Shape& s,
                           hipStream_t st) {
-    switch (s.hs) {
-        case 16: return fwd_f32_hs<16>(out, lse, qkv, s, st);
-        case 32: return fwd_f32_hs<32>(out, lse, qkv, s, st);
-        case 64: return fwd_f32_hs<64>(out, lse, qkv, s, st);
-        case 128: return fwd_f32_hs<128>(out, lse, qkv, s, st);
-        default: return hipErrorInvalidValue;
-    }
+    ATTN_DISPATCH_HS(fwd_f32_hs, out, lse, qkv, s, st)
 }
 
-hipError_t launch_bwd_f32(float* dqkv, const float* dout, const float* qkv, const float* out,
-                          const float* lse, float* Dws, const Shape& s, hipStream_t st) {
-    switch (s.hs) {
-        case 16: return bwd_f32_hs<16>(dqkv, dout, qkv, out, lse, Dws, s, st);
-        case 32: return bwd_f32_hs<32>(dqkv, dout, qkv, out, lse, Dws, s, st);
-        case 64: return bwd_f32_hs<64>(dqkv, dout, qkv, out, lse, Dws, s, st);
-        case 128: return bwd_f32_hs<128>(dqkv, dout, qkv, out, lse, Dws, s, st);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_prepass_f32(float* D, const float* dout, const float* out, const Shape& s,
+                              hipStream_t st) {
+    ATTN_DISPATCH_HS(prepass_f32_hs, D, dout, out, s, st)
 }
+
+hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                           const float* D, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, dout, qkv, lse, D, s, st)
+}
+
+hipError_t launch_dq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                         const float* D, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dq_f32_hs, dqkv, dout, qkv, lse, D, s, st)
+}
+
+#undef ATTN_DISPATCH_HS
 
 }  // namespace attn

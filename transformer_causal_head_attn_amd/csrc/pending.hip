@@ -4,13 +4,6 @@
 
 namespace attn {
 
-hipError_t launch_fwd_bf16(uint16_t*, float*, const uint16_t*, const Shape&, hipStream_t) {
-    return hipErrorNotSupported;
-}
-hipError_t launch_bwd_bf16(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
-                           const float*, float*, const Shape&, hipStream_t) {
-    return hipErrorNotSupported;
-}
 hipError_t launch_fwd_materialized(float*, float*, float*, const float*, const Shape&,
                                    hipStream_t) {
     return hipErrorNotSupported;
