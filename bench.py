@@ -125,6 +125,49 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     return total_ms, wall * 1e3 / steps, per_kernel
 
 
+def run_materialized(la, torch, w, steps, warmup):
+    """Time the materialised fp32 forward and backward (whole calls) and
+    report them against their compulsory traffic: every T x T matrix the
+    mode produces is written once and every one it consumes is read once."""
+    from workloads import workload_inputs
+    qkv_c, dout_c = workload_inputs(w, "f32")
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    B, T, C, NH, c = w.B, w.T, w.C, w.NH, int(w.causal)
+    out = torch.empty((B, T, C), device="cuda")
+    pre = torch.empty((B, NH, T, T), device="cuda")
+    att = torch.empty_like(pre)
+    datt = torch.empty_like(pre)
+    dpre = torch.empty_like(pre)
+    dqkv = torch.empty_like(qkv)
+    fwd = lambda: la.attn_forward_materialized(out, pre, att, qkv, B, T, C, NH, c)
+    bwd = lambda: la.attn_backward_materialized(dqkv, dpre, datt, dout, qkv, att, B, T, C, NH, c)
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(steps):
+        e[0].record()
+        fwd()
+        e[1].record()
+        bwd()
+        e[2].record()
+        torch.cuda.synchronize()
+        tf += e[0].elapsed_time(e[1])
+        tb += e[1].elapsed_time(e[2])
+    tf, tb = tf / steps, tb / steps
+    M = B * NH * T * T * 4
+    io = B * T * C * 4
+    fwd_bytes = 3 * io + 2 * M + io          # qkv in; preatt, att, out out
+    bwd_bytes = io + 3 * io + M + 2 * M + 3 * io   # dout, qkv, att in; datt, dpreatt, dqkv out
+    return {"workload": f"{w.name} {w.label()}", "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+            "fwd_gbs": round(fwd_bytes / (tf * 1e-3) / 1e9, 1),
+            "bwd_gbs": round(bwd_bytes / (tb * 1e-3) / 1e9, 1),
+            "bytes_note": "compulsory bytes: each T x T matrix written or read once, "
+                          "packed tensors once"}
+
+
 def cpu_baseline(w, dtype, budget_s):
     """The fp64 oracle, as it stands, on the first heads of the same
     workload in (b, h) order until the CPU budget is spent."""
@@ -211,6 +254,9 @@ def main():
             "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
             "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
             "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
+
+    if not args.no_extra and dtype == "f32":
+        line["materialized_f32"] = run_materialized(la, torch, w, min(args.steps, 10), 2)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_budget_s)

@@ -45,7 +45,8 @@
  * (attn_set_stream; default: the null stream) and return without waiting.
  * Results are deterministic: no atomics, fixed reduction order.
  *
- * Workspace.  attn_backward* needs B*NH*T floats of scratch for D; libattn
+ * Workspace.  attn_backward and attn_backward_bf16 need B*NH*T floats of
+ * scratch for D; libattn
  * keeps one grow-only buffer per device, allocated with hipMalloc on first
  * need, and frees it in attn_release().  With the environment variable
  * ATTN_TEST_FAIL_ALLOC=1 that allocation fails (ATTN_EHIP) before any HIP
@@ -147,6 +148,8 @@ int attn_forward_materialized(float* out, float* preatt, float* att, const float
 /*
  * Materialised backward, fp32, from the forward's att: writes datt = dout.v
  * (dense, every (t,j)), dpreatt (exactly 0 on masked entries) and dqkv.
+ * With causal = 1 only the lower triangle of att is read (entries above the
+ * diagonal are taken as 0).  Needs no workspace.
  * (llm.c attention_backward.cu: attention_backward_cpu and
  * softmax_autoregressive_backward_kernel7.)
  */

@@ -333,10 +333,7 @@ int attn_backward_materialized(float* dqkv, float* dpreatt, float* datt, const f
                         {att, nbytes(M, 4), "att"}};
     int rc = check_args(B, T, C, NH, causal, outs, 3, ins, 3, true);
     if (rc) return rc;
-    float* D = nullptr;
-    rc = workspace(nbytes((long long)B * NH * T, 4), &D);
-    if (rc) return rc;
-    return launched(attn::launch_bwd_materialized(dqkv, dpreatt, datt, dout, qkv, att, D,
+    return launched(attn::launch_bwd_materialized(dqkv, dpreatt, datt, dout, qkv, att,
                                                   shape_of(B, T, C, NH, causal), g_stream),
                     "attn_backward_materialized launch");
 }

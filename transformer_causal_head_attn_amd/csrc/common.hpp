@@ -90,7 +90,7 @@ hipError_t launch_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* 
 hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
                                    const Shape& s, hipStream_t st);
 hipError_t launch_bwd_materialized(float* dqkv, float* dpreatt, float* datt, const float* dout,
-                                   const float* qkv, const float* att, float* Dws, const Shape& s,
+                                   const float* qkv, const float* att, const Shape& s,
                                    hipStream_t st);
 
 }  // namespace attn
