@@ -45,7 +45,22 @@ def parse_args():
                    help="CPU seconds the oracle baseline may spend on its sample")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the secondary measurements (other dtype)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                   help="only run a plain device-to-device copy of MB megabytes (3 times), "
+                        "to calibrate the HBM byte counters of a profiler run")
     return p.parse_args()
+
+
+def calibrate_copy(torch, mb):
+    n = mb * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def kernel_flops(w):
@@ -203,6 +218,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
     import transformer_causal_head_attn_amd as la
     from workloads import WORKLOADS
 

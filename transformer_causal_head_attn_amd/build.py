@@ -18,6 +18,9 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 vector ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep matrix-core accumulators in ordinary VGPRs (gfx950 allows it):
+    # avoids v_accvgpr copies around every softmax step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

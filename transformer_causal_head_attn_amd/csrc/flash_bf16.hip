@@ -1,37 +1,48 @@
 // flash_bf16.hip -- fused attention forward and backward with bfloat16
 // tensors and fp32 accumulation for gfx950 (v_mfma_f32_16x16x32_bf16).
 //
-// Same method and tiling as the fp32 kernels (flash_f32.hip): the
-// self-attention of "Umakini wa kujitegemea, kerneli za CUDA na
-// FlashAttention" (section 1) computed tile by tile with a running softmax,
-// keeping only the per-row log-sum-exp, and the analytic backward of
-// attention_backward_cpu in llm.c dev/cuda/attention_backward.cu with the
-// closed-form softmax gradient of its kernel 7.  Low-precision operands with
-// higher-precision accumulation follow the mixed-precision part of "LLM
-// Systems 10 & 11: Accelerating Transformer Training and Inference"
-// (section 1): Q, K, V, dO are bf16, every product accumulates in fp32, the
-// softmax runs in fp32, and P and dS are rounded to bf16 only to enter the
-// matrix cores.  lse and D stay fp32.
+// Same method as the fp32 kernels (flash_f32.hip): the self-attention of
+// "Umakini wa kujitegemea, kerneli za CUDA na FlashAttention" (section 1)
+// computed tile by tile with a running softmax, keeping only the per-row
+// log-sum-exp, and the analytic backward of attention_backward_cpu in llm.c
+// dev/cuda/attention_backward.cu with the closed-form softmax gradient of
+// its kernel 7.  Low-precision operands with higher-precision accumulation
+// follow the mixed-precision part of "LLM Systems 10 & 11: Accelerating
+// Transformer Training and Inference" (section 1): Q, K, V, dO are bf16,
+// every product accumulates in fp32, the softmax runs in fp32, and P and dS
+// are rounded to bf16 only to enter the matrix cores.  lse and D stay fp32.
 //
-// gfx950 mapping.  One bf16 MFMA contracts 32 k-values: lane group g = l/16
-// supplies eight of them.  For Q.K and dO.V the contraction is over hs and a
-// lane takes k = 32s + 8g .. +7 (16 contiguous bytes).  For the products
-// that contract over keys or queries (P V, dO^T P, Q^T dS, K^T dS^T) the
-// operand coming out of the score accumulators holds, in lane group g, the
-// rows 16n + 4g + i; a 32-wide step t then pairs score blocks n = 2t, 2t+1
-// and lane group g supplies rows {32t + 4g + i, 32t + 16 + 4g + i : i < 4}.
-// The matching operand is read from a transposed LDS copy of its tile
-// (feature-major), two 8-byte reads per step.  Tiles are staged once from
-// global memory into whichever of the row-major and transposed LDS copies
-// the kernel needs.
+// gfx950 mapping.
+//  * One bf16 MFMA contracts 32 k-values; lane group g = l/16 supplies eight.
+//    For Q.K and dO.V (contraction over hs) a lane takes k = 32s + 8g .. +7,
+//    one 16-byte LDS read of a row-major tile.
+//  * For the products that contract over keys or queries (P V, dO^T P,
+//    Q^T dS, K^T dS^T) the operand that comes out of the score accumulators
+//    holds, in lane group g, the rows 16n + 4g + i; a 32-wide step t pairs
+//    score blocks n = 2t, 2t+1.  The matching operand (eight rows of one
+//    column of a row-major tile) comes from two ds_read_b64_tr_b16
+//    transpose reads, so no transposed copy of any tile is kept.
+//  * Every wave owns 32 rows (two 16-row blocks) of the tile it keeps in
+//    registers, so each operand read from LDS feeds two matrix-core ops;
+//    with 16 rows per wave the kernels would need more LDS bandwidth than
+//    a CU has.
+//  * The next streamed tile is loaded into registers while the current one
+//    is used (one LDS buffer, two barriers per step).
+//  * Forward: a row's running maximum is only raised (and its O, l
+//    rescaled) when the row's tile maximum exceeds it by more than 8 in the
+//    log2 domain (probabilities stay below 2^8); otherwise the stale maximum
+//    is kept, which changes no result (numerator and denominator share it),
+//    and the wave skips the rescale when none of its rows needs one.
 #include "common.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int kTile = 64;
-constexpr int kThreads = 256;
-constexpr int kLDT = kTile + 8;   // row stride (elements) of transposed tiles
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kStream = 64;     // rows of the streamed tile per step
+constexpr float kLazyMax = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -45,11 +56,10 @@ struct Lane {
 };
 
 template <int HS>
-struct BfGeom {
-    static constexpr int LDR = HS + 8;                 // row-major tile stride (elements)
+struct Geom {
+    static constexpr int LDR = HS + 8;                  // LDS row stride (elements)
     static constexpr int KSTEPS = HS >= 32 ? HS / 32 : 1;
     static constexpr int MB = HS / 16;
-    static constexpr int NB = kTile / 16;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -58,72 +68,44 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return r;
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-    return as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-}
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(make_uint4(0u, 0u, 0u, 0u)); }
 
-// Eight bf16 of one row for contraction step s: k = 32s + 8g .. +7.
-// Lanes whose k-range lies beyond HS (only when HS = 16) supply zeros.
+// Eight bf16 of one row for contraction step s: k = 32s + 8g .. +7; zeros
+// where that range lies beyond HS (only when HS = 16).
 template <int HS>
-__device__ __forceinline__ bf16x8 load_kchunk_global(const uint16_t* rowp, bool valid, int s,
-                                                     int g) {
+__device__ __forceinline__ bf16x8 row_chunk_global(const uint16_t* rowp, bool valid, int s, int g) {
     const int k0 = 32 * s + 8 * g;
     if (!valid || k0 >= HS) return zero_bf16x8();
     return as_bf16x8(*reinterpret_cast<const uint4*>(rowp + k0));
 }
 
 template <int HS>
-__device__ __forceinline__ bf16x8 load_kchunk_lds(const uint16_t* rowp, int s, int g) {
+__device__ __forceinline__ bf16x8 row_chunk_lds(const uint16_t* tile, int row, int s, int g) {
     const int k0 = 32 * s + 8 * g;
     if (k0 >= HS) return zero_bf16x8();
-    return as_bf16x8(*reinterpret_cast<const uint4*>(rowp + k0));
+    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + row * Geom<HS>::LDR + k0));
 }
 
-// Stage a kTile x HS bf16 tile (global rows row0.., stride ld elements) into
-// LDS: row-major copy `rm` (stride LDR) and/or transposed copy `tr`
-// (tr[d*kLDT + row], stride kLDT).  Rows >= T are zero.  Each work item
-// moves two rows x 8 columns so the transposed copy is written as packed
-// pairs of rows (one dword per column).
-template <int HS, bool ROW, bool TRANS>
-__device__ __forceinline__ void stage_tile_bf16(uint16_t* rm, uint16_t* tr, const uint16_t* base,
-                                                size_t ld, int row0, int T, int tid) {
-    constexpr int CH = HS / 8;                 // 16-byte chunks per row
-    constexpr int ITEMS = (kTile / 2) * CH;
-    constexpr int LDR = BfGeom<HS>::LDR;
-#pragma unroll
-    for (int e = tid; e < ITEMS; e += kThreads) {
-        const int rp = e / CH, c = e - (e / CH) * CH;
-        const int r0 = 2 * rp;
-        const int j0 = row0 + r0;
-        uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
-        if (j0 < T) a = *reinterpret_cast<const uint4*>(base + (size_t)j0 * ld + 8 * c);
-        if (j0 + 1 < T) b = *reinterpret_cast<const uint4*>(base + (size_t)(j0 + 1) * ld + 8 * c);
-        if (ROW) {
-            *reinterpret_cast<uint4*>(rm + r0 * LDR + 8 * c) = a;
-            *reinterpret_cast<uint4*>(rm + (r0 + 1) * LDR + 8 * c) = b;
-        }
-        if (TRANS) {
-            const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-            const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                // columns 8c + 2q (low halves) and 8c + 2q + 1 (high halves)
-                const uint32_t lo = (av[q] & 0xffffu) | (bv[q] << 16);
-                const uint32_t hi = (av[q] >> 16) | (bv[q] & 0xffff0000u);
-                *reinterpret_cast<uint32_t*>(tr + (8 * c + 2 * q) * kLDT + r0) = lo;
-                *reinterpret_cast<uint32_t*>(tr + (8 * c + 2 * q + 1) * kLDT + r0) = hi;
-            }
-        }
-    }
+__device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Operand for a key/query-contracting product read from a transposed tile:
-// row `d` of tr, entries {32t + 4g + i, 32t + 16 + 4g + i : i < 4}.
-__device__ __forceinline__ bf16x8 load_trans_operand(const uint16_t* tr, int d, int t, int g) {
-    const uint16_t* p = tr + d * kLDT + 32 * t + 4 * g;
-    const uint2 lo = *reinterpret_cast<const uint2*>(p);
-    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+// Column operand from a row-major LDS tile: lane (j = l%16, g) receives
+// tile[base + 4g + e][col0 + j] for e < 4 and tile[base + 16 + 4g + e - 4]
+// [col0 + j] for e >= 4.  Within a 16-lane group, ds_read_b64_tr_b16 hands
+// lane j element (j % 4) of the 8-byte blocks addressed by lanes 4e + j/4, so
+// lane i addresses row (.. + i/4), columns col0 + 4(i%4) .. +3.
+template <int HS>
+__device__ __forceinline__ bf16x8 col_operand(const uint16_t* tile, int base, int col0, int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const uint16_t* p = tile + (base + 4 * g + (j >> 2)) * Geom<HS>::LDR + col0 + 4 * (j & 3);
+    const s16x4 a = tr_read(p);
+    const s16x4 b = tr_read(p + 16 * Geom<HS>::LDR);
+    bf16x8 r;
+    __builtin_memcpy(&r, &a, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+    return r;
 }
 
 // Pack score-layout values of blocks n = 2t (x) and 2t+1 (y) into the
@@ -150,6 +132,34 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, const f32x4& v) {
     __builtin_memcpy(p, &r, 8);
 }
 
+// A kStream x HS bf16 tile held in registers between its global load and
+// its LDS store (row-major, stride LDR); rows >= T are zero.
+template <int HS>
+struct TileRegs {
+    static constexpr int CH = HS / 8;                        // 16-byte chunks per row
+    static constexpr int TOTAL = kStream * CH;
+    static constexpr int N = (TOTAL + kThreads - 1) / kThreads;
+    uint4 v[N];
+    __device__ __forceinline__ void fetch(const uint16_t* base, size_t ld, int row0, int T, int tid) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int e = tid + k * kThreads;
+            const int row = e / CH, c = e - (e / CH) * CH;
+            const int j = row0 + row;
+            v[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (e < TOTAL && j < T) v[k] = *reinterpret_cast<const uint4*>(base + (size_t)j * ld + 8 * c);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int e = tid + k * kThreads;
+            const int row = e / CH, c = e - (e / CH) * CH;
+            if (e < TOTAL) *reinterpret_cast<uint4*>(lds + row * Geom<HS>::LDR + 8 * c) = v[k];
+        }
+    }
+};
+
 __device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_first_high,
                                               int& tile, int& bh) {
     const int bid = blockIdx.x;
@@ -158,19 +168,25 @@ __device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_fir
     tile = heavy_first_high ? (ntiles - 1 - rank) : rank;
 }
 
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // ------------------------------------------------------------------ forward
-template <int HS>
+// Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
+// stream through LDS 64 at a time.
+template <int HS, int QB>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
                                                             float scale_log2) {
-    using G = BfGeom<HS>;
-    __shared__ uint16_t Ks[kTile * G::LDR];
-    __shared__ uint16_t Vt[HS * kLDT];
+    using G = Geom<HS>;
+    constexpr int R = 16 * QB;
+    constexpr int BM = 4 * R;
+    __shared__ uint16_t Ks[kStream * G::LDR];
+    __shared__ uint16_t Vs[kStream * G::LDR];
 
     const Lane L;
-    const int nqt = (T + kTile - 1) / kTile;
+    const int nqt = (T + BM - 1) / BM;
     const int BH = gridDim.x / nqt;
     int qt, bh;
     tile_of_block(BH, nqt, causal != 0, qt, bh);
@@ -180,85 +196,126 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
     const uint16_t* kbase = qbase + C;
     const uint16_t* vbase = qbase + 2 * (size_t)C;
 
-    const int qrow = qt * kTile + 16 * L.w + L.r16;
-    bf16x8 qreg[G::KSTEPS];
+    const int r0 = qt * BM + L.w * R;   // this wave's first query row
+    bf16x8 qreg[QB][G::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < G::KSTEPS; ++s)
-        qreg[s] = load_kchunk_global<HS>(qbase + (size_t)qrow * C3, qrow < T, s, L.g);
-
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 o[G::MB];
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = r0 + 16 * qb + L.r16;
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < G::KSTEPS; ++s)
+            qreg[qb][s] = row_chunk_global<HS>(qbase + (size_t)q * C3, q < T, s, L.g);
+    }
 
-    const int nkt = causal ? (qt + 1) : nqt;
+    float m[QB], lsum[QB];
+    f32x4 o[QB][G::MB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb) o[qb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nkt_all = (T + kStream - 1) / kStream;
+    const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    TileRegs<HS> rk, rv;
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    rv.fetch(vbase, C3, 0, T, L.tid);
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
-        stage_tile_bf16<HS, true, false>(Ks, nullptr, kbase, C3, kt * kTile, T, L.tid);
-        stage_tile_bf16<HS, false, true>(nullptr, Vt, vbase, C3, kt * kTile, T, L.tid);
+        rk.store(Ks, L.tid);
+        rv.store(Vs, L.tid);
         __syncthreads();
+        if (kt + 1 < nkt) {
+            rk.fetch(kbase, C3, (kt + 1) * kStream, T, L.tid);
+            rv.fetch(vbase, C3, (kt + 1) * kStream, T, L.tid);
+        }
+        const int k0 = kt * kStream;
+        if (causal && k0 > r0 + R - 1) continue;   // every key after every row of this wave
+        const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 
-        f32x4 s[G::NB];
+        // S^T blocks: s[qb][n][i] = S[r0 + 16qb + r16][k0 + 16n + 4g + i]
+        f32x4 s[QB][4];
 #pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* kr = Ks + (16 * n + L.r16) * G::LDR;
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int st = 0; st < G::KSTEPS; ++st)
-                acc = mfma_bf16(load_kchunk_lds<HS>(kr, st, L.g), qreg[st], acc);
-            s[n] = acc;
+            for (int n = 0; n < 4; ++n) s[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+#pragma unroll
+            for (int st = 0; st < G::KSTEPS; ++st) {
+                const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[qb][n] = mfma_bf16(kc, qreg[qb][st], s[qb][n]);
+            }
         }
 
-        const bool edge = (kt == nkt - 1);
-        float mloc = -INFINITY;
 #pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = r0 + 16 * qb + L.r16;
+            if (edge) {   // keys >= lim are masked (select, not branch)
+                const int lim = causal ? min(T, row + 1) : T;
+                const int kb0 = k0 + 4 * L.g;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = s[n][i] * scale_log2;
-                if (edge) {
-                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
-                    if (kv >= T || (causal && kv > qrow)) x = -INFINITY;
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[qb][n][i] = (kb0 + 16 * n + i < lim) ? s[qb][n][i] : -INFINITY;
+            }
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[qb][n][i]);
+            mloc = group4_max(mloc) * scale_log2;
+            // Each row decides for itself (so a row's result depends on its
+            // own scores only); the wave skips the rescale when no row needs it.
+            const bool need = mloc > m[qb] + kLazyMax;
+            if (wave_any(need)) {
+                const float alpha = need ? fast_exp2(m[qb] - mloc) : 1.0f;   // m = -inf -> 0
+                m[qb] = need ? mloc : m[qb];
+                lsum[qb] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < G::MB; ++mb) o[qb][mb] *= alpha;
+            }
+            const float nm = -m[qb];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = fast_exp2(fmaf(s[qb][n][i], scale_log2, nm));
+                    s[qb][n][i] = p;
+                    lsum[qb] += p;
                 }
-                s[n][i] = x;
-                mloc = fmaxf(mloc, x);
             }
         }
-        mloc = group4_max(mloc);
-        const float mnew = fmaxf(m, mloc);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[n][i] - mnew);
-                s[n][i] = p;
-                psum += p;
-            }
-        }
-        lsum = lsum * alpha + psum;
-#pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb) o[mb] *= alpha;
 
         // O^T += V^T P^T, 32 keys per step
 #pragma unroll
-        for (int t = 0; t < G::NB / 2; ++t) {
-            const bf16x8 pb = pack_pair(s[2 * t], s[2 * t + 1]);
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 pb[QB];
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb)
-                o[mb] = mfma_bf16(load_trans_operand(Vt, 16 * mb + L.r16, t, L.g), pb, o[mb]);
+            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair(s[qb][2 * t], s[qb][2 * t + 1]);
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) {
+                const bf16x8 vop = col_operand<HS>(Vs, 32 * t, 16 * mb, L.l);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) o[qb][mb] = mfma_bf16(vop, pb[qb], o[qb][mb]);
+            }
         }
     }
 
-    const float ltot = group4_sum(lsum);
-    if (qrow < T) {
-        const float inv = 1.0f / ltot;
-        uint16_t* orow = out + ((size_t)b * T + qrow) * C + (size_t)h * HS;
 #pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(orow + 16 * mb + 4 * L.g, o[mb] * inv);
-        if (L.g == 0) lse[(size_t)bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = r0 + 16 * qb + L.r16;
+        const float ltot = group4_sum(lsum[qb]);
+        if (row < T) {
+            const float inv = 1.0f / ltot;
+            uint16_t* orow = out + ((size_t)b * T + row) * C + (size_t)h * HS;
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(orow + 16 * mb + 4 * L.g, o[qb][mb] * inv);
+            if (L.g == 0) lse[(size_t)bh * T + row] = (m[qb] + __log2f(ltot)) * kLn2;
+        }
     }
 }
 
@@ -296,25 +353,27 @@ __global__ __launch_bounds__(kThreads) void prepass_bf16_kernel(float* __restric
 }
 
 // ----------------------------------------------------- backward dK / dV
-template <int HS>
+// Workgroup: a 4*R-row K/V tile of one head (R = 16*KB rows per wave, kept
+// in registers); Q and dO stream through LDS 64 rows at a time.
+template <int HS, int KB>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
     float scale_log2) {
-    using G = BfGeom<HS>;
-    __shared__ uint16_t Qs[kTile * G::LDR];
-    __shared__ uint16_t dOs[kTile * G::LDR];
-    __shared__ uint16_t Qt[HS * kLDT];
-    __shared__ uint16_t dOt[HS * kLDT];
-    __shared__ float Ls[kTile];
-    __shared__ float Dl[kTile];
+    using G = Geom<HS>;
+    constexpr int R = 16 * KB;
+    constexpr int BN = 4 * R;
+    __shared__ uint16_t Qs[kStream * G::LDR];
+    __shared__ uint16_t dOs[kStream * G::LDR];
+    __shared__ float Ls[kStream];
+    __shared__ float Dl[kStream];
 
     const Lane L;
-    const int nt = (T + kTile - 1) / kTile;
-    const int BH = gridDim.x / nt;
-    int kt, bh;
-    tile_of_block(BH, nt, false, kt, bh);
+    const int nkvt = (T + BN - 1) / BN;
+    const int BH = gridDim.x / nkvt;
+    int kvt, bh;
+    tile_of_block(BH, nkvt, false, kvt, bh);   // kvt = 0 sees the most queries
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -324,96 +383,145 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
     const float* lrow = lse + (size_t)bh * T;
     const float* drow = Dws + (size_t)bh * T;
 
-    const int kvrow = kt * kTile + 16 * L.w + L.r16;
-    bf16x8 kreg[G::KSTEPS], vreg[G::KSTEPS];
+    const int c0 = kvt * BN + L.w * R;   // this wave's first key row
+    bf16x8 kreg[KB][G::KSTEPS], vreg[KB][G::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < G::KSTEPS; ++s) {
-        kreg[s] = load_kchunk_global<HS>(kbase + (size_t)kvrow * C3, kvrow < T, s, L.g);
-        vreg[s] = load_kchunk_global<HS>(vbase + (size_t)kvrow * C3, kvrow < T, s, L.g);
-    }
-
-    f32x4 dk[G::MB], dv[G::MB];
+    for (int kb = 0; kb < KB; ++kb) {
+        const int kv = c0 + 16 * kb + L.r16;
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-        dk[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dv[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < G::KSTEPS; ++s) {
+            kreg[kb][s] = row_chunk_global<HS>(kbase + (size_t)kv * C3, kv < T, s, L.g);
+            vreg[kb][s] = row_chunk_global<HS>(vbase + (size_t)kv * C3, kv < T, s, L.g);
+        }
     }
+    f32x4 dk[KB][G::MB], dv[KB][G::MB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb) {
+            dk[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dv[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
-    const int qt0 = causal ? kt : 0;
-    for (int qt = qt0; qt < nt; ++qt) {
+    const int nqt = (T + kStream - 1) / kStream;
+    const int qt0 = causal ? (kvt * BN) / kStream : 0;
+    TileRegs<HS> rq, rd;
+    float rl = 0.f, rD = 0.f;
+    auto fetch = [&](int qt) {
+        rq.fetch(qbase, C3, qt * kStream, T, L.tid);
+        rd.fetch(dobase, (size_t)C, qt * kStream, T, L.tid);
+        if (L.tid < kStream) {
+            const int q = qt * kStream + L.tid;
+            rl = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
+            rD = (q < T) ? drow[q] : 0.f;
+        }
+    };
+    fetch(qt0);
+    for (int qt = qt0; qt < nqt; ++qt) {
         __syncthreads();
-        stage_tile_bf16<HS, true, true>(Qs, Qt, qbase, C3, qt * kTile, T, L.tid);
-        stage_tile_bf16<HS, true, true>(dOs, dOt, dobase, (size_t)C, qt * kTile, T, L.tid);
-        if (L.tid < kTile) {
-            const int q = qt * kTile + L.tid;
-            Ls[L.tid] = (q < T) ? lrow[q] * kLog2e : INFINITY;
-            Dl[L.tid] = (q < T) ? drow[q] : 0.f;
+        rq.store(Qs, L.tid);
+        rd.store(dOs, L.tid);
+        if (L.tid < kStream) {
+            Ls[L.tid] = rl;
+            Dl[L.tid] = rD;
         }
         __syncthreads();
-        const bool diag = causal && (qt == kt);
+        if (qt + 1 < nqt) fetch(qt + 1);
+        const int q0 = qt * kStream;
+        if (causal && q0 + kStream - 1 < c0) continue;   // every query before every key here
+        const bool diag = causal && (q0 < c0 + R - 1);
 
-        // p[n][i], ds[n][i] for q = qt*64 + 16n + 4g + i, kv = kvrow
-        f32x4 p[G::NB], ds[G::NB];
+        // p[kb][n][i], ds[kb][n][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16
+        f32x4 p[KB][4], ds[KB][4];
 #pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* qr = Qs + (16 * n + L.r16) * G::LDR;
-            const uint16_t* dr = dOs + (16 * n + L.r16) * G::LDR;
+        for (int n = 0; n < 4; ++n) {
+            f32x4 s[KB], dp[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int st = 0; st < G::KSTEPS; ++st) {
-                s = mfma_bf16(load_kchunk_lds<HS>(qr, st, L.g), kreg[st], s);
-                dp = mfma_bf16(load_kchunk_lds<HS>(dr, st, L.g), vreg[st], dp);
+                const bf16x8 qc = row_chunk_lds<HS>(Qs, 16 * n + L.r16, st, L.g);
+                const bf16x8 dc = row_chunk_lds<HS>(dOs, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    s[kb] = mfma_bf16(qc, kreg[kb][st], s[kb]);
+                    dp[kb] = mfma_bf16(dc, vreg[kb][st], dp[kb]);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ql = 16 * n + 4 * L.g + i;
-                float pv = fast_exp2(s[i] * scale_log2 - Ls[ql]);
-                if (diag && (qt * kTile + ql < kvrow)) pv = 0.f;
-                p[n][i] = pv;
-                ds[n][i] = pv * (dp[i] - Dl[ql]);
+                const float l2 = Ls[ql], dd = Dl[ql];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
+                    // causal: query q0 + ql sees key c0 + 16kb + r16 only if q >= kv
+                    pv = (!diag || q0 + ql >= c0 + 16 * kb + L.r16) ? pv : 0.f;
+                    p[kb][n][i] = pv;
+                    ds[kb][n][i] = pv * (dp[kb][i] - dd);
+                }
             }
         }
         // dV^T += dO^T P and dK^T += Q^T dS, 32 queries per step
 #pragma unroll
-        for (int t = 0; t < G::NB / 2; ++t) {
-            const bf16x8 pb = pack_pair(p[2 * t], p[2 * t + 1]);
-            const bf16x8 sb = pack_pair(ds[2 * t], ds[2 * t + 1]);
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 pb[KB], sb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                pb[kb] = pack_pair(p[kb][2 * t], p[kb][2 * t + 1]);
+                sb[kb] = pack_pair(ds[kb][2 * t], ds[kb][2 * t + 1]);
+            }
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                dv[mb] = mfma_bf16(load_trans_operand(dOt, 16 * mb + L.r16, t, L.g), pb, dv[mb]);
-                dk[mb] = mfma_bf16(load_trans_operand(Qt, 16 * mb + L.r16, t, L.g), sb, dk[mb]);
+                const bf16x8 dop = col_operand<HS>(dOs, 32 * t, 16 * mb, L.l);
+                const bf16x8 qop = col_operand<HS>(Qs, 32 * t, 16 * mb, L.l);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    dv[kb][mb] = mfma_bf16(dop, pb[kb], dv[kb][mb]);
+                    dk[kb][mb] = mfma_bf16(qop, sb[kb], dk[kb][mb]);
+                }
             }
         }
     }
 
-    if (kvrow < T) {
-        uint16_t* dkrow = dqkv + ((size_t)b * T + kvrow) * C3 + C + (size_t)h * HS;
-        uint16_t* dvrow = dkrow + C;
 #pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb) {
-            store_bf16x4(dkrow + 16 * mb + 4 * L.g, dk[mb] * scale);
-            store_bf16x4(dvrow + 16 * mb + 4 * L.g, dv[mb]);
+    for (int kb = 0; kb < KB; ++kb) {
+        const int kv = c0 + 16 * kb + L.r16;
+        if (kv < T) {
+            uint16_t* dkrow = dqkv + ((size_t)b * T + kv) * C3 + C + (size_t)h * HS;
+            uint16_t* dvrow = dkrow + C;
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) {
+                store_bf16x4(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
+                store_bf16x4(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
+            }
         }
     }
 }
 
 // ----------------------------------------------------------- backward dQ
-template <int HS>
+// Workgroup: a 4*R-row Q tile (R = 16*QB rows per wave, Q and dO in
+// registers); K and V stream through LDS 64 rows at a time.
+template <int HS, int QB>
 __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
     float scale_log2) {
-    using G = BfGeom<HS>;
-    __shared__ uint16_t Ks[kTile * G::LDR];
-    __shared__ uint16_t Kt[HS * kLDT];
-    __shared__ uint16_t Vs[kTile * G::LDR];
+    using G = Geom<HS>;
+    constexpr int R = 16 * QB;
+    constexpr int BM = 4 * R;
+    __shared__ uint16_t Ks[kStream * G::LDR];
+    __shared__ uint16_t Vs[kStream * G::LDR];
 
     const Lane L;
-    const int nt = (T + kTile - 1) / kTile;
-    const int BH = gridDim.x / nt;
+    const int nqt = (T + BM - 1) / BM;
+    const int BH = gridDim.x / nqt;
     int qt, bh;
-    tile_of_block(BH, nt, causal != 0, qt, bh);
+    tile_of_block(BH, nqt, causal != 0, qt, bh);
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -421,75 +529,116 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     const uint16_t* vbase = qbase + 2 * (size_t)C;
     const uint16_t* dobase = dout + (size_t)b * T * C + (size_t)h * HS;
 
-    const int qrow = qt * kTile + 16 * L.w + L.r16;
-    const bool qvalid = qrow < T;
-    bf16x8 qreg[G::KSTEPS], doreg[G::KSTEPS];
+    const int r0 = qt * BM + L.w * R;
+    bf16x8 qreg[QB][G::KSTEPS], doreg[QB][G::KSTEPS];
+    float l2[QB], Dq[QB];
 #pragma unroll
-    for (int s = 0; s < G::KSTEPS; ++s) {
-        qreg[s] = load_kchunk_global<HS>(qbase + (size_t)qrow * C3, qvalid, s, L.g);
-        doreg[s] = load_kchunk_global<HS>(dobase + (size_t)qrow * C, qvalid, s, L.g);
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = r0 + 16 * qb + L.r16;
+        const bool v = q < T;
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+            qreg[qb][s] = row_chunk_global<HS>(qbase + (size_t)q * C3, v, s, L.g);
+            doreg[qb][s] = row_chunk_global<HS>(dobase + (size_t)q * C, v, s, L.g);
+        }
+        l2[qb] = v ? lse[(size_t)bh * T + q] * kLog2e : INFINITY;
+        Dq[qb] = v ? Dws[(size_t)bh * T + q] : 0.f;
     }
-    const float l2 = qvalid ? lse[(size_t)bh * T + qrow] * kLog2e : INFINITY;
-    const float Dq = qvalid ? Dws[(size_t)bh * T + qrow] : 0.f;
-
-    f32x4 dq[G::MB];
+    f32x4 dq[QB][G::MB];
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) dq[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb) dq[qb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkt = causal ? (qt + 1) : nt;
+    const int nkt_all = (T + kStream - 1) / kStream;
+    const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    TileRegs<HS> rk, rv;
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    rv.fetch(vbase, C3, 0, T, L.tid);
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
-        stage_tile_bf16<HS, true, true>(Ks, Kt, kbase, C3, kt * kTile, T, L.tid);
-        stage_tile_bf16<HS, true, false>(Vs, nullptr, vbase, C3, kt * kTile, T, L.tid);
+        rk.store(Ks, L.tid);
+        rv.store(Vs, L.tid);
         __syncthreads();
-        const bool edge = (kt == nkt - 1);
+        if (kt + 1 < nkt) {
+            rk.fetch(kbase, C3, (kt + 1) * kStream, T, L.tid);
+            rv.fetch(vbase, C3, (kt + 1) * kStream, T, L.tid);
+        }
+        const int k0 = kt * kStream;
+        if (causal && k0 > r0 + R - 1) continue;
+        const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 
-        f32x4 ds[G::NB];
+        // ds[qb][n][i] for q = r0 + 16qb + r16, kv = k0 + 16n + 4g + i
+        f32x4 ds[QB][4];
 #pragma unroll
-        for (int n = 0; n < G::NB; ++n) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* kr = Ks + (16 * n + L.r16) * G::LDR;
-            const uint16_t* vr = Vs + (16 * n + L.r16) * G::LDR;
+        for (int n = 0; n < 4; ++n) {
+            f32x4 s[QB], dp[QB];
 #pragma unroll
-            for (int st = 0; st < G::KSTEPS; ++st) {
-                s = mfma_bf16(load_kchunk_lds<HS>(kr, st, L.g), qreg[st], s);
-                dp = mfma_bf16(load_kchunk_lds<HS>(vr, st, L.g), doreg[st], dp);
+            for (int qb = 0; qb < QB; ++qb) {
+                s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float pv = fast_exp2(s[i] * scale_log2 - l2);
-                if (edge) {
-                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
-                    if (kv >= T || (causal && kv > qrow)) pv = 0.f;
+            for (int st = 0; st < G::KSTEPS; ++st) {
+                const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
+                const bf16x8 vc = row_chunk_lds<HS>(Vs, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    s[qb] = mfma_bf16(kc, qreg[qb][st], s[qb]);
+                    dp[qb] = mfma_bf16(vc, doreg[qb][st], dp[qb]);
                 }
-                ds[n][i] = pv * (dp[i] - Dq);
+            }
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int row = r0 + 16 * qb + L.r16;
+                const int lim = edge ? (causal ? min(T, row + 1) : T) : 0x7fffffff;
+                const int kb0 = k0 + 16 * n + 4 * L.g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
+                    pv = (kb0 + i < lim) ? pv : 0.f;
+                    ds[qb][n][i] = pv * (dp[qb][i] - Dq[qb]);
+                }
             }
         }
         // dQ^T += K^T dS^T, 32 keys per step
 #pragma unroll
-        for (int t = 0; t < G::NB / 2; ++t) {
-            const bf16x8 sb = pack_pair(ds[2 * t], ds[2 * t + 1]);
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 sb[QB];
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb)
-                dq[mb] = mfma_bf16(load_trans_operand(Kt, 16 * mb + L.r16, t, L.g), sb, dq[mb]);
+            for (int qb = 0; qb < QB; ++qb) sb[qb] = pack_pair(ds[qb][2 * t], ds[qb][2 * t + 1]);
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) {
+                const bf16x8 kop = col_operand<HS>(Ks, 32 * t, 16 * mb, L.l);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) dq[qb][mb] = mfma_bf16(kop, sb[qb], dq[qb][mb]);
+            }
         }
     }
 
-    if (qvalid) {
-        uint16_t* dqrow = dqkv + ((size_t)b * T + qrow) * C3 + (size_t)h * HS;
 #pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(dqrow + 16 * mb + 4 * L.g, dq[mb] * scale);
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = r0 + 16 * qb + L.r16;
+        if (q < T) {
+            uint16_t* dqrow = dqkv + ((size_t)b * T + q) * C3 + (size_t)h * HS;
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(dqrow + 16 * mb + 4 * L.g, dq[qb][mb] * scale);
+        }
     }
 }
+
+constexpr int kQB = 2;   // 16-row blocks per wave in the forward and dQ kernels
+constexpr int kKB = 2;   // 16-row blocks per wave in the dK/dV kernel
 
 template <int HS>
 hipError_t fwd_bf16_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                        hipStream_t st) {
-    const int nqt = (s.T + kTile - 1) / kTile;
+    constexpr int BM = 64 * kQB;
+    const int nqt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nqt * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
-    hipLaunchKernelGGL(fwd_bf16_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, out, lse, qkv, s.T,
-                       s.C, s.NH, s.causal, scale_log2);
+    hipLaunchKernelGGL((fwd_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
+                       qkv, s.T, s.C, s.NH, s.causal, scale_log2);
     return hipGetLastError();
 }
 
@@ -507,22 +656,24 @@ hipError_t prepass_bf16_hs(float* D, const uint16_t* dout, const uint16_t* out, 
 template <int HS>
 hipError_t dkdv_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                         const float* lse, const float* D, const Shape& s, hipStream_t st) {
-    const int nt = (s.T + kTile - 1) / kTile;
+    constexpr int BN = 64 * kKB;
+    const int nt = (s.T + BN - 1) / BN;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout,
-                       qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<HS, kKB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
     return hipGetLastError();
 }
 
 template <int HS>
 hipError_t dq_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv, const float* lse,
                       const float* D, const Shape& s, hipStream_t st) {
-    const int nt = (s.T + kTile - 1) / kTile;
+    constexpr int BM = 64 * kQB;
+    const int nt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(bwd_dq_bf16_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
     return hipGetLastError();
 }
 

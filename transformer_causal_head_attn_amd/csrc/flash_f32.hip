@@ -35,6 +35,8 @@ namespace {
 
 constexpr int kTile = 64;      // rows per Q tile and per K/V tile
 constexpr int kThreads = 256;  // 4 waves
+// The forward and dQ kernels ask for >= 3 resident waves per SIMD (a
+// register cap); the dK/dV kernel does better with more registers.
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -47,21 +49,33 @@ struct Lane {
     }
 };
 
-// Copy a kTile x HS fp32 tile (rows row0.., row stride `ld` floats) from
-// global memory into LDS (row stride LDK), zero-filling rows >= T.
-template <int HS, int LDK>
-__device__ __forceinline__ void load_tile_f32(float* lds, const float* base, size_t ld,
-                                              int row0, int T, int tid) {
-    constexpr int C4 = HS / 4;
+// A kTile x HS fp32 tile held in registers between its global load and its
+// LDS store, so the load of the next tile overlaps the current tile's math.
+template <int HS>
+struct TileRegs {
+    static constexpr int C4 = HS / 4;
+    static constexpr int N = kTile * C4 / kThreads;   // float4 per thread
+    float4 v[N];
+    __device__ __forceinline__ void fetch(const float* base, size_t ld, int row0, int T, int tid) {
 #pragma unroll
-    for (int e = tid; e < kTile * C4; e += kThreads) {
-        const int row = e / C4, c4 = e % C4;
-        const int j = row0 + row;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < T) v = *reinterpret_cast<const float4*>(base + (size_t)j * ld + 4 * c4);
-        *reinterpret_cast<float4*>(lds + row * LDK + 4 * c4) = v;
+        for (int k = 0; k < N; ++k) {
+            const int e = tid + k * kThreads;
+            const int row = e / C4, c4 = e % C4;
+            const int j = row0 + row;
+            v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < T) v[k] = *reinterpret_cast<const float4*>(base + (size_t)j * ld + 4 * c4);
+        }
     }
-}
+    template <int LDK>
+    __device__ __forceinline__ void store(float* lds, int tid) const {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int e = tid + k * kThreads;
+            const int row = e / C4, c4 = e % C4;
+            *reinterpret_cast<float4*>(lds + row * LDK + 4 * c4) = v[k];
+        }
+    }
+};
 
 // Load this lane's HS/4 contiguous values of one row (k = (HS/4)*g + s).
 template <int HS>
@@ -91,7 +105,7 @@ __device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_fir
 
 // ------------------------------------------------------------------ forward
 template <int HS>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(float* __restrict__ out,
+__global__ __launch_bounds__(kThreads, 3) void fwd_f32_kernel(float* __restrict__ out,
                                                            float* __restrict__ lse,
                                                            const float* __restrict__ qkv, int T,
                                                            int C, int NH, int causal,
@@ -125,11 +139,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(float* __restrict__ o
     for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nkt = causal ? (qt + 1) : nqt;
+    TileRegs<HS> rk, rv;
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    rv.fetch(vbase, C3, 0, T, L.tid);
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
-        load_tile_f32<HS, LDK>(Ks, kbase, C3, kt * kTile, T, L.tid);
-        load_tile_f32<HS, LDK>(Vs, vbase, C3, kt * kTile, T, L.tid);
+        rk.template store<LDK>(Ks, L.tid);
+        rv.template store<LDK>(Vs, L.tid);
         __syncthreads();
+        if (kt + 1 < nkt) {   // next tile's loads fly while this one is used
+            rk.fetch(kbase, C3, (kt + 1) * kTile, T, L.tid);
+            rv.fetch(vbase, C3, (kt + 1) * kTile, T, L.tid);
+        }
 
         // S^T blocks: s[n][i] = S[qrow][kt*64 + 16n + 4g + i]
         f32x4 s[NB];
@@ -148,18 +169,16 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(float* __restrict__ o
             s[n] = acc;
         }
 
-        // scale, mask (only the last tile holds the diagonal and the tail)
-        const bool edge = (kt == nkt - 1);
+        // keys >= lim are masked; only the last tile holds the diagonal and
+        // the tail (select, not branch)
+        const int lim = (kt == nkt - 1) ? (causal ? min(T, qrow + 1) : T) : 0x7fffffff;
+        const int kb0 = kt * kTile + 4 * L.g;
         float mloc = -INFINITY;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = s[n][i] * scale_log2;
-                if (edge) {
-                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
-                    if (kv >= T || (causal && kv > qrow)) x = -INFINITY;
-                }
+                const float x = (kb0 + 16 * n + i < lim) ? s[n][i] * scale_log2 : -INFINITY;
                 s[n][i] = x;
                 mloc = fmaxf(mloc, x);
             }
@@ -281,16 +300,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
     }
 
     const int qt0 = causal ? kt : 0;
-    for (int qt = qt0; qt < nt; ++qt) {
-        __syncthreads();
-        load_tile_f32<HS, LDK>(Qs, qbase, C3, qt * kTile, T, L.tid);
-        load_tile_f32<HS, LDK>(dOs, dobase, (size_t)C, qt * kTile, T, L.tid);
+    TileRegs<HS> rq, rd;
+    float rl = 0.f, rD = 0.f;
+    auto fetch = [&](int qt) {
+        rq.fetch(qbase, C3, qt * kTile, T, L.tid);
+        rd.fetch(dobase, (size_t)C, qt * kTile, T, L.tid);
         if (L.tid < kTile) {
             const int q = qt * kTile + L.tid;
-            Ls[L.tid] = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
-            Dl[L.tid] = (q < T) ? drow[q] : 0.f;
+            rl = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
+            rD = (q < T) ? drow[q] : 0.f;
+        }
+    };
+    fetch(qt0);
+    for (int qt = qt0; qt < nt; ++qt) {
+        __syncthreads();
+        rq.template store<LDK>(Qs, L.tid);
+        rd.template store<LDK>(dOs, L.tid);
+        if (L.tid < kTile) {
+            Ls[L.tid] = rl;
+            Dl[L.tid] = rD;
         }
         __syncthreads();
+        if (qt + 1 < nt) fetch(qt + 1);
         const bool diag = causal && (qt == kt);
 
 #pragma unroll
@@ -317,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int ql = 16 * n + 4 * L.g + i;
                 float pv = fast_exp2(s[i] * scale_log2 - Ls[ql]);
-                if (diag && (qt * kTile + ql < kvrow)) pv = 0.f;
+                pv = (!diag || qt * kTile + ql >= kvrow) ? pv : 0.f;   // causal: q >= kv
                 p[i] = pv;
                 ds[i] = pv * (dp[i] - Dl[ql]);
             }
@@ -353,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
 // Per K/V tile: S^T = K Q^T, P, dP^T = V dO^T, dS = P * (dP - D),
 // dQ^T += K^T dS^T (scale applied at the end).
 template <int HS>
-__global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(
+__global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
     float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
     int causal, float scale, float scale_log2) {
@@ -389,12 +420,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(
     for (int mb = 0; mb < MB; ++mb) dq[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nkt = causal ? (qt + 1) : nt;
+    TileRegs<HS> rk, rv;
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    rv.fetch(vbase, C3, 0, T, L.tid);
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
-        load_tile_f32<HS, LDK>(Ks, kbase, C3, kt * kTile, T, L.tid);
-        load_tile_f32<HS, LDK>(Vs, vbase, C3, kt * kTile, T, L.tid);
+        rk.template store<LDK>(Ks, L.tid);
+        rv.template store<LDK>(Vs, L.tid);
         __syncthreads();
-        const bool edge = (kt == nkt - 1);
+        if (kt + 1 < nkt) {
+            rk.fetch(kbase, C3, (kt + 1) * kTile, T, L.tid);
+            rv.fetch(vbase, C3, (kt + 1) * kTile, T, L.tid);
+        }
+        const int lim = (kt == nkt - 1) ? (causal ? min(T, qrow + 1) : T) : 0x7fffffff;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
             // s[i] = S[qrow][kv = kt*64 + 16n + 4g + i], dp likewise
@@ -415,13 +453,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(
                 dp = mfma_f32(va.w, doreg[4 * c + 3], dp);
             }
             float ds[4];
+            const int kb0 = kt * kTile + 16 * n + 4 * L.g;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float pv = fast_exp2(s[i] * scale_log2 - l2);
-                if (edge) {
-                    const int kv = kt * kTile + 16 * n + 4 * L.g + i;
-                    if (kv >= T || (causal && kv > qrow)) pv = 0.f;
-                }
+                pv = (kb0 + i < lim) ? pv : 0.f;
                 ds[i] = pv * (dp[i] - Dq);
             }
 #pragma unroll
