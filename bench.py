@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention path on one MI355X.
 
-One step = one forward (attn_forward) plus one backward (pre-pass, dK/dV
-kernel, dQ kernel) over the workload's synthetic batch, inputs resident in
-device memory.  Prints one JSON line.
+One step = one forward (attn_forward) plus one backward (dQ kernel, which
+also forms D = rowsum(dO*O), then dK/dV kernel) over the workload's
+synthetic batch, inputs resident in device memory.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16]
 
@@ -37,7 +37,8 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=60,
+                   help="untimed steps; the GPU needs ~20 ms of work to reach steady clocks")
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--dtype", choices=["f32", "bf16"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -68,13 +69,8 @@ def kernel_flops(w):
     (query, key) pair per contraction it performs."""
     u = 2 * w.hs * w.pairs * w.B * w.NH
     return {"fwd": 2 * u,       # S = Q K^T, O = P V
-            "prepass": 0,
             "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
-            "dq": 3 * u}        # S, dP, dQ = dS K
-
-
-def prepass_bytes(w, esize):
-    return 2 * w.B * w.T * w.C * esize + w.B * w.NH * w.T * 4
+            "dq": 3 * u}        # S, dP, dQ = dS K (plus the D = dO.O row sums)
 
 
 def source_sha(dtype):
@@ -109,14 +105,12 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     D = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
     sfx = "_bf16" if dtype == "bf16" else ""
     fwd = getattr(la, "attn_forward" + sfx)
-    pre = getattr(la, "attn_backward_preprocess" + sfx)
     dkdv = getattr(la, "attn_backward_dkdv" + sfx)
     dq = getattr(la, "attn_backward_dq" + sfx)
     c = int(w.causal)
     stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
-              ("prepass", lambda: pre(D, dout, out, B, T, C, NH)),
-              ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c)),
-              ("dq", lambda: dq(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
+              ("dq", lambda: dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c)),
+              ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
 
     for _ in range(warmup):
         for _, fn in stages:
@@ -233,16 +227,11 @@ def main():
     peak = PEAK_TFLOPS[dtype]
 
     kf = kernel_flops(w)
-    esize = 2 if dtype == "bf16" else 4
     kernels = {}
     for name, ms in per_kernel.items():
         rec = {"ms": round(ms, 5)}
-        if kf[name]:
-            rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
-            rec["frac_peak"] = round(rec["tflops"] / peak, 4)
-        else:
-            rec["gbs"] = round(prepass_bytes(w, esize) / (ms * 1e-3) / 1e9, 1)
-            rec["frac_hbm"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
+        rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
+        rec["frac_peak"] = round(rec["tflops"] / peak, 4)
         kernels[name] = rec
     dom = max(per_kernel, key=per_kernel.get)
     achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12

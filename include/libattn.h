@@ -85,8 +85,8 @@ int attn_forward(float* out, float* lse, const float* qkv,
 
 /*
  * Fused backward, fp32.  Reads dout (B,T,C), qkv, and the forward's out and
- * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  Runs a D = rowsum(dout*out)
- * pre-pass, a dK/dV kernel and a dQ kernel, all recomputing the
+ * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  Runs a dQ kernel (which also
+ * forms D = rowsum(dout*out)) and then a dK/dV kernel, both recomputing the
  * probabilities from lse.
  */
 int attn_backward(float* dqkv, const float* dout, const float* qkv,
@@ -94,24 +94,24 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   int B, int T, int C, int NH, int causal);
 
 /*
- * The three stages of attn_backward, for callers that want to time, order or
+ * The stages of attn_backward, for callers that want to time, order or
  * overlap them, or to own the D buffer (these calls allocate nothing):
- *   attn_backward_preprocess: D (B,NH,T) fp32 = rowsum over each head's hs
- *       columns of dout * out (D[t] = sum_j att[t,j] datt[t,j], the row term
- *       of the closed-form softmax gradient);
- *   attn_backward_dkdv: writes only the dk and dv thirds of dqkv;
- *   attn_backward_dq: writes only the dq third of dqkv.
- * dkdv and dq read D and lse; they may run in either order after the
- * pre-pass.  Running all three equals attn_backward.
+ *   attn_backward_dq: writes D (B,NH,T) fp32 = dout . out per row and head
+ *       (D[t] = sum_j att[t,j] datt[t,j], the row term of the closed-form
+ *       softmax gradient) and the dq third of dqkv;
+ *   attn_backward_dkdv: reads that D, writes the dk and dv thirds of dqkv.
+ * attn_backward runs dq then dkdv on the same stream.  attn_backward_preprocess
+ * computes D alone (the same value attn_backward_dq writes), for callers that
+ * run dkdv first or need D by itself.
  */
 int attn_backward_preprocess(float* D, const float* dout, const float* out,
                              int B, int T, int C, int NH);
+int attn_backward_dq(float* dqkv, float* D, const float* dout, const float* qkv,
+                     const float* out, const float* lse,
+                     int B, int T, int C, int NH, int causal);
 int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv,
                        const float* lse, const float* D,
                        int B, int T, int C, int NH, int causal);
-int attn_backward_dq(float* dqkv, const float* dout, const float* qkv,
-                     const float* lse, const float* D,
-                     int B, int T, int C, int NH, int causal);
 
 /*
  * Fused forward and backward with bfloat16 inputs and outputs and fp32
@@ -125,15 +125,15 @@ int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv,
 int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                        const uint16_t* out, const float* lse,
                        int B, int T, int C, int NH, int causal);
-/* bf16 versions of the three backward stages (D stays fp32). */
+/* bf16 versions of the backward stages (D stays fp32). */
 int attn_backward_preprocess_bf16(float* D, const uint16_t* dout, const uint16_t* out,
                                   int B, int T, int C, int NH);
+int attn_backward_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                          const uint16_t* out, const float* lse,
+                          int B, int T, int C, int NH, int causal);
 int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                             const float* lse, const float* D,
                             int B, int T, int C, int NH, int causal);
-int attn_backward_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                          const float* lse, const float* D,
-                          int B, int T, int C, int NH, int causal);
 
 /*
  * Materialised forward, fp32, as the pages' reference does it: writes the

@@ -59,8 +59,8 @@ def load(path: str | None = None):
                            ("attn_backward", 5), ("attn_backward_bf16", 5),
                            ("attn_forward_materialized", 4),
                            ("attn_backward_materialized", 6),
-                           ("attn_backward_dkdv", 5), ("attn_backward_dq", 5),
-                           ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 5)):
+                           ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
+                           ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6)):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * nptr + [i] * 5
             fn.restype = i
@@ -135,12 +135,12 @@ def attn_backward_dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
           *_dims(B, T, C, NH, causal))
 
 
-def attn_backward_dq(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+def attn_backward_dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
     f = torch.float32
     _call("attn_backward_dq", _check(dqkv, "dqkv", f, B * T * 3 * C),
-          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
-          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
-          *_dims(B, T, C, NH, causal))
+          _check(D, "D", f, B * NH * T), _check(dout, "dout", f, B * T * C),
+          _check(qkv, "qkv", f, B * T * 3 * C), _check(out, "out", f, B * T * C),
+          _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
 
 
 def attn_forward_bf16(out, lse, qkv, B, T, C, NH, causal) -> None:
@@ -172,12 +172,12 @@ def attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> Non
           *_dims(B, T, C, NH, causal))
 
 
-def attn_backward_dq_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+def attn_backward_dq_bf16(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
     h, f = torch.bfloat16, torch.float32
     _call("attn_backward_dq_bf16", _check(dqkv, "dqkv", h, B * T * 3 * C),
-          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
-          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
-          *_dims(B, T, C, NH, causal))
+          _check(D, "D", f, B * NH * T), _check(dout, "dout", h, B * T * C),
+          _check(qkv, "qkv", h, B * T * 3 * C), _check(out, "out", h, B * T * C),
+          _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
 
 
 def attn_forward_materialized(out, preatt, att, qkv, B, T, C, NH, causal) -> None:

@@ -183,9 +183,8 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
     const attn::Shape s = shape_of(B, T, C, NH, causal);
-    hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
+    hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
-    if (e == hipSuccess) e = attn::launch_dq_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward launch");
 }
 
@@ -215,18 +214,18 @@ int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv, const f
                     "attn_backward_dkdv launch");
 }
 
-int attn_backward_dq(float* dqkv, const float* dout, const float* qkv, const float* lse,
-                     const float* D, int B, int T, int C, int NH, int causal) {
+int attn_backward_dq(float* dqkv, float* D, const float* dout, const float* qkv, const float* out,
+                     const float* lse, int B, int T, int C, int NH, int causal) {
     const long long BT = (long long)B * T;
-    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}, {D, nbytes(BT * NH, 4), "D"}};
     const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
                         {qkv, nbytes(BT * 3 * C, 4), "qkv"},
-                        {lse, nbytes(BT * NH, 4), "lse"},
-                        {D, nbytes(BT * NH, 4), "D"}};
-    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+                        {out, nbytes(BT * C, 4), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 4, false);
     if (rc) return rc;
-    return launched(attn::launch_dq_f32(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
-                                        g_stream),
+    return launched(attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse,
+                                        shape_of(B, T, C, NH, causal), g_stream),
                     "attn_backward_dq launch");
 }
 
@@ -256,9 +255,8 @@ int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
     const attn::Shape s = shape_of(B, T, C, NH, causal);
-    hipError_t e = attn::launch_prepass_bf16(D, dout, out, s, g_stream);
+    hipError_t e = attn::launch_dq_bf16(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
-    if (e == hipSuccess) e = attn::launch_dq_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward_bf16 launch");
 }
 
@@ -289,19 +287,19 @@ int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t
                     "attn_backward_dkdv_bf16 launch");
 }
 
-int attn_backward_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                          const float* lse, const float* D, int B, int T, int C, int NH,
+int attn_backward_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                          const uint16_t* out, const float* lse, int B, int T, int C, int NH,
                           int causal) {
     const long long BT = (long long)B * T;
-    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}, {D, nbytes(BT * NH, 4), "D"}};
     const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
                         {qkv, nbytes(BT * 3 * C, 2), "qkv"},
-                        {lse, nbytes(BT * NH, 4), "lse"},
-                        {D, nbytes(BT * NH, 4), "D"}};
-    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+                        {out, nbytes(BT * C, 2), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 4, false);
     if (rc) return rc;
-    return launched(attn::launch_dq_bf16(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
-                                         g_stream),
+    return launched(attn::launch_dq_bf16(dqkv, D, dout, qkv, out, lse,
+                                         shape_of(B, T, C, NH, causal), g_stream),
                     "attn_backward_dq_bf16 launch");
 }
 

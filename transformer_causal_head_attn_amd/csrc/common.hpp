@@ -22,21 +22,26 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Wave64 lane exchange across the four 16-lane groups (xor 16, xor 32).
-__device__ __forceinline__ float xor_lanes(float x, int mask) {
-    return __shfl_xor(x, mask, 64);
-}
-
-// Maximum / sum over the four lanes l, l^16, l^32, l^48 that share l % 16.
+// Reductions over the four lanes l, l^16, l^32, l^48 that share l % 16,
+// with gfx950's lane-swap instructions (VALU, no LDS round trip):
+// v_permlane32_swap(x, x) returns (lower half, upper half) of the wave in
+// every lane position, v_permlane16_swap(x, x) (even row, odd row) of each
+// pair of 16-lane rows.  Every lane of a group ends with the same bits.
 __device__ __forceinline__ float group4_max(float x) {
-    x = fmaxf(x, xor_lanes(x, 16));
-    x = fmaxf(x, xor_lanes(x, 32));
-    return x;
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float x) {
-    x += xor_lanes(x, 16);
-    x += xor_lanes(x, 32);
-    return x;
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -75,8 +80,8 @@ hipError_t launch_prepass_f32(float* D, const float* dout, const float* out, con
                               hipStream_t st);
 hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
                            const float* D, const Shape& s, hipStream_t st);
-hipError_t launch_dq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
-                         const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_f32(float* dqkv, float* D, const float* dout, const float* qkv,
+                         const float* out, const float* lse, const Shape& s, hipStream_t st);
 // bf16 fused path (bf16 tensors as raw 16-bit patterns)
 hipError_t launch_fwd_bf16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                            hipStream_t st);
@@ -84,8 +89,8 @@ hipError_t launch_prepass_bf16(float* D, const uint16_t* dout, const uint16_t* o
                                const Shape& s, hipStream_t st);
 hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                             const float* lse, const float* D, const Shape& s, hipStream_t st);
-hipError_t launch_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                          const float* lse, const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                          const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
 // materialised fp32 path
 hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
                                    const Shape& s, hipStream_t st);

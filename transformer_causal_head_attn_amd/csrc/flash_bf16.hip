@@ -172,7 +172,8 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 
 // ------------------------------------------------------------------ forward
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
-// stream through LDS 64 at a time.
+// stream through LDS 64 at a time (one buffer; the next tile's registers
+// are loaded while the current tile is used).
 template <int HS, int QB>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
@@ -218,38 +219,29 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
 
     const int nkt_all = (T + kStream - 1) / kStream;
     const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
-    TileRegs<HS> rk, rv;
-    rk.fetch(kbase, C3, 0, T, L.tid);
-    rv.fetch(vbase, C3, 0, T, L.tid);
-    for (int kt = 0; kt < nkt; ++kt) {
-        __syncthreads();
-        rk.store(Ks, L.tid);
-        rv.store(Vs, L.tid);
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            rk.fetch(kbase, C3, (kt + 1) * kStream, T, L.tid);
-            rv.fetch(vbase, C3, (kt + 1) * kStream, T, L.tid);
-        }
-        const int k0 = kt * kStream;
-        if (causal && k0 > r0 + R - 1) continue;   // every key after every row of this wave
-        const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
+    // last key tile with a key <= some row of this wave
+    const int last = causal ? min(nkt - 1, (r0 + R - 1) / kStream) : nkt - 1;
 
-        // S^T blocks: s[qb][n][i] = S[r0 + 16qb + r16][k0 + 16n + 4g + i]
-        f32x4 s[QB][4];
+    auto scores = [&](const uint16_t* kt_lds, f32x4 (&sc)[QB][4]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) s[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < 4; ++n) sc[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
 #pragma unroll
             for (int st = 0; st < G::KSTEPS; ++st) {
-                const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
+                const bf16x8 kc = row_chunk_lds<HS>(kt_lds, 16 * n + L.r16, st, L.g);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb][n] = mfma_bf16(kc, qreg[qb][st], s[qb][n]);
+                for (int qb = 0; qb < QB; ++qb) sc[qb][n] = mfma_bf16(kc, qreg[qb][st], sc[qb][n]);
             }
         }
+    };
 
+    // softmax of tile j in place (scores -> probabilities), then O += P V
+    auto consume = [&](int j, f32x4 (&sc)[QB][4], const uint16_t* vt_lds) {
+        const int k0 = j * kStream;
+        const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int row = r0 + 16 * qb + L.r16;
@@ -260,13 +252,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
                 for (int n = 0; n < 4; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        s[qb][n][i] = (kb0 + 16 * n + i < lim) ? s[qb][n][i] : -INFINITY;
+                        sc[qb][n][i] = (kb0 + 16 * n + i < lim) ? sc[qb][n][i] : -INFINITY;
             }
             float mloc = -INFINITY;
 #pragma unroll
             for (int n = 0; n < 4; ++n)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[qb][n][i]);
+                for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[qb][n][i]);
             mloc = group4_max(mloc) * scale_log2;
             // Each row decides for itself (so a row's result depends on its
             // own scores only); the wave skips the rescale when no row needs it.
@@ -283,25 +275,44 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
             for (int n = 0; n < 4; ++n) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(fmaf(s[qb][n][i], scale_log2, nm));
-                    s[qb][n][i] = p;
+                    const float p = fast_exp2(fmaf(sc[qb][n][i], scale_log2, nm));
+                    sc[qb][n][i] = p;
                     lsum[qb] += p;
                 }
             }
         }
-
         // O^T += V^T P^T, 32 keys per step
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             bf16x8 pb[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair(s[qb][2 * t], s[qb][2 * t + 1]);
+            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair(sc[qb][2 * t], sc[qb][2 * t + 1]);
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                const bf16x8 vop = col_operand<HS>(Vs, 32 * t, 16 * mb, L.l);
+                const bf16x8 vop = col_operand<HS>(vt_lds, 32 * t, 16 * mb, L.l);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) o[qb][mb] = mfma_bf16(vop, pb[qb], o[qb][mb]);
             }
+        }
+    };
+
+    TileRegs<HS> rk, rv;
+    {
+        f32x4 sc[QB][4];
+        rk.fetch(kbase, C3, 0, T, L.tid);
+        rv.fetch(vbase, C3, 0, T, L.tid);
+        for (int j = 0; j < nkt; ++j) {
+            __syncthreads();
+            rk.store(Ks, L.tid);
+            rv.store(Vs, L.tid);
+            __syncthreads();
+            if (j + 1 < nkt) {
+                rk.fetch(kbase, C3, (j + 1) * kStream, T, L.tid);
+                rv.fetch(vbase, C3, (j + 1) * kStream, T, L.tid);
+            }
+            if (j > last) continue;
+            scores(Ks, sc);
+            consume(j, sc, Vs);
         }
     }
 
@@ -504,12 +515,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
 
 // ----------------------------------------------------------- backward dQ
 // Workgroup: a 4*R-row Q tile (R = 16*QB rows per wave, Q and dO in
-// registers); K and V stream through LDS 64 rows at a time.
+// registers); K and V stream through LDS 64 rows at a time.  It first forms
+// D = dO . O for its rows and writes it out for the dK/dV kernel, which runs
+// after it.
 template <int HS, int QB>
 __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
-    uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
-    const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
-    const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
+    uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
     float scale_log2) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
@@ -542,7 +555,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
             doreg[qb][s] = row_chunk_global<HS>(dobase + (size_t)q * C, v, s, L.g);
         }
         l2[qb] = v ? lse[(size_t)bh * T + q] * kLog2e : INFINITY;
-        Dq[qb] = v ? Dws[(size_t)bh * T + q] : 0.f;
+        // D = dO . O for this row (the pre-pass, fused): the lane's columns,
+        // then the four lanes of the row; written for the dK/dV kernel.
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+            const bf16x8 oc = row_chunk_global<HS>(out + ((size_t)b * T + q) * C + (size_t)h * HS, v, s, L.g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)doreg[qb][s][e], (float)oc[e], acc);
+        }
+        Dq[qb] = group4_sum(acc);
+        if (v && L.g == 0) Dws[(size_t)bh * T + q] = Dq[qb];
     }
     f32x4 dq[QB][G::MB];
 #pragma unroll
@@ -627,8 +650,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     }
 }
 
-constexpr int kQB = 2;   // 16-row blocks per wave in the forward and dQ kernels
-constexpr int kKB = 2;   // 16-row blocks per wave in the dK/dV kernel
+// 16-row blocks per wave (measured on the GPT-2, ViT and long-context
+// shapes: 2 beats 1 and 4 in the forward, dQ and dK/dV kernels)
+constexpr int kQB = 2;
+constexpr int kKB = 2;
 
 template <int HS>
 hipError_t fwd_bf16_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
@@ -666,14 +691,14 @@ hipError_t dkdv_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qk
 }
 
 template <int HS>
-hipError_t dq_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv, const float* lse,
-                      const float* D, const Shape& s, hipStream_t st) {
+hipError_t dq_bf16_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                      const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
-                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv, D,
+                       dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -703,9 +728,9 @@ hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t
     ATTN_DISPATCH_HS(dkdv_bf16_hs, dqkv, dout, qkv, lse, D, s, st)
 }
 
-hipError_t launch_dq_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                          const float* lse, const float* D, const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(dq_bf16_hs, dqkv, dout, qkv, lse, D, s, st)
+hipError_t launch_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                          const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dq_bf16_hs, dqkv, D, dout, qkv, out, lse, s, st)
 }
 
 #undef ATTN_DISPATCH_HS

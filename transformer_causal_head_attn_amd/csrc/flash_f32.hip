@@ -381,13 +381,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
 
 // ----------------------------------------------------------- backward dQ
 // One workgroup per (64-row Q tile, head); loops over the key tiles it sees.
-// Per K/V tile: S^T = K Q^T, P, dP^T = V dO^T, dS = P * (dP - D),
-// dQ^T += K^T dS^T (scale applied at the end).
+// It first forms D = dO . O for its rows (written out for the dK/dV kernel,
+// which runs after it).  Per K/V tile: S^T = K Q^T, P, dP^T = V dO^T,
+// dS = P * (dP - D), dQ^T += K^T dS^T (scale applied at the end).
 template <int HS>
 __global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
-    int causal, float scale, float scale_log2) {
+    float* __restrict__ dqkv, float* __restrict__ Dws, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ out, const float* __restrict__ lse,
+    int T, int C, int NH, int causal, float scale, float scale_log2) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
     constexpr int NB = kTile / 16;
@@ -413,7 +414,18 @@ __global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
     load_row_part<HS>(qreg, qbase + (size_t)qrow * C3, qvalid, L.g);
     load_row_part<HS>(doreg, dobase + (size_t)qrow * C, qvalid, L.g);
     const float l2 = qvalid ? lse[(size_t)bh * T + qrow] * kLog2e : INFINITY;
-    const float Dq = qvalid ? Dws[(size_t)bh * T + qrow] : 0.f;
+    // D = dO . O for this row (the pre-pass, fused): the lane's HS/4 columns,
+    // then the four lanes of the row; written for the dK/dV kernel.
+    float Dq;
+    {
+        float oreg[KS];
+        load_row_part<HS>(oreg, out + (size_t)b * T * C + (size_t)h * HS + (size_t)qrow * C, qvalid, L.g);
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) acc = fmaf(doreg[k], oreg[k], acc);
+        Dq = group4_sum(acc);
+        if (qvalid && L.g == 0) Dws[(size_t)bh * T + qrow] = Dq;
+    }
 
     f32x4 dq[MB];
 #pragma unroll
@@ -512,13 +524,13 @@ hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const f
 }
 
 template <int HS>
-hipError_t dq_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
-                     const float* D, const Shape& s, hipStream_t st) {
+hipError_t dq_f32_hs(float* dqkv, float* D, const float* dout, const float* qkv, const float* out,
+                     const float* lse, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, D, dout, qkv,
+                       out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -548,9 +560,9 @@ hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, con
     ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, dout, qkv, lse, D, s, st)
 }
 
-hipError_t launch_dq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
-                         const float* D, const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(dq_f32_hs, dqkv, dout, qkv, lse, D, s, st)
+hipError_t launch_dq_f32(float* dqkv, float* D, const float* dout, const float* qkv,
+                         const float* out, const float* lse, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dq_f32_hs, dqkv, D, dout, qkv, out, lse, s, st)
 }
 
 #undef ATTN_DISPATCH_HS
