@@ -15,7 +15,9 @@
 //           dv = att^T dO,  dq = dpreatt K,  dk = dpreatt^T Q
 //
 // The two row kernels are bound by memory traffic (each reads one or two
-// T x T matrices and writes one); the four products are matrix-core work.
+// T x T matrices and writes one; in causal mode the masked upper triangle is
+// only written, never read); the dense score products are bound by the fp32
+// matrix cores, the four products with an hs-wide operand by both.
 // In causal mode the products skip 64 x 64 blocks of att / dpreatt that lie
 // wholly above the diagonal and treat entries above the diagonal as 0, so
 // only the lower triangle of an att argument is ever read.
@@ -26,7 +28,6 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kThreads = 256;
-constexpr int kLDA = kTile + 4;   // LDS row stride of a 64 x 64 fp32 block
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -42,7 +43,9 @@ struct Lane {
 // ------------------------------------------- dense scores M = X Y^T per head
 // X rows t and Y rows j are hs-vectors inside packed tensors (row strides
 // ldx, ldy elements); M is the head's T x T row-major matrix.  One workgroup
-// per 64 x 64 block; each wave owns 16 rows of X in registers.
+// per 64-row strip of M: each wave keeps 16 rows of X in registers and the
+// workgroup walks the column tiles, staging Y through LDS with the next
+// tile's registers loaded while the current one is used.
 template <int HS>
 __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
                                                           const float* __restrict__ X,
@@ -51,12 +54,13 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
                                                           size_t batch_x, size_t batch_y) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
+    constexpr int C4 = HS / 4;
+    constexpr int NY = kTile * C4 / kThreads;   // Y float4 per thread per tile
     __shared__ float Ys[kTile * LDK];
     const Lane L;
     const int nt = (T + kTile - 1) / kTile;
-    const int ct = blockIdx.x % nt;
-    const int rt = (blockIdx.x / nt) % nt;
-    const int bh = blockIdx.x / (nt * nt);
+    const int rt = blockIdx.x % nt;
+    const int bh = blockIdx.x / nt;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const float* xb = X + (size_t)b * batch_x + (size_t)h * HS;
     const float* yb = Y + (size_t)b * batch_y + (size_t)h * HS;
@@ -72,39 +76,50 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
         xr[4 * c + 2] = v.z;
         xr[4 * c + 3] = v.w;
     }
-    constexpr int C4 = HS / 4;
-    for (int e = L.tid; e < kTile * C4; e += kThreads) {
-        const int row = e / C4, c4 = e % C4;
-        const int j = ct * kTile + row;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < T) v = *reinterpret_cast<const float4*>(yb + (size_t)j * ldy + 4 * c4);
-        *reinterpret_cast<float4*>(Ys + row * LDK + 4 * c4) = v;
-    }
-    __syncthreads();
-
+    float4 ry[NY];
+    auto fetch = [&](int ct) {
+#pragma unroll
+        for (int k = 0; k < NY; ++k) {
+            const int e = L.tid + k * kThreads;
+            const int j = ct * kTile + e / C4;
+            ry[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < T) ry[k] = *reinterpret_cast<const float4*>(yb + (size_t)j * ldy + 4 * (e % C4));
+        }
+    };
     float* mrow = M + ((size_t)bh * T + t) * T;
     const bool vec = (T % 4) == 0;
+    fetch(0);
+    for (int ct = 0; ct < nt; ++ct) {
+        __syncthreads();
 #pragma unroll
-    for (int n = 0; n < kTile / 16; ++n) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float* yr = Ys + (16 * n + L.r16) * LDK + KS * L.g;
-#pragma unroll
-        for (int c = 0; c < KS / 4; ++c) {
-            const float4 yy = *reinterpret_cast<const float4*>(yr + 4 * c);
-            acc = mfma_f32(yy.x, xr[4 * c + 0], acc);
-            acc = mfma_f32(yy.y, xr[4 * c + 1], acc);
-            acc = mfma_f32(yy.z, xr[4 * c + 2], acc);
-            acc = mfma_f32(yy.w, xr[4 * c + 3], acc);
+        for (int k = 0; k < NY; ++k) {
+            const int e = L.tid + k * kThreads;
+            *reinterpret_cast<float4*>(Ys + (e / C4) * LDK + 4 * (e % C4)) = ry[k];
         }
-        // acc[i] = M[t][ct*64 + 16n + 4g + i]
-        const int j0 = ct * kTile + 16 * n + 4 * L.g;
-        if (t < T) {
-            if (vec && j0 + 3 < T) {
-                *reinterpret_cast<float4*>(mrow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            } else {
+        __syncthreads();
+        if (ct + 1 < nt) fetch(ct + 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (j0 + i < T) mrow[j0 + i] = acc[i];
+        for (int n = 0; n < kTile / 16; ++n) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const float* yr = Ys + (16 * n + L.r16) * LDK + KS * L.g;
+#pragma unroll
+            for (int c = 0; c < KS / 4; ++c) {
+                const float4 yy = *reinterpret_cast<const float4*>(yr + 4 * c);
+                acc = mfma_f32(yy.x, xr[4 * c + 0], acc);
+                acc = mfma_f32(yy.y, xr[4 * c + 1], acc);
+                acc = mfma_f32(yy.z, xr[4 * c + 2], acc);
+                acc = mfma_f32(yy.w, xr[4 * c + 3], acc);
+            }
+            // acc[i] = M[t][ct*64 + 16n + 4g + i]
+            const int j0 = ct * kTile + 16 * n + 4 * L.g;
+            if (t < T) {
+                if (vec && j0 + 3 < T) {
+                    *reinterpret_cast<float4*>(mrow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (j0 + i < T) mrow[j0 + i] = acc[i];
+                }
             }
         }
     }
@@ -113,9 +128,16 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
 // ------------------------------------------ C = op(A) Bm per head (T x hs)
 // A is the head's T x T matrix (att or dpreatt); op(A) = A, or A^T when
 // TRANS.  Bm and C are hs-column slices of packed tensors (row strides ldb,
-// ldc).  Causal: A is lower triangular, so output row block rt needs the
-// contraction blocks kt <= rt (A) or kt >= rt (A^T); entries above the
-// diagonal are read as 0.
+// ldc).  A workgroup owns 64 output rows (16 per wave; two blocks per wave
+// measured slower: half the workgroups, fewer resident waves) and walks the
+// contraction in 64-wide blocks.  Causal: A is lower triangular, so the
+// output rows of block rt need contraction blocks up to the diagonal (A) or
+// from it (A^T); entries above the diagonal are read as 0.  op(A) = A reads
+// 16 contiguous values of a block row per lane (16-byte loads, row stride 68
+// floats); op(A) = A^T reads a block column (row stride 65 floats, so the
+// lanes hit distinct banks); Bm rows have stride hs+1 for the same reason.
+// The next A and Bm blocks are loaded into registers while the current ones
+// are used.
 template <int HS, bool TRANS>
 __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
                                                          const float* __restrict__ A,
@@ -123,65 +145,143 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
                                                          int NH, int causal, size_t ldb,
                                                          size_t ldc, size_t batch_b,
                                                          size_t batch_c) {
-    constexpr int LDB = HS + 4;
+    constexpr int RB = 1;                        // 16-row output blocks per wave
+    constexpr int BR = 4 * 16 * RB;              // output rows per workgroup (64)
+    // LDS A block: op(A) = A: BR rows x 64 contraction columns (stride 68);
+    // op(A) = A^T: 64 contraction rows x BR output columns (stride BR + 1).
+    constexpr int AROWS = TRANS ? kTile : BR;
+    constexpr int ACOLS = TRANS ? BR : kTile;
+    constexpr int LDA = TRANS ? BR + 1 : kTile + 4;
+    constexpr int LDB = HS + 1;
     constexpr int MB = HS / 16;
-    __shared__ float As[kTile * kLDA];
+    constexpr int NA4 = AROWS * ACOLS / 4 / kThreads;   // A float4 per thread per block
+    constexpr int C4 = HS / 4;
+    constexpr int NB4 = kTile * C4 / kThreads;          // Bm float4 per thread per block
+    __shared__ float As[AROWS * LDA];
     __shared__ float Bs[kTile * LDB];
     const Lane L;
-    const int nt = (T + kTile - 1) / kTile;
-    const int rt = blockIdx.x % nt;
-    const int bh = blockIdx.x / nt;
+    const int nrt = (T + BR - 1) / BR;
+    const int nkt = (T + kTile - 1) / kTile;
+    const int rt = blockIdx.x % nrt;
+    const int bh = blockIdx.x / nrt;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const float* Ah = A + (size_t)bh * T * T;
     const float* bb = Bm + (size_t)b * batch_b + (size_t)h * HS;
-    const int row = rt * kTile + 16 * L.w + L.r16;   // this lane's output row
+    const int row0 = rt * BR;
 
-    f32x4 o[MB];
+    f32x4 o[RB][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) o[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    int k0 = 0, k1 = nt;
+    int k0 = 0, k1 = nkt;
     if (causal) {
-        if (TRANS) k0 = rt;
-        else k1 = rt + 1;
+        if (TRANS) k0 = row0 / kTile;
+        else k1 = min(nkt, (row0 + BR - 1) / kTile + 1);
     }
+    float4 ra[NA4];
+    float4 rbv[NB4];
+    const bool vecA = (T % 4) == 0;
+    auto fetch = [&](int kt) {
+        const int R0 = TRANS ? kt * kTile : row0;   // A rows of the block
+        const int C0 = TRANS ? row0 : kt * kTile;   // A columns of the block
+        constexpr int CQ = ACOLS / 4;               // float4 per block row
+#pragma unroll
+        for (int k = 0; k < NA4; ++k) {
+            const int e = L.tid + k * kThreads;
+            const int gr = R0 + e / CQ, gc = C0 + 4 * (e % CQ);
+            float v[4];
+            if (vecA) {
+                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (gr < T && gc < T && (!causal || gc <= gr))
+                    q = *reinterpret_cast<const float4*>(Ah + (size_t)gr * T + gc);
+                v[0] = q.x;
+                v[1] = q.y;
+                v[2] = q.z;
+                v[3] = q.w;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v[u] = (gr < T && gc + u < T) ? Ah[(size_t)gr * T + gc + u] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (!causal || gc + u <= gr) ? v[u] : 0.f;
+            ra[k] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+#pragma unroll
+        for (int k = 0; k < NB4; ++k) {
+            const int e = L.tid + k * kThreads;
+            const int kk = kt * kTile + e / C4;
+            rbv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kk < T) rbv[k] = *reinterpret_cast<const float4*>(bb + (size_t)kk * ldb + 4 * (e % C4));
+        }
+    };
+    auto store = [&]() {
+        // LDS holds the A block as it lies in memory: As[r][c] = A[R0 + r][C0 + c]
+        constexpr int CQ = ACOLS / 4;
+#pragma unroll
+        for (int k = 0; k < NA4; ++k) {
+            const int e = L.tid + k * kThreads;
+            float* d = As + (e / CQ) * LDA + 4 * (e % CQ);
+            d[0] = ra[k].x;
+            d[1] = ra[k].y;
+            d[2] = ra[k].z;
+            d[3] = ra[k].w;
+        }
+#pragma unroll
+        for (int k = 0; k < NB4; ++k) {
+            const int e = L.tid + k * kThreads;
+            float* d = Bs + (e / C4) * LDB + 4 * (e % C4);
+            d[0] = rbv[k].x;
+            d[1] = rbv[k].y;
+            d[2] = rbv[k].z;
+            d[3] = rbv[k].w;
+        }
+    };
+    if (k0 < k1) fetch(k0);
     for (int kt = k0; kt < k1; ++kt) {
         __syncthreads();
-        // A block: rows R0.., cols C0.. of the T x T matrix
-        const int R0 = TRANS ? kt * kTile : rt * kTile;
-        const int C0 = TRANS ? rt * kTile : kt * kTile;
-        for (int e = L.tid; e < kTile * kTile; e += kThreads) {
-            const int r = e / kTile, c = e % kTile;
-            const int gr = R0 + r, gc = C0 + c;
-            float v = 0.f;
-            if (gr < T && gc < T && (!causal || gc <= gr)) v = Ah[(size_t)gr * T + gc];
-            As[r * kLDA + c] = v;
-        }
-        constexpr int C4 = HS / 4;
-        for (int e = L.tid; e < kTile * C4; e += kThreads) {
-            const int r = e / C4, c4 = e % C4;
-            const int k = kt * kTile + r;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k < T) v = *reinterpret_cast<const float4*>(bb + (size_t)k * ldb + 4 * c4);
-            *reinterpret_cast<float4*>(Bs + r * LDB + 4 * c4) = v;
-        }
+        store();
         __syncthreads();
+        if (kt + 1 < k1) fetch(kt + 1);
         // C^T[d][row] += sum_kk Bm[kk][d] * op(A)[row][kk],  kk = 16g + s
-        const int lr = 16 * L.w + L.r16;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const int kk = 16 * L.g + s;
-            const float a = TRANS ? As[kk * kLDA + lr] : As[lr * kLDA + kk];
+        for (int rb = 0; rb < RB; ++rb) {
+            const int lr = 16 * (L.w * RB + rb) + L.r16;   // output row within the block
+            float av[16];
+            if (TRANS) {   // op(A)[lr][kk] = A[kk][lr]: a block column
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) o[mb] = mfma_f32(Bs[kk * LDB + 16 * mb + L.r16], a, o[mb]);
+                for (int s2 = 0; s2 < 16; ++s2) av[s2] = As[(16 * L.g + s2) * LDA + lr];
+            } else {       // a block row, 16 contiguous values
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 q = *reinterpret_cast<const float4*>(As + lr * LDA + 16 * L.g + 4 * c);
+                    av[4 * c + 0] = q.x;
+                    av[4 * c + 1] = q.y;
+                    av[4 * c + 2] = q.z;
+                    av[4 * c + 3] = q.w;
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 16; ++s2) {
+                const int kk = 16 * L.g + s2;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    o[rb][mb] = mfma_f32(Bs[kk * LDB + 16 * mb + L.r16], av[s2], o[rb][mb]);
+            }
         }
     }
-    if (row < T) {
-        float* crow = Cm + (size_t)b * batch_c + (size_t)row * ldc + (size_t)h * HS;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            *reinterpret_cast<float4*>(crow + 16 * mb + 4 * L.g) =
-                make_float4(o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = row0 + 16 * (L.w * RB + rb) + L.r16;
+        if (row < T) {
+            float* crow = Cm + (size_t)b * batch_c + (size_t)row * ldc + (size_t)h * HS;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                *reinterpret_cast<float4*>(crow + 16 * mb + 4 * L.g) =
+                    make_float4(o[rb][mb][0], o[rb][mb][1], o[rb][mb][2], o[rb][mb][3]);
+        }
     }
 }
 
@@ -199,6 +299,53 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // att[t, j] = exp(scale*(preatt[t,j] - max)) / sum over j in U(t); 0 elsewhere.
+// Row held in registers as NV float4 per lane (T <= 256*NV, T % 4 == 0);
+// entries j > t of a causal row are never read (only written as 0).
+template <int NV>
+__global__ __launch_bounds__(kThreads) void softmax_rows_vec_kernel(
+    float* __restrict__ att, const float* __restrict__ pre, int T, long long rows, int causal,
+    float scale_log2) {
+    const long long r = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;
+    const int t = (int)(r % T);
+    const int nj = causal ? t + 1 : T;
+    const float* p = pre + (size_t)r * T;
+    float* a = att + (size_t)r * T;
+    float x[NV][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int j0 = 4 * (lane + 64 * v);
+        float4 q = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (j0 < nj) q = *reinterpret_cast<const float4*>(p + j0);
+        x[v][0] = (j0 + 0 < nj) ? q.x : -INFINITY;
+        x[v][1] = (j0 + 1 < nj) ? q.y : -INFINITY;
+        x[v][2] = (j0 + 2 < nj) ? q.z : -INFINITY;
+        x[v][3] = (j0 + 3 < nj) ? q.w : -INFINITY;
+        mx = fmaxf(mx, fmaxf(fmaxf(x[v][0], x[v][1]), fmaxf(x[v][2], x[v][3])));
+    }
+    const float M = wave_max(mx) * scale_log2;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[v][e] = fast_exp2(fmaf(x[v][e], scale_log2, -M));   // masked: exp2(-inf) = 0
+            sum += x[v][e];
+        }
+    const float inv = 1.0f / wave_sum(sum);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int j0 = 4 * (lane + 64 * v);
+        if (j0 < T)
+            *reinterpret_cast<float4*>(a + j0) =
+                make_float4(x[v][0] * inv, x[v][1] * inv, x[v][2] * inv, x[v][3] * inv);
+    }
+}
+
+// Same for any T: two passes over the row (running max and normaliser, then
+// the writes); scalar accesses.
 __global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float* __restrict__ att,
                                                                 const float* __restrict__ pre,
                                                                 int T, long long rows, int causal,
@@ -210,7 +357,6 @@ __global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float* __restric
     const int nj = causal ? t + 1 : T;
     const float* p = pre + (size_t)r * T;
     float* a = att + (size_t)r * T;
-    // pass 1: running max and normaliser (log2 domain)
     float m = -INFINITY, l = 0.f;
     for (int j = lane; j < nj; j += 64) {
         const float x = p[j] * scale_log2;
@@ -221,11 +367,58 @@ __global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float* __restric
     const float M = wave_max(m);
     l = (m == -INFINITY) ? 0.f : l * fast_exp2(m - M);
     const float inv = 1.0f / wave_sum(l);
-    // pass 2: write every entry of the row
     for (int j = lane; j < T; j += 64) a[j] = (j < nj) ? fast_exp2(p[j] * scale_log2 - M) * inv : 0.f;
 }
 
-// dpreatt[t, j] = scale * att * (datt - sum_{j' in U(t)} att datt) on U(t); 0 elsewhere.
+// dpreatt[t, j] = scale * att * (datt - sum_{j' in U(t)} att datt) on U(t); 0
+// elsewhere.  Rows held in registers as NV float4 per lane (T <= 256*NV,
+// T % 4 == 0): att and datt are read once; entries j > t of a causal row are
+// not read.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void softmax_bwd_rows_vec_kernel(
+    float* __restrict__ dpre, const float* __restrict__ att, const float* __restrict__ datt,
+    int T, long long rows, int causal, float scale) {
+    const long long r = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;
+    const int t = (int)(r % T);
+    const int nj = causal ? t + 1 : T;
+    const float* a = att + (size_t)r * T;
+    const float* d = datt + (size_t)r * T;
+    float* o = dpre + (size_t)r * T;
+    float av[NV][4], dv[NV][4];
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int j0 = 4 * (lane + 64 * v);
+        float4 qa = make_float4(0.f, 0.f, 0.f, 0.f), qd = qa;
+        if (j0 < nj) {
+            qa = *reinterpret_cast<const float4*>(a + j0);
+            qd = *reinterpret_cast<const float4*>(d + j0);
+        }
+        av[v][0] = (j0 + 0 < nj) ? qa.x : 0.f;
+        av[v][1] = (j0 + 1 < nj) ? qa.y : 0.f;
+        av[v][2] = (j0 + 2 < nj) ? qa.z : 0.f;
+        av[v][3] = (j0 + 3 < nj) ? qa.w : 0.f;
+        dv[v][0] = qd.x;
+        dv[v][1] = qd.y;
+        dv[v][2] = qd.z;
+        dv[v][3] = qd.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(av[v][e], dv[v][e], acc);
+    }
+    const float D = wave_sum(acc);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int j0 = 4 * (lane + 64 * v);
+        if (j0 < T)   // masked entries have av = 0 -> exact 0
+            *reinterpret_cast<float4*>(o + j0) = make_float4(
+                scale * av[v][0] * (dv[v][0] - D), scale * av[v][1] * (dv[v][1] - D),
+                scale * av[v][2] * (dv[v][2] - D), scale * av[v][3] * (dv[v][3] - D));
+    }
+}
+
+// Same for any T: two passes over the row; scalar accesses.
 __global__ __launch_bounds__(kThreads) void softmax_bwd_rows_kernel(
     float* __restrict__ dpre, const float* __restrict__ att, const float* __restrict__ datt,
     int T, long long rows, int causal, float scale) {
@@ -243,6 +436,37 @@ __global__ __launch_bounds__(kThreads) void softmax_bwd_rows_kernel(
     for (int j = lane; j < T; j += 64) o[j] = (j < nj) ? scale * a[j] * (d[j] - D) : 0.f;
 }
 
+hipError_t launch_softmax_bwd_rows(float* dpre, const float* att, const float* datt, int T,
+                                   long long rows, int causal, float scale, hipStream_t st) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), blk(kThreads);
+    if (T % 4 == 0 && T <= 4096) {
+        if (T <= 256) hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<1>, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+        else if (T <= 512) hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<2>, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+        else if (T <= 1024) hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<4>, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+        else if (T <= 2048) hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<8>, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+        else hipLaunchKernelGGL(softmax_bwd_rows_vec_kernel<16>, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+    } else {
+        hipLaunchKernelGGL(softmax_bwd_rows_kernel, grid, blk, 0, st, dpre, att, datt, T, rows, causal, scale);
+    }
+    return hipGetLastError();
+}
+
+// Launch the forward row softmax: register-resident rows when they fit.
+hipError_t launch_softmax_rows(float* att, const float* pre, int T, long long rows, int causal,
+                               float scale_log2, hipStream_t st) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), blk(kThreads);
+    if (T % 4 == 0 && T <= 4096) {
+        if (T <= 256) hipLaunchKernelGGL(softmax_rows_vec_kernel<1>, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+        else if (T <= 512) hipLaunchKernelGGL(softmax_rows_vec_kernel<2>, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+        else if (T <= 1024) hipLaunchKernelGGL(softmax_rows_vec_kernel<4>, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+        else if (T <= 2048) hipLaunchKernelGGL(softmax_rows_vec_kernel<8>, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+        else hipLaunchKernelGGL(softmax_rows_vec_kernel<16>, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+    } else {
+        hipLaunchKernelGGL(softmax_rows_kernel, grid, blk, 0, st, att, pre, T, rows, causal, scale_log2);
+    }
+    return hipGetLastError();
+}
+
 template <int HS>
 hipError_t fwd_hs(float* out, float* preatt, float* att, const float* qkv, const Shape& s,
                   hipStream_t st) {
@@ -250,18 +474,17 @@ hipError_t fwd_hs(float* out, float* preatt, float* att, const float* qkv, const
     const size_t C3 = 3 * (size_t)s.C;
     const size_t bstride = (size_t)s.T * C3;
     const long long BH = (long long)s.B * s.NH;
-    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt * nt)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
                        preatt, qkv, qkv + s.C, s.T, s.NH, C3, C3, bstride, bstride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = BH * s.T;
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st,
-                       att, preatt, s.T, rows, s.causal, scale * kLog2e);
-    e = hipGetLastError();
+    e = launch_softmax_rows(att, preatt, s.T, rows, s.causal, scale * kLog2e, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((apply_kernel<HS, false>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
-                       out, att, qkv + 2 * s.C, s.T, s.NH, s.causal, C3, (size_t)s.C, bstride,
+    const unsigned ga = (unsigned)(BH * nt);
+    hipLaunchKernelGGL((apply_kernel<HS, false>), dim3(ga), dim3(kThreads), 0, st, out, att,
+                       qkv + 2 * s.C, s.T, s.NH, s.causal, C3, (size_t)s.C, bstride,
                        (size_t)s.T * s.C);
     return hipGetLastError();
 }
@@ -275,15 +498,13 @@ hipError_t bwd_hs(float* dqkv, float* dpreatt, float* datt, const float* dout, c
     const size_t bq = (size_t)s.T * C3, bo = (size_t)s.T * C;
     const long long BH = (long long)s.B * s.NH;
     // datt = dO V^T
-    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt * nt)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
                        datt, dout, qkv + 2 * C, s.T, s.NH, C, C3, bo, bq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = BH * s.T;
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(softmax_bwd_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0,
-                       st, dpreatt, att, datt, s.T, rows, s.causal, scale);
-    e = hipGetLastError();
+    e = launch_softmax_bwd_rows(dpreatt, att, datt, s.T, rows, s.causal, scale, st);
     if (e != hipSuccess) return e;
     const unsigned g = (unsigned)(BH * nt);
     // dv = att^T dO
