@@ -73,6 +73,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Compute units of the current device (cached per device id).
+inline int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Whether causal tiles should run in balanced pairs (one light, one heavy per
+// workgroup): only while the paired grid keeps >= 2 workgroups per CU.
+inline bool pair_tiles(int ntiles, int causal, long long BH) {
+    return causal && ntiles > 1 && BH * ((ntiles + 1) / 2) >= 2LL * device_cu_count();
+}
+
 // ---- launchers (return hipSuccess or the launch error) ----
 // fp32 fused path
 hipError_t launch_fwd_f32(float* out, float* lse, const float* qkv, const Shape& s, hipStream_t st);

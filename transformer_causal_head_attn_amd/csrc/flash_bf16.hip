@@ -160,26 +160,44 @@ struct TileRegs {
     }
 };
 
-__device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_first_high,
-                                              int& tile, int& bh) {
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Causal tiles carry unequal work (tile i of a Q-tile kernel sees i+1 key
+// tiles, tile j of a K/V-tile kernel nt-j query tiles), so when the grid is
+// large enough one workgroup runs tiles i and nt-1-i back to back: every
+// workgroup then does nt+1 units and the grid has no tail.  Pairing halves
+// the grid, so it is used only while at least two paired workgroups per CU
+// remain (pair_tiles on the host).  Otherwise tiles run one per workgroup,
+// heaviest first (the longest-first order of kernel 8 in llm.c's
+// attention_backward.cu).
+// Consecutive workgroup ids walk the heads, so all tiles of a head land on
+// one XCD (one L2) whenever B*NH is a multiple of 8.
+__device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool heavy_high,
+                                              int& bh, int& ta, int& tb) {
     const int bid = blockIdx.x;
     const int rank = bid / BH;
     bh = bid - rank * BH;
-    tile = heavy_first_high ? (ntiles - 1 - rank) : rank;
+    if (paired) {
+        ta = rank;
+        tb = nt - 1 - rank;
+        if (tb == ta) tb = -1;
+    } else {   // heaviest tile first, so the last workgroups to start are short
+        ta = heavy_high ? nt - 1 - rank : rank;
+        tb = -1;
+    }
 }
 
-__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+__host__ __device__ inline int grid_tiles(int nt, bool paired) { return paired ? (nt + 1) / 2 : nt; }
 
 // ------------------------------------------------------------------ forward
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
 // stream through LDS 64 at a time (one buffer; the next tile's registers
 // are loaded while the current tile is used).
 template <int HS, int QB>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse,
-                                                            const uint16_t* __restrict__ qkv,
-                                                            int T, int C, int NH, int causal,
-                                                            float scale_log2) {
+__device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __restrict__ out,
+                                              float* __restrict__ lse,
+                                              const uint16_t* __restrict__ qkv, int T, int C,
+                                              int NH, int causal, float scale_log2) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
     constexpr int BM = 4 * R;
@@ -187,10 +205,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
     __shared__ uint16_t Vs[kStream * G::LDR];
 
     const Lane L;
-    const int nqt = (T + BM - 1) / BM;
-    const int BH = gridDim.x / nqt;
-    int qt, bh;
-    tile_of_block(BH, nqt, causal != 0, qt, bh);
+    const int qt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -367,8 +382,8 @@ __global__ __launch_bounds__(kThreads) void prepass_bf16_kernel(float* __restric
 // Workgroup: a 4*R-row K/V tile of one head (R = 16*KB rows per wave, kept
 // in registers); Q and dO stream through LDS 64 rows at a time.
 template <int HS, int KB>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
-    uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
+__device__ __forceinline__ void bwd_dkdv_bf16_tile(
+    int tile_, int bh_, uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
     float scale_log2) {
@@ -381,10 +396,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
     __shared__ float Dl[kStream];
 
     const Lane L;
-    const int nkvt = (T + BN - 1) / BN;
-    const int BH = gridDim.x / nkvt;
-    int kvt, bh;
-    tile_of_block(BH, nkvt, false, kvt, bh);   // kvt = 0 sees the most queries
+    const int kvt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -442,48 +454,51 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
         if (causal && q0 + kStream - 1 < c0) continue;   // every query before every key here
         const bool diag = causal && (q0 < c0 + R - 1);
 
-        // p[kb][n][i], ds[kb][n][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16
-        f32x4 p[KB][4], ds[KB][4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            f32x4 s[KB], dp[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int st = 0; st < G::KSTEPS; ++st) {
-                const bf16x8 qc = row_chunk_lds<HS>(Qs, 16 * n + L.r16, st, L.g);
-                const bf16x8 dc = row_chunk_lds<HS>(dOs, 16 * n + L.r16, st, L.g);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    s[kb] = mfma_bf16(qc, kreg[kb][st], s[kb]);
-                    dp[kb] = mfma_bf16(dc, vreg[kb][st], dp[kb]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ql = 16 * n + 4 * L.g + i;
-                const float l2 = Ls[ql], dd = Dl[ql];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
-                    // causal: query q0 + ql sees key c0 + 16kb + r16 only if q >= kv
-                    pv = (!diag || q0 + ql >= c0 + 16 * kb + L.r16) ? pv : 0.f;
-                    p[kb][n][i] = pv;
-                    ds[kb][n][i] = pv * (dp[kb][i] - dd);
-                }
-            }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS, 32 queries per step
+        // Two 16-query blocks n = 2t, 2t+1 at a time: scores and dP, then P and
+        // dS packed to bf16 and used at once for dV^T += dO^T P and
+        // dK^T += Q^T dS (32 queries per matrix-core step).
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            f32x4 p[KB][2], ds[KB][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int n = 2 * t + u;
+                // s[kb][i], dp[kb][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16
+                f32x4 s[KB], dp[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int st = 0; st < G::KSTEPS; ++st) {
+                    const bf16x8 qc = row_chunk_lds<HS>(Qs, 16 * n + L.r16, st, L.g);
+                    const bf16x8 dc = row_chunk_lds<HS>(dOs, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        s[kb] = mfma_bf16(qc, kreg[kb][st], s[kb]);
+                        dp[kb] = mfma_bf16(dc, vreg[kb][st], dp[kb]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ql = 16 * n + 4 * L.g + i;
+                    const float l2 = Ls[ql], dd = Dl[ql];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
+                        // causal: query q0 + ql sees key c0 + 16kb + r16 only if q >= kv
+                        pv = (!diag || q0 + ql >= c0 + 16 * kb + L.r16) ? pv : 0.f;
+                        p[kb][u][i] = pv;
+                        ds[kb][u][i] = pv * (dp[kb][i] - dd);
+                    }
+                }
+            }
             bf16x8 pb[KB], sb[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                pb[kb] = pack_pair(p[kb][2 * t], p[kb][2 * t + 1]);
-                sb[kb] = pack_pair(ds[kb][2 * t], ds[kb][2 * t + 1]);
+                pb[kb] = pack_pair(p[kb][0], p[kb][1]);
+                sb[kb] = pack_pair(ds[kb][0], ds[kb][1]);
             }
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
@@ -519,11 +534,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
 // D = dO . O for its rows and writes it out for the dK/dV kernel, which runs
 // after it.
 template <int HS, int QB>
-__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
-    uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
-    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
-    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
-    float scale_log2) {
+__device__ __forceinline__ void bwd_dq_bf16_tile(
+    int tile_, int bh_, uint16_t* __restrict__ dqkv, float* __restrict__ Dws,
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ qkv,
+    const uint16_t* __restrict__ out, const float* __restrict__ lse, int T, int C, int NH,
+    int causal, float scale, float scale_log2) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
     constexpr int BM = 4 * R;
@@ -531,10 +546,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     __shared__ uint16_t Vs[kStream * G::LDR];
 
     const Lane L;
-    const int nqt = (T + BM - 1) / BM;
-    const int BH = gridDim.x / nqt;
-    int qt, bh;
-    tile_of_block(BH, nqt, causal != 0, qt, bh);
+    const int qt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -591,45 +603,47 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
         if (causal && k0 > r0 + R - 1) continue;
         const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 
-        // ds[qb][n][i] for q = r0 + 16qb + r16, kv = k0 + 16n + 4g + i
-        f32x4 ds[QB][4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            f32x4 s[QB], dp[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int st = 0; st < G::KSTEPS; ++st) {
-                const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
-                const bf16x8 vc = row_chunk_lds<HS>(Vs, 16 * n + L.r16, st, L.g);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    s[qb] = mfma_bf16(kc, qreg[qb][st], s[qb]);
-                    dp[qb] = mfma_bf16(vc, doreg[qb][st], dp[qb]);
-                }
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int row = r0 + 16 * qb + L.r16;
-                const int lim = edge ? (causal ? min(T, row + 1) : T) : 0x7fffffff;
-                const int kb0 = k0 + 16 * n + 4 * L.g;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
-                    pv = (kb0 + i < lim) ? pv : 0.f;
-                    ds[qb][n][i] = pv * (dp[qb][i] - Dq[qb]);
-                }
-            }
-        }
-        // dQ^T += K^T dS^T, 32 keys per step
+        // Two 16-key blocks n = 2t, 2t+1 at a time: S^T and dP^T, then dS packed
+        // to bf16 and used at once for dQ^T += K^T dS^T (32 keys per step).
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            f32x4 ds[QB][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int n = 2 * t + u;
+                // s[qb][i], dp[qb][i] for q = r0 + 16qb + r16, kv = k0 + 16n + 4g + i
+                f32x4 s[QB], dp[QB];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int st = 0; st < G::KSTEPS; ++st) {
+                    const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
+                    const bf16x8 vc = row_chunk_lds<HS>(Vs, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        s[qb] = mfma_bf16(kc, qreg[qb][st], s[qb]);
+                        dp[qb] = mfma_bf16(vc, doreg[qb][st], dp[qb]);
+                    }
+                }
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int row = r0 + 16 * qb + L.r16;
+                    const int lim = edge ? (causal ? min(T, row + 1) : T) : 0x7fffffff;
+                    const int kb0 = k0 + 16 * n + 4 * L.g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
+                        pv = (kb0 + i < lim) ? pv : 0.f;
+                        ds[qb][u][i] = pv * (dp[qb][i] - Dq[qb]);
+                    }
+                }
+            }
             bf16x8 sb[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sb[qb] = pack_pair(ds[qb][2 * t], ds[qb][2 * t + 1]);
+            for (int qb = 0; qb < QB; ++qb) sb[qb] = pack_pair(ds[qb][0], ds[qb][1]);
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
                 const bf16x8 kop = col_operand<HS>(Ks, 32 * t, 16 * mb, L.l);
@@ -650,20 +664,74 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     }
 }
 
-// 16-row blocks per wave (measured on the GPT-2, ViT and long-context
-// shapes: 2 beats 1 and 4 in the forward, dQ and dK/dV kernels)
+// 16-row blocks per wave in the forward and dQ kernels (measured on the
+// GPT-2, ViT and long-context shapes: 2 beats 1 and 4)
+// ------------------------------------------------------------- kernels
+// Each runs its tile function on one tile, or on a balanced pair of causal
+// tiles (see pair_of_block).
+template <int HS, int QB>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict__ out,
+                                                            float* __restrict__ lse,
+                                                            const uint16_t* __restrict__ qkv,
+                                                            int T, int C, int NH, int causal,
+                                                            float scale_log2, int paired) {
+    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    fwd_bf16_tile<HS, QB>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        fwd_bf16_tile<HS, QB>(tb, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    }
+}
+
+template <int HS, int KB>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
+    uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
+    const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
+    float scale_log2, int paired) {
+    const int nt = (T + 64 * KB - 1) / (64 * KB);
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
+    bwd_dkdv_bf16_tile<HS, KB>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        bwd_dkdv_bf16_tile<HS, KB>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    }
+}
+
+template <int HS, int QB>
+__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
+    uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
+    float scale_log2, int paired) {
+    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    bwd_dq_bf16_tile<HS, QB>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        bwd_dq_bf16_tile<HS, QB>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    }
+}
+
 constexpr int kQB = 2;
-constexpr int kKB = 2;
+// dK/dV: 32 K/V rows per wave for hs <= 64, 16 for hs = 128 (fewer
+// registers, more resident waves; measured faster on the long-context shape)
+constexpr int kb_for(int hs) { return hs >= 128 ? 1 : 2; }
 
 template <int HS>
 hipError_t fwd_bf16_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                        hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nqt = (s.T + BM - 1) / BM;
-    const unsigned grid = (unsigned)(nqt * s.B * s.NH);
+    const bool paired = pair_tiles(nqt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
     hipLaunchKernelGGL((fwd_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
-                       qkv, s.T, s.C, s.NH, s.causal, scale_log2);
+                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)paired);
     return hipGetLastError();
 }
 
@@ -681,12 +749,15 @@ hipError_t prepass_bf16_hs(float* D, const uint16_t* dout, const uint16_t* out, 
 template <int HS>
 hipError_t dkdv_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                         const float* lse, const float* D, const Shape& s, hipStream_t st) {
-    constexpr int BN = 64 * kKB;
+    constexpr int KB = kb_for(HS);
+    constexpr int BN = 64 * KB;
     const int nt = (s.T + BN - 1) / BN;
-    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<HS, kKB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
-                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
+                       (int)paired);
     return hipGetLastError();
 }
 
@@ -695,10 +766,12 @@ hipError_t dq_bf16_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
                       const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nt = (s.T + BM - 1) / BM;
-    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv, D,
-                       dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+                       dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
+                       (int)paired);
     return hipGetLastError();
 }
 

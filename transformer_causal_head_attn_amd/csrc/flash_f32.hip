@@ -24,10 +24,11 @@
 //  * the contraction index k of every Q.K product is numbered
 //    k = (hs/4)*g + s for lane group g and step s, so each lane's operand
 //    values are contiguous and move with 16-byte loads;
-//  * causal work skips every key tile beyond the diagonal; workgroups are
-//    issued heaviest tile first so the causal tail does not idle CUs, and
-//    consecutive workgroup ids walk the heads so that all tiles of a head
-//    land on one XCD (one L2) whenever B*NH is a multiple of 8.
+//  * causal work skips every key tile beyond the diagonal, and a workgroup
+//    runs a light and a heavy causal tile back to back so all workgroups
+//    carry equal work (no tail); consecutive workgroup ids walk the heads so
+//    that all tiles of a head land on one XCD (one L2) whenever B*NH is a
+//    multiple of 8.
 #include "common.hpp"
 
 namespace attn {
@@ -35,8 +36,9 @@ namespace {
 
 constexpr int kTile = 64;      // rows per Q tile and per K/V tile
 constexpr int kThreads = 256;  // 4 waves
-// The forward and dQ kernels ask for >= 3 resident waves per SIMD (a
-// register cap); the dK/dV kernel does better with more registers.
+// The forward and dQ kernels ask for >= 3 resident waves per SIMD (2 for
+// hs = 128; a register cap); the dK/dV kernel does better with more
+// registers.
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -93,23 +95,39 @@ __device__ __forceinline__ void load_row_part(float (&r)[HS / 4], const float* r
     }
 }
 
-// Map a linear workgroup id to (tile, bh): tiles in decreasing order of work
-// for causal problems, heads fastest.
-__device__ __forceinline__ void tile_of_block(int BH, int ntiles, bool heavy_first_high,
-                                              int& tile, int& bh) {
+// Causal tiles carry unequal work (tile i of a Q-tile kernel sees i+1 key
+// tiles, tile j of a K/V-tile kernel nt-j query tiles), so when the grid is
+// large enough one workgroup runs tiles i and nt-1-i back to back: every
+// workgroup then does nt+1 units and the grid has no tail.  Pairing halves
+// the grid, so it is used only while at least two paired workgroups per CU
+// remain (pair_tiles on the host).  Otherwise tiles run one per workgroup,
+// heaviest first (the longest-first order of kernel 8 in llm.c's
+// attention_backward.cu).
+// Consecutive workgroup ids walk the heads, so all tiles of a head land on
+// one XCD (one L2) whenever B*NH is a multiple of 8.
+__device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool heavy_high,
+                                              int& bh, int& ta, int& tb) {
     const int bid = blockIdx.x;
     const int rank = bid / BH;
     bh = bid - rank * BH;
-    tile = heavy_first_high ? (ntiles - 1 - rank) : rank;
+    if (paired) {
+        ta = rank;
+        tb = nt - 1 - rank;
+        if (tb == ta) tb = -1;
+    } else {   // heaviest tile first, so the last workgroups to start are short
+        ta = heavy_high ? nt - 1 - rank : rank;
+        tb = -1;
+    }
 }
+
+__host__ __device__ inline int grid_tiles(int nt, bool paired) { return paired ? (nt + 1) / 2 : nt; }
 
 // ------------------------------------------------------------------ forward
 template <int HS>
-__global__ __launch_bounds__(kThreads, 3) void fwd_f32_kernel(float* __restrict__ out,
-                                                           float* __restrict__ lse,
-                                                           const float* __restrict__ qkv, int T,
-                                                           int C, int NH, int causal,
-                                                           float scale_log2) {
+__device__ __forceinline__ void fwd_f32_tile(int tile_, int bh_, float* __restrict__ out,
+                                             float* __restrict__ lse,
+                                             const float* __restrict__ qkv, int T, int C, int NH,
+                                             int causal, float scale_log2) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
     constexpr int NB = kTile / 16;   // 16-key blocks per tile
@@ -119,9 +137,7 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_f32_kernel(float* __restrict_
 
     const Lane L;
     const int nqt = (T + kTile - 1) / kTile;
-    const int BH = gridDim.x / nqt;
-    int qt, bh;
-    tile_of_block(BH, nqt, causal != 0, qt, bh);
+    const int qt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -260,10 +276,10 @@ __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict
 // it.  Per Q tile: S = Q K^T, P = exp(scale*S - lse), dV^T += dO^T P,
 // dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS (scale applied at the end).
 template <int HS>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
-    int causal, float scale, float scale_log2) {
+__device__ __forceinline__ void bwd_dkdv_f32_tile(
+    int tile_, int bh_, float* __restrict__ dqkv, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
+    int T, int C, int NH, int causal, float scale, float scale_log2) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
     constexpr int NB = kTile / 16;
@@ -275,9 +291,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
 
     const Lane L;
     const int nt = (T + kTile - 1) / kTile;
-    const int BH = gridDim.x / nt;
-    int kt, bh;
-    tile_of_block(BH, nt, false, kt, bh);   // kt = 0 has the most Q tiles
+    const int kt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -385,10 +399,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
 // which runs after it).  Per K/V tile: S^T = K Q^T, P, dP^T = V dO^T,
 // dS = P * (dP - D), dQ^T += K^T dS^T (scale applied at the end).
 template <int HS>
-__global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
-    float* __restrict__ dqkv, float* __restrict__ Dws, const float* __restrict__ dout,
-    const float* __restrict__ qkv, const float* __restrict__ out, const float* __restrict__ lse,
-    int T, int C, int NH, int causal, float scale, float scale_log2) {
+__device__ __forceinline__ void bwd_dq_f32_tile(
+    int tile_, int bh_, float* __restrict__ dqkv, float* __restrict__ Dws,
+    const float* __restrict__ dout, const float* __restrict__ qkv, const float* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
+    float scale_log2) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
     constexpr int NB = kTile / 16;
@@ -398,9 +413,7 @@ __global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
 
     const Lane L;
     const int nt = (T + kTile - 1) / kTile;
-    const int BH = gridDim.x / nt;
-    int qt, bh;
-    tile_of_block(BH, nt, causal != 0, qt, bh);
+    const int qt = tile_, bh = bh_;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const size_t C3 = 3 * (size_t)C;
     const float* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
@@ -491,13 +504,63 @@ __global__ __launch_bounds__(kThreads, 3) void bwd_dq_f32_kernel(
     }
 }
 
+// ------------------------------------------------------------- kernels
+// Each runs its tile function on one tile, or on a balanced pair of causal
+// tiles (see pair_of_block).
+template <int HS>
+__global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(float* __restrict__ out,
+                                                              float* __restrict__ lse,
+                                                              const float* __restrict__ qkv,
+                                                              int T, int C, int NH, int causal,
+                                                              float scale_log2, int paired) {
+    const int nt = (T + kTile - 1) / kTile;
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    fwd_f32_tile<HS>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        fwd_f32_tile<HS>(tb, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    }
+}
+
+template <int HS>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
+    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
+    int causal, float scale, float scale_log2, int paired) {
+    const int nt = (T + kTile - 1) / kTile;
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
+    bwd_dkdv_f32_tile<HS>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        bwd_dkdv_f32_tile<HS>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    }
+}
+
+template <int HS>
+__global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void bwd_dq_f32_kernel(
+    float* __restrict__ dqkv, float* __restrict__ Dws, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ out, const float* __restrict__ lse,
+    int T, int C, int NH, int causal, float scale, float scale_log2, int paired) {
+    const int nt = (T + kTile - 1) / kTile;
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    bwd_dq_f32_tile<HS>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    if (tb >= 0) {
+        __syncthreads();
+        bwd_dq_f32_tile<HS>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    }
+}
+
 template <int HS>
 hipError_t fwd_f32_hs(float* out, float* lse, const float* qkv, const Shape& s, hipStream_t st) {
     const int nqt = (s.T + kTile - 1) / kTile;
-    const unsigned grid = (unsigned)(nqt * s.B * s.NH);
+    const bool paired = pair_tiles(nqt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
     hipLaunchKernelGGL(fwd_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, out, lse, qkv, s.T,
-                       s.C, s.NH, s.causal, scale_log2);
+                       s.C, s.NH, s.causal, scale_log2, (int)paired);
     return hipGetLastError();
 }
 
@@ -516,10 +579,11 @@ template <int HS>
 hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
                        const float* D, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
-    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e, (int)paired);
     return hipGetLastError();
 }
 
@@ -527,10 +591,11 @@ template <int HS>
 hipError_t dq_f32_hs(float* dqkv, float* D, const float* dout, const float* qkv, const float* out,
                      const float* lse, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
-    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
+    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, D, dout, qkv,
-                       out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e);
+                       out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e, (int)paired);
     return hipGetLastError();
 }
 
