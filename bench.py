@@ -37,8 +37,10 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=60,
-                   help="untimed steps; the GPU needs ~20 ms of work to reach steady clocks")
+    p.add_argument("--warmup", type=int, default=600,
+                   help="untimed steps per dtype; the bf16 kernels reach their steady speed "
+                        "only after ~70 ms of work (600 bf16 steps of the GPT-2 layer), the "
+                        "fp32 ones after ~30 ms")
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--dtype", choices=["f32", "bf16"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
