@@ -57,6 +57,8 @@ def _load():
             lib.oracle_forward.restype = i
             lib.oracle_backward.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i]
             lib.oracle_backward.restype = i
+            lib.oracle_forward_block.argtypes = [dp, dp, dp] + [i] * 9
+            lib.oracle_forward_block.restype = i
             lib.oracle_set_threads.argtypes = [i]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
@@ -111,6 +113,24 @@ def forward(qkv, NH: int, causal: bool = True, materialized: bool = False):
         raise RuntimeError(f"oracle_forward failed with status {rc}")
     if materialized:
         return out, lse, pre, att
+    return out, lse
+
+
+def forward_block(qkv, NH: int, causal: bool, q0: int, q1: int, k0: int, k1: int):
+    """Forward of query rows [q0, q1) against keys [k0, k1) (each row keeps
+    its causal limit).  Return (out (B, q1-q0, C), lse (B, NH, q1-q0)),
+    float64; rows with no key in the range get out 0 and lse -inf."""
+    qkv = _as_f64(qkv)
+    B, T, C = _dims(qkv, NH)
+    nq = q1 - q0
+    if not (0 <= q0 < q1 <= T and 0 <= k0 <= k1 <= T):
+        raise ValueError(f"bad ranges q[{q0},{q1}) k[{k0},{k1}) for T={T}")
+    out = np.empty((B, nq, C), np.float64)
+    lse = np.empty((B, NH, nq), np.float64)
+    rc = _load().oracle_forward_block(_ptr(out), _ptr(lse), _ptr(qkv), B, T, C, NH,
+                                      int(bool(causal)), q0, q1, k0, k1)
+    if rc != 0:
+        raise RuntimeError(f"oracle_forward_block failed with status {rc}")
     return out, lse
 
 

@@ -143,6 +143,67 @@ int oracle_forward(double* out, double* lse, double* preatt, double* att,
 }
 
 /*
+ * Forward restricted to query rows [q0, q1) and keys [k0, k1): each row t
+ * attends to U(t) intersected with {k0..k1-1}, with the same four passes as
+ * oracle_forward.  out is (B, q1-q0, C) and lse is (B, NH, q1-q0).  A row
+ * with no key in the range gets out = 0 and lse = -inf (an empty softmax;
+ * the pages never form one, so this is the reading used for the partial
+ * results that a split of the key range produces).  With q0 = 0, q1 = T,
+ * k0 = 0, k1 = T it computes exactly what oracle_forward does, in the same
+ * order.
+ */
+int oracle_forward_block(double* out, double* lse, const double* qkv, int B, int T, int C,
+                         int NH, int causal, int q0, int q1, int k0, int k1) {
+    int rc = check_dims(B, T, C, NH, causal);
+    if (rc) return rc;
+    if (!out || !lse || !qkv) return ORACLE_EINVAL;
+    if (q0 < 0 || q1 > T || q0 >= q1 || k0 < 0 || k1 > T || k0 > k1) return ORACLE_EINVAL;
+    const int hs = C / NH;
+    const int nq = q1 - q0;
+    const size_t C3 = 3 * (size_t)C;
+    const double scale = 1.0 / sqrt((double)hs);
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double* pre = (double*)malloc(sizeof(double) * (size_t)T);
+        double* a = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!pre || !a) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for collapse(3) schedule(dynamic, 8)
+        for (int b = 0; b < B; b++)
+            for (int r = 0; r < nq; r++)
+                for (int h = 0; h < NH; h++) {
+                    if (!pre || !a) continue;
+                    const int t = q0 + r;
+                    const double* q = qkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
+                    /* keys k0 .. k0+nj-1: the range cut by the causal limit */
+                    const double* kbase = qkv + ((size_t)b * T + k0) * C3 + C + (size_t)h * hs;
+                    const double* vbase = qkv + ((size_t)b * T + k0) * C3 + 2 * (size_t)C + (size_t)h * hs;
+                    const int hi = causal ? (t + 1 < k1 ? t + 1 : k1) : k1;
+                    const int nj = hi > k0 ? hi - k0 : 0;
+                    double* o = out + ((size_t)b * nq + r) * C + (size_t)h * hs;
+                    for (int i = 0; i < hs; i++) o[i] = 0.0;
+                    if (nj == 0) {
+                        lse[((size_t)b * NH + h) * nq + r] = -INFINITY;
+                        continue;
+                    }
+                    lse[((size_t)b * NH + h) * nq + r] =
+                        softmax_row(pre, a, q, kbase, C3, hs, nj, nj, scale);
+                    for (int j = 0; j < nj; j++) {
+                        const double* vj = vbase + (size_t)j * C3;
+                        for (int i = 0; i < hs; i++) o[i] += a[j] * vj[i];
+                    }
+                }
+        free(pre);
+        free(a);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/*
  * Backward: dqkv (B,T,3C) is overwritten with [dq | dk | dv].  The forward
  * probabilities are recomputed from qkv row by row, so memory stays O(T)
  * per thread unless datt / dpreatt (B,NH,T,T) are requested (non-NULL).

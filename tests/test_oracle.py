@@ -298,3 +298,83 @@ def test_invalid_arguments(oracle_mod):
         oracle_mod.forward(qkv, 3, True)  # C=8 not a multiple of NH=3
     with pytest.raises(ValueError):
         oracle_mod.forward(qkv[:, :, :7], 1, True)
+
+
+# ------------------------------------------ key-range and query-range block ----
+# oracle.forward_block restricts rows and keys; it is pinned to the full
+# forward (exact equality where the computation is the same), to the merge
+# identity that recombines a split of the key range, and to closed forms.
+
+def merge_parts(parts):
+    """Recombine (out, lse) results over disjoint key sets: weights
+    exp(lse_p - L) with L = log sum_p exp(lse_p) (plain numpy)."""
+    outs = np.stack([o for o, _ in parts])          # (P, B, T, C)
+    lses = np.stack([l for _, l in parts])          # (P, B, NH, T)
+    L = np.logaddexp.reduce(lses, axis=0)           # (B, NH, T)
+    P, B, T, C = outs.shape
+    NH = lses.shape[2]
+    w = np.exp(lses - L[None])                      # (P, B, NH, T)
+    w = np.repeat(w.transpose(0, 1, 3, 2), C // NH, axis=3)   # (P, B, T, C)
+    return (w * outs).sum(0), L
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_full_range_is_forward(oracle_mod, causal):
+    qkv, _ = rnd(2, 45, 48, seed=61)
+    out, lse = oracle_mod.forward(qkv, 3, causal)
+    ob, lb = oracle_mod.forward_block(qkv, 3, causal, 0, 45, 0, 45)
+    assert np.array_equal(ob, out) and np.array_equal(lb, lse)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_query_range_is_rows_of_forward(oracle_mod, causal):
+    qkv, _ = rnd(2, 45, 48, seed=62)
+    out, lse = oracle_mod.forward(qkv, 3, causal)
+    ob, lb = oracle_mod.forward_block(qkv, 3, causal, 17, 45, 0, 45)
+    assert np.array_equal(ob, out[:, 17:]) and np.array_equal(lb, lse[:, :, 17:])
+    od, ld = oracle_mod.forward_block(qkv, 3, causal, 44, 45, 0, 45)   # decode row
+    assert np.array_equal(od, out[:, 44:]) and np.array_equal(ld, lse[:, :, 44:])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("cuts", [(20,), (7, 30), (1, 2, 40)])
+def test_key_split_merges_to_forward(oracle_mod, causal, cuts):
+    T = 45
+    qkv, _ = rnd(2, T, 48, seed=63)
+    out, lse = oracle_mod.forward(qkv, 3, causal)
+    edges = (0,) + cuts + (T,)
+    parts = [oracle_mod.forward_block(qkv, 3, causal, 0, T, a, b) for a, b in zip(edges, edges[1:])]
+    mo, ml = merge_parts(parts)
+    np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-12)
+
+
+def test_block_rows_without_keys(oracle_mod):
+    """Causal rows before k0 see no key of the range: out 0, lse -inf."""
+    qkv, _ = rnd(1, 20, 16, seed=64)
+    ob, lb = oracle_mod.forward_block(qkv, 2, True, 0, 20, 12, 20)
+    assert np.all(ob[:, :12] == 0.0) and np.all(np.isneginf(lb[:, :, :12]))
+    assert np.all(np.isfinite(lb[:, :, 12:]))
+    oe, le = oracle_mod.forward_block(qkv, 2, False, 0, 20, 5, 5)      # empty range
+    assert np.all(oe == 0.0) and np.all(np.isneginf(le))
+
+
+def test_block_single_key_closed_form(oracle_mod):
+    """One key j: the softmax is 1, so out = v_j and lse = scale q.k_j."""
+    qkv, _ = rnd(2, 9, 32, seed=65)
+    NH, j = 2, 4
+    q, k, v = split_heads(qkv, NH)
+    ob, lb = oracle_mod.forward_block(qkv, NH, False, 0, 9, j, j + 1)
+    hs = 16
+    for h in range(NH):
+        np.testing.assert_array_equal(ob[:, :, h * hs:(h + 1) * hs],
+                                      np.repeat(v[:, h, j:j + 1], 9, axis=1))
+        ref = np.einsum("bti,bi->bt", q[:, h], k[:, h, j]) / math.sqrt(hs)
+        np.testing.assert_allclose(lb[:, h], ref, rtol=1e-15, atol=1e-15)
+
+
+def test_block_invalid_ranges(oracle_mod):
+    qkv, _ = rnd(1, 8, 16, seed=66)
+    for q0, q1, k0, k1 in [(3, 3, 0, 8), (0, 9, 0, 8), (0, 8, 5, 4), (-1, 8, 0, 8)]:
+        with pytest.raises(ValueError):
+            oracle_mod.forward_block(qkv, 2, True, q0, q1, k0, k1)
