@@ -179,6 +179,39 @@ def run_materialized(la, torch, w, steps, warmup):
                           "packed tensors once"}
 
 
+def run_decode(la, torch, w, dtype, steps, warmup):
+    """Time attn_decode (last query row against all T keys, key ranges
+    merged) on the workload's inputs.  It is HBM-bound: the compulsory bytes
+    are every key and value row of every head read once, plus the query row
+    and the output."""
+    from workloads import workload_inputs
+    qkv_c, _ = workload_inputs(w, dtype)
+    qkv = qkv_c.cuda()
+    B, T, C, NH = w.B, w.T, w.C, w.NH
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty((B, C), dtype=tdt, device="cuda")
+    lse = torch.empty((B, NH), device="cuda")
+    fn = la.attn_decode_bf16 if dtype == "bf16" else la.attn_decode
+    call = lambda: fn(out, lse, qkv, B, T, C, NH)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    esz = 2 if dtype == "bf16" else 4
+    nbytes = (2 * B * T * C + 2 * B * C) * esz + B * NH * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"decode over {w.name} {w.label()}", "dtype": dtype,
+            "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / 8000.0, 4),
+            "bytes_note": "compulsory bytes: K and V of every head once, q row and out"}
+
+
 def cpu_baseline(w, dtype, budget_s):
     """The fp64 oracle, as it stands, on the first heads of the same
     workload in (b, h) order until the CPU budget is spent."""
@@ -266,6 +299,10 @@ def main():
 
     if not args.no_extra and dtype == "f32":
         line["materialized_f32"] = run_materialized(la, torch, w, min(args.steps, 10), 2)
+
+    if not args.no_extra:
+        line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),
+                          run_decode(la, torch, WORKLOADS[5], "bf16", 50, 200)]
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, dtype, args.cpu_budget_s)

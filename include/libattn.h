@@ -46,9 +46,11 @@
  * Results are deterministic: no atomics, fixed reduction order.
  *
  * Workspace.  attn_backward and attn_backward_bf16 need B*NH*T floats of
- * scratch for D; libattn
- * keeps one grow-only buffer per device, allocated with hipMalloc on first
- * need, and frees it in attn_release().  With the environment variable
+ * scratch for D, attn_decode and attn_decode_bf16 room for their partial
+ * results; libattn keeps one grow-only buffer per device, allocated with
+ * hipMalloc on first need, and frees it in attn_release().  Calls that use
+ * it share it, so such calls on one device must not overlap in time (calls
+ * on one stream never do).  With the environment variable
  * ATTN_TEST_FAIL_ALLOC=1 that allocation fails (ATTN_EHIP) before any HIP
  * call, so callers can test their error handling on any host.
  *
@@ -157,6 +159,43 @@ int attn_backward_materialized(float* dqkv, float* dpreatt, float* datt,
                                const float* dout, const float* qkv, const float* att,
                                int B, int T, int C, int NH, int causal);
 
+/*
+ * Decode, fp32: attention of the last query row t = T-1 of every sequence
+ * and head against all of its keys 0..T-1 (the causal row T-1, which is also
+ * the non-causal one) -- one step of autoregressive inference over the
+ * packed qkv of the T tokens so far, the same computation with a single
+ * query row ("LLM Systems 10 & 11: Accelerating Transformer Training and
+ * Inference", section 2).  Reads only row T-1 of q and rows 0..T-1 of k, v.
+ * Writes out (B, C) = [b, h*hs+i] and lse (B, NH).  The keys are split into
+ * ranges of 128 or 256 per workgroup and the partial results merged as
+ * attn_merge does; the partials live in the library workspace (at most
+ * ceil(T/128) * B * (C + NH) floats).
+ */
+int attn_decode(float* out, float* lse, const float* qkv, int B, int T, int C, int NH);
+
+/* Decode with bf16 qkv and out (fp32 arithmetic, fp32 lse). */
+int attn_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C,
+                     int NH);
+
+/*
+ * Merge of partial attention results over disjoint key sets: the rescale
+ * the online softmax applies between key tiles (FlashAttention part of
+ * "Umakini wa kujitegemea, kerneli za CUDA na FlashAttention"), applied
+ * across parts.  Part p gives o_parts[p] (B, T, C) fp32, normalised over its
+ * own keys, and lse_parts[p] (B, NH, T) (natural log, scaled domain; -inf for
+ * a row with no key in the part).  Writes
+ *     lse = log sum_p exp(lse_p),   out = sum_p exp(lse_p - lse) o_p,
+ * and out = 0, lse = -inf where every part is empty.  o_parts is
+ * (nparts, B, T, C) and lse_parts (nparts, B, NH, T), contiguous; nparts >= 1.
+ * Needs no workspace.
+ */
+int attn_merge(float* out, float* lse, const float* o_parts, const float* lse_parts, int nparts,
+               int B, int T, int C, int NH);
+
+/* Merge with a bf16 out (parts and lse stay fp32). */
+int attn_merge_bf16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
+                    int nparts, int B, int T, int C, int NH);
+
 /* Set the HIP stream (a hipStream_t, or NULL for the null stream) used by
  * the calling thread's subsequent calls.  Always returns ATTN_OK. */
 int attn_set_stream(void* hip_stream);
@@ -165,7 +204,7 @@ int attn_set_stream(void* hip_stream);
  * The string stays valid until the thread's next libattn call. */
 const char* attn_last_error(void);
 
-/* Free the backward workspace on every device it was allocated on.  Must
+/* Free the workspace on every device it was allocated on.  Must
  * not race with work still queued that uses it (synchronise first). */
 void attn_release(void);
 

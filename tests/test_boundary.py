@@ -163,3 +163,67 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 64, 192)
     with pytest.raises(ValueError):
         la.forward(x, 4, True)
+
+
+DECODE = ["attn_decode", "attn_decode_bf16"]
+MERGE = ["attn_merge", "attn_merge_bf16"]
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_decode_arguments(name):
+    lib = la.load()
+    fn = getattr(lib, name)
+    p = ptrs(3)
+    assert fn(*p, 0, 64, 64, 4) == la.ATTN_EINVAL          # B < 1
+    assert fn(*p, 1, 0, 64, 4) == la.ATTN_EINVAL           # T < 1
+    assert fn(*p, 1, 64, 66, 4) == la.ATTN_EINVAL          # C % NH
+    assert fn(*p, 1, 64, 96, 4) == la.ATTN_EUNSUPPORTED    # hs = 24
+    for i in range(3):
+        q = ptrs(3)
+        q[i] = ctypes.c_void_p(0)
+        assert fn(*q, 1, 64, 64, 4) == la.ATTN_EINVAL
+        assert "NULL" in lib.attn_last_error().decode()
+    q = ptrs(3)
+    q[1] = ctypes.c_void_p(BASE + 4)                       # lse overlaps out (B*C*esize bytes)
+    assert fn(*q, 1, 64, 64, 4) == la.ATTN_EINVAL
+    q = ptrs(3)
+    q[2] = ctypes.c_void_p(BASE + STEP + 2)                # misaligned qkv
+    assert fn(*q, 1, 64, 64, 4) == la.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("name", MERGE)
+def test_merge_arguments(name):
+    lib = la.load()
+    fn = getattr(lib, name)
+    p = ptrs(4)
+    assert fn(*p, 0, 1, 8, 64, 4) == la.ATTN_EINVAL        # nparts < 1
+    assert "nparts" in lib.attn_last_error().decode()
+    assert fn(*p, 2, 0, 8, 64, 4) == la.ATTN_EINVAL        # B < 1
+    assert fn(*p, 2, 1, 8, 64, 3) == la.ATTN_EINVAL        # C % NH
+    assert fn(*p, 2, 1, 8, 48, 1) == la.ATTN_EUNSUPPORTED  # hs = 48
+    for i in range(4):
+        q = ptrs(4)
+        q[i] = ctypes.c_void_p(0)
+        assert fn(*q, 2, 1, 8, 64, 4) == la.ATTN_EINVAL
+    q = ptrs(4)
+    q[2] = ctypes.c_void_p(BASE + 16)                      # o_parts inside out
+    assert fn(*q, 2, 1, 8, 64, 4) == la.ATTN_EINVAL
+    assert "overlaps" in lib.attn_last_error().decode()
+
+
+def test_forced_workspace_failure_decode():
+    """attn_decode keeps its partial results in the workspace: the forced
+    allocation failure reaches it too, before any HIP call."""
+    code = (
+        "import ctypes, transformer_causal_head_attn_amd as la\n"
+        "lib = la.load()\n"
+        "p = [ctypes.c_void_p((1 << 40) + i * (1 << 36)) for i in range(3)]\n"
+        "rc = lib.attn_decode(*p, 1, 64, 64, 4)\n"
+        "print(rc, lib.attn_last_error().decode())\n"
+    )
+    env = dict(os.environ, ATTN_TEST_FAIL_ALLOC="1", PYTHONPATH=ROOT)
+    res = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=120)
+    assert res.returncode == 0, res.stderr
+    rc, msg = res.stdout.split(" ", 1)
+    assert int(rc) == la.ATTN_EHIP and "forced" in msg

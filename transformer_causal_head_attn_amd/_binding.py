@@ -29,6 +29,7 @@ EXPORTS = (
     "attn_forward_bf16", "attn_backward_bf16",
     "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
     "attn_forward_materialized", "attn_backward_materialized",
+    "attn_decode", "attn_decode_bf16", "attn_merge", "attn_merge_bf16",
     "attn_set_stream", "attn_last_error", "attn_release",
 )
 
@@ -64,9 +65,14 @@ def load(path: str | None = None):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * nptr + [i] * 5
             fn.restype = i
-        for name in ("attn_backward_preprocess", "attn_backward_preprocess_bf16"):
+        for name in ("attn_backward_preprocess", "attn_backward_preprocess_bf16",
+                     "attn_decode", "attn_decode_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
+            fn.restype = i
+        for name in ("attn_merge", "attn_merge_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 4 + [i] * 5
             fn.restype = i
         lib.attn_set_stream.argtypes = [vp]
         lib.attn_set_stream.restype = i
@@ -197,6 +203,34 @@ def attn_backward_materialized(dqkv, dpreatt, datt, dout, qkv, att, B, T, C, NH,
           _check(att, "att", f, M), *_dims(B, T, C, NH, causal))
 
 
+def attn_decode(out, lse, qkv, B, T, C, NH) -> None:
+    f = torch.float32
+    _call("attn_decode", _check(out, "out", f, B * C), _check(lse, "lse", f, B * NH),
+          _check(qkv, "qkv", f, B * T * 3 * C), int(B), int(T), int(C), int(NH))
+
+
+def attn_decode_bf16(out, lse, qkv, B, T, C, NH) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_decode_bf16", _check(out, "out", h, B * C), _check(lse, "lse", f, B * NH),
+          _check(qkv, "qkv", h, B * T * 3 * C), int(B), int(T), int(C), int(NH))
+
+
+def attn_merge(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
+    f = torch.float32
+    _call("attn_merge", _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(o_parts, "o_parts", f, nparts * B * T * C),
+          _check(lse_parts, "lse_parts", f, nparts * B * NH * T),
+          int(nparts), int(B), int(T), int(C), int(NH))
+
+
+def attn_merge_bf16(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
+    h, f = torch.bfloat16, torch.float32
+    _call("attn_merge_bf16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(o_parts, "o_parts", f, nparts * B * T * C),
+          _check(lse_parts, "lse_parts", f, nparts * B * NH * T),
+          int(nparts), int(B), int(T), int(C), int(NH))
+
+
 def attn_set_stream(stream) -> None:
     """Set the calling thread's libattn stream (a torch.cuda.Stream, a raw
     hipStream_t integer, or None for the null stream).  The functions above
@@ -259,3 +293,26 @@ def backward_materialized(dout, qkv, att, NH: int, causal: bool = True):
     datt = torch.empty_like(att)
     attn_backward_materialized(dqkv, dpre, datt, dout, qkv, att, B, T, C, NH, int(causal))
     return dqkv, dpre, datt
+
+
+def decode(qkv: torch.Tensor, NH: int):
+    """Allocate (out (B, C), lse (B, NH)) and run the decode for the last
+    position of each sequence (fp32 or bf16 by qkv's dtype)."""
+    B, T, C = _shape(qkv, NH)
+    out = torch.empty((B, C), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, NH), dtype=torch.float32, device=qkv.device)
+    fn = attn_decode_bf16 if qkv.dtype == torch.bfloat16 else attn_decode
+    fn(out, lse, qkv, B, T, C, NH)
+    return out, lse
+
+
+def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torch.float32):
+    """Merge partial results o_parts (P, B, T, C) fp32 and lse_parts
+    (P, B, NH, T) into (out (B, T, C) of out_dtype, lse (B, NH, T))."""
+    P, B, T, C = o_parts.shape
+    NH = lse_parts.shape[2]
+    out = torch.empty((B, T, C), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=o_parts.device)
+    fn = attn_merge_bf16 if out_dtype == torch.bfloat16 else attn_merge
+    fn(out, lse, o_parts, lse_parts, P, B, T, C, NH)
+    return out, lse

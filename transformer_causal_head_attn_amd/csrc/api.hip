@@ -336,4 +336,63 @@ int attn_backward_materialized(float* dqkv, float* dpreatt, float* datt, const f
                     "attn_backward_materialized launch");
 }
 
+int attn_decode(float* out, float* lse, const float* qkv, int B, int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes((long long)B * C, 4), "out"},
+                         {lse, nbytes((long long)B * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 4), "qkv"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, 0);
+    float* ws = nullptr;
+    rc = workspace(attn::decode_workspace_floats(s) * 4, &ws);
+    if (rc) return rc;
+    return launched(attn::launch_decode_f32(out, lse, qkv, ws, s, g_stream), "attn_decode launch");
+}
+
+int attn_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes((long long)B * C, 2), "out"},
+                         {lse, nbytes((long long)B * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 2), "qkv"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, 0);
+    float* ws = nullptr;
+    rc = workspace(attn::decode_workspace_floats(s) * 4, &ws);
+    if (rc) return rc;
+    return launched(attn::launch_decode_bf16(out, lse, qkv, ws, s, g_stream),
+                    "attn_decode_bf16 launch");
+}
+
+namespace {
+int check_merge(void* out, size_t out_elem, float* lse, const float* o_parts,
+                const float* lse_parts, int nparts, int B, int T, int C, int NH) {
+    if (nparts < 1) return fail(ATTN_EINVAL, "nparts must be >= 1 (got %d)", nparts);
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, out_elem), "out"}, {lse, nbytes(BT * NH, 4), "lse"}};
+    const Span ins[] = {{o_parts, nbytes(BT * C * nparts, 4), "o_parts"},
+                        {lse_parts, nbytes(BT * NH * nparts, 4), "lse_parts"}};
+    return check_args(B, T, C, NH, 0, outs, 2, ins, 2, false);
+}
+}  // namespace
+
+int attn_merge(float* out, float* lse, const float* o_parts, const float* lse_parts, int nparts,
+               int B, int T, int C, int NH) {
+    int rc = check_merge(out, 4, lse, o_parts, lse_parts, nparts, B, T, C, NH);
+    if (rc) return rc;
+    return launched(attn::launch_merge_f32(out, lse, o_parts, lse_parts, nparts,
+                                           shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_merge launch");
+}
+
+int attn_merge_bf16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
+                    int nparts, int B, int T, int C, int NH) {
+    int rc = check_merge(out, 2, lse, o_parts, lse_parts, nparts, B, T, C, NH);
+    if (rc) return rc;
+    return launched(attn::launch_merge_bf16(out, lse, o_parts, lse_parts, nparts,
+                                            shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_merge_bf16 launch");
+}
+
 }  // extern "C"

@@ -119,4 +119,17 @@ hipError_t launch_bwd_materialized(float* dqkv, float* dpreatt, float* datt, con
                                    const float* qkv, const float* att, const Shape& s,
                                    hipStream_t st);
 
+// decode (one query row per sequence, key ranges merged) and the merge of
+// partial (O, lse) results
+int decode_range_len(const Shape& s);
+size_t decode_workspace_floats(const Shape& s);
+hipError_t launch_decode_f32(float* out, float* lse, const float* qkv, float* ws, const Shape& s,
+                             hipStream_t st);
+hipError_t launch_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, float* ws,
+                              const Shape& s, hipStream_t st);
+hipError_t launch_merge_f32(float* out, float* lse, const float* o_parts, const float* lse_parts,
+                            int P, const Shape& s, hipStream_t st);
+hipError_t launch_merge_bf16(uint16_t* out, float* lse, const float* o_parts,
+                             const float* lse_parts, int P, const Shape& s, hipStream_t st);
+
 }  // namespace attn
