@@ -128,3 +128,39 @@ def test_merge_rows_without_keys(la, oracle_mod):
     ro, rl = oracle_mod.forward_block(qkv, NH, True, 0, T, 10, 30)
     assert_close(out[:, 10:], ro[:, 10:], "f32", "out")
     assert_close(lse[:, :, 10:], rl[:, :, 10:], "f32", "lse")
+
+
+def test_decode_many_ranges(la, oracle_mod):
+    """257 ranges of 128 keys merged for a single head (one workgroup per
+    range, more ranges than a workgroup has threads)."""
+    B, T, C, NH = 1, 128 * 257, 16, 1
+    _case(f"decode f32 B{B} T{T} C{C} NH{NH} (257 ranges)")
+    qkv, _ = make_inputs(B, T, C, "f32", seed=81)
+    out, lse = la.decode(qkv.cuda(), NH)
+    torch.cuda.synchronize()
+    ro, rl = _decode_ref(oracle_mod, qkv, NH)
+    assert_close(out.cpu(), ro, "f32", "decode out")
+    assert_close(lse.cpu(), rl, "f32", "decode lse")
+
+
+def test_decode_calls_in_a_row(la, oracle_mod):
+    """The partial results share the library workspace with the backward's
+    D: alternating shapes, with a backward in between, give the same bits
+    and the oracle's values each time."""
+    _case("decode calls in a row")
+    qa, _ = make_inputs(4, 500, 256, "f32", seed=82)
+    qb, db = make_inputs(2, 300, 512, "f32", seed=83)
+    qa_, qb_ = qa.cuda(), qb.cuda()
+    a1 = la.decode(qa_, 4)
+    b1 = la.decode(qb_, 8)
+    o, l = la.forward(qb_, 8, True)
+    la.backward(db.cuda(), qb_, o, l, 8, True)
+    a2 = la.decode(qa_, 4)
+    b2 = la.decode(qb_, 8)
+    torch.cuda.synchronize()
+    for x, y in zip(a1 + b1, a2 + b2):
+        assert torch.equal(x, y)
+    ro, rl = _decode_ref(oracle_mod, qa, 4)
+    assert_close(a2[0].cpu(), ro, "f32", "decode out")
+    ro, rl = _decode_ref(oracle_mod, qb, 8)
+    assert_close(b2[0].cpu(), ro, "f32", "decode out")

@@ -97,8 +97,12 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
     float q[VEC];
     Vec<E>::load(q, base + (size_t)(T - 1) * C3);
 
-    // scores (log2 domain) of the range's keys; -inf past T
+    // K rows of the range, and its V rows too when they fit in registers
+    // (then both loads are in flight together instead of one after the
+    // other, around the softmax)
+    constexpr bool kEarlyV = NP * VEC <= 64;
     float kx[NP][VEC];
+    float vx[kEarlyV ? NP : 1][VEC];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int j = k0 + p * KPP + kg;
@@ -106,6 +110,17 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
         for (int i = 0; i < VEC; ++i) kx[p][i] = 0.f;
         if (j < T) Vec<E>::load(kx[p], base + C + (size_t)j * C3);
     }
+    if constexpr (kEarlyV) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int j = k0 + p * KPP + kg;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) vx[p][i] = 0.f;
+            if (j < T) Vec<E>::load(vx[p], base + 2 * (size_t)C + (size_t)j * C3);
+        }
+    }
+
+    // scores (log2 domain) of the range's keys; -inf past T
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int j = k0 + p * KPP + kg;
@@ -146,11 +161,16 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
     for (int p = 0; p < NP; ++p) {
         const int j = k0 + p * KPP + kg;
         if (j < T) {
-            float vx[VEC];
-            Vec<E>::load(vx, base + 2 * (size_t)C + (size_t)j * C3);
+            float v[VEC];
+            if constexpr (kEarlyV) {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) v[i] = vx[p][i];
+            } else {
+                Vec<E>::load(v, base + 2 * (size_t)C + (size_t)j * C3);
+            }
             const float w = sc[p * KPP + kg];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) acc[i] = fmaf(w, vx[i], acc[i]);
+            for (int i = 0; i < VEC; ++i) acc[i] = fmaf(w, v[i], acc[i]);
         }
     }
 #pragma unroll
