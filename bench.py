@@ -27,10 +27,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd causal TFLOP/s and % MFMA peak, B8 T1024 C768 NH12"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}   # MI355X dense MFMA
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_causal_head_attn_amd", "csrc")
-KERNEL_SOURCE = {"f32": "flash_f32.hip", "bf16": "flash_bf16.hip"}
+KERNEL_SOURCE = {"f32": "flash_f32.hip", "bf16": "flash_half.hip", "f16": "flash_half.hip"}
 
 
 def parse_args():
@@ -42,7 +42,7 @@ def parse_args():
                         "only after ~70 ms of work (600 bf16 steps of the GPT-2 layer), the "
                         "fp32 ones after ~30 ms")
     p.add_argument("--workload", type=int, default=3)
-    p.add_argument("--dtype", choices=["f32", "bf16"], default=None)
+    p.add_argument("--dtype", choices=["f32", "bf16", "f16"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="CPU seconds the oracle baseline may spend on its sample")
@@ -100,12 +100,12 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     qkv_c, dout_c = workload_inputs(w, dtype)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
     B, T, C, NH = w.B, w.T, w.C, w.NH
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
     out = torch.empty((B, T, C), dtype=tdt, device="cuda")
     lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
     dqkv = torch.empty_like(qkv)
     D = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
-    sfx = "_bf16" if dtype == "bf16" else ""
+    sfx = "" if dtype == "f32" else "_" + dtype
     fwd = getattr(la, "attn_forward" + sfx)
     dkdv = getattr(la, "attn_backward_dkdv" + sfx)
     dq = getattr(la, "attn_backward_dq" + sfx)
@@ -185,6 +185,8 @@ def run_decode(la, torch, w, dtype, steps, warmup):
     are every key and value row of every head read once, plus the query row
     and the output."""
     from workloads import workload_inputs
+    if dtype == "f16":   # decode is built for fp32 and bf16 only
+        dtype = "bf16"
     qkv_c, _ = workload_inputs(w, dtype)
     qkv = qkv_c.cuda()
     B, T, C, NH = w.B, w.T, w.C, w.NH
@@ -289,13 +291,15 @@ def main():
     }
 
     if not args.no_extra:
-        other = "bf16" if dtype == "f32" else "f32"
-        o_total, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
-        o_val = flops / (o_total * 1e-3) / 1e12
-        line["same_workload_" + other] = {
-            "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
-            "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
-            "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
+        for other in ("f32", "bf16", "f16"):
+            if other == dtype:
+                continue
+            o_total, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
+            o_val = flops / (o_total * 1e-3) / 1e12
+            line["same_workload_" + other] = {
+                "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
+                "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
+                "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
 
     if not args.no_extra and dtype == "f32":
         line["materialized_f32"] = run_materialized(la, torch, w, min(args.steps, 10), 2)

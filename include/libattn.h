@@ -45,7 +45,7 @@
  * (attn_set_stream; default: the null stream) and return without waiting.
  * Results are deterministic: no atomics, fixed reduction order.
  *
- * Workspace.  attn_backward and attn_backward_bf16 need B*NH*T floats of
+ * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need B*NH*T floats of
  * scratch for D, attn_decode and attn_decode_bf16 room for their partial
  * results; libattn keeps one grow-only buffer per device, allocated with
  * hipMalloc on first need, and frees it in attn_release().  Calls that use
@@ -136,6 +136,28 @@ int attn_backward_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const 
 int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                             const float* lse, const float* D,
                             int B, int T, int C, int NH, int causal);
+
+/*
+ * The same fused forward, backward and backward stages with IEEE half
+ * (fp16) tensors, passed as uint16_t bit patterns: the section names FP16
+ * beside BF16 for mixed-precision training.  Same kernels, fp16 matrix-core
+ * operands, fp32 accumulation, round to nearest even on output; lse and D
+ * stay fp32.  fp16 keeps 3 more mantissa bits than bf16 but its range ends
+ * at 65504: out, dS and the gradients must stay inside it.
+ */
+int attn_forward_f16(uint16_t* out, float* lse, const uint16_t* qkv,
+                     int B, int T, int C, int NH, int causal);
+int attn_backward_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                      const uint16_t* out, const float* lse,
+                      int B, int T, int C, int NH, int causal);
+int attn_backward_preprocess_f16(float* D, const uint16_t* dout, const uint16_t* out,
+                                 int B, int T, int C, int NH);
+int attn_backward_dq_f16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                         const uint16_t* out, const float* lse,
+                         int B, int T, int C, int NH, int causal);
+int attn_backward_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                           const float* lse, const float* D,
+                           int B, int T, int C, int NH, int causal);
 
 /*
  * Materialised forward, fp32, as the pages' reference does it: writes the

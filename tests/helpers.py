@@ -5,7 +5,9 @@ import numpy as np
 import torch
 
 # Tolerances on |gpu - oracle| <= atol + rtol * |oracle|, elementwise.
-TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2)}
+# fp16 (not in the stated targets) gets ten of its rounding steps, 2^-11 each:
+# the same margin over one rounding that the bf16 bound leaves over bf16's 2^-8.
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2), "f16": (5e-3, 5e-3)}
 
 
 def assert_close(gpu, ref, dtype: str, what: str):

@@ -67,8 +67,11 @@ ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_forward_bf16", 3),
          ("attn_backward_bf16", 5), ("attn_forward_materialized", 4),
          ("attn_backward_materialized", 6),
          ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
-         ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6)]
-STAGE0 = [("attn_backward_preprocess", 3), ("attn_backward_preprocess_bf16", 3)]
+         ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6),
+         ("attn_forward_f16", 3), ("attn_backward_f16", 5),
+         ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6)]
+STAGE0 = [("attn_backward_preprocess", 3), ("attn_backward_preprocess_bf16", 3),
+          ("attn_backward_preprocess_f16", 3)]
 
 
 @pytest.mark.parametrize("name,nptr", ENTRY)

@@ -28,6 +28,8 @@ EXPORTS = (
     "attn_backward_preprocess", "attn_backward_dkdv", "attn_backward_dq",
     "attn_forward_bf16", "attn_backward_bf16",
     "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
+    "attn_forward_f16", "attn_backward_f16",
+    "attn_backward_preprocess_f16", "attn_backward_dkdv_f16", "attn_backward_dq_f16",
     "attn_forward_materialized", "attn_backward_materialized",
     "attn_decode", "attn_decode_bf16", "attn_merge", "attn_merge_bf16",
     "attn_set_stream", "attn_last_error", "attn_release",
@@ -61,11 +63,14 @@ def load(path: str | None = None):
                            ("attn_forward_materialized", 4),
                            ("attn_backward_materialized", 6),
                            ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
-                           ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6)):
+                           ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6),
+                           ("attn_forward_f16", 3), ("attn_backward_f16", 5),
+                           ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6)):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * nptr + [i] * 5
             fn.restype = i
         for name in ("attn_backward_preprocess", "attn_backward_preprocess_bf16",
+                     "attn_backward_preprocess_f16",
                      "attn_decode", "attn_decode_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
@@ -186,6 +191,43 @@ def attn_backward_dq_bf16(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> 
           _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
 
 
+def attn_forward_f16(out, lse, qkv, B, T, C, NH, causal) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_forward_f16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(qkv, "qkv", h, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_f16(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_backward_f16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
+          _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_preprocess_f16(D, dout, out, B, T, C, NH) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_backward_preprocess_f16", _check(D, "D", f, B * NH * T),
+          _check(dout, "dout", h, B * T * C), _check(out, "out", h, B * T * C),
+          int(B), int(T), int(C), int(NH))
+
+
+def attn_backward_dkdv_f16(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_backward_dkdv_f16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(dout, "dout", h, B * T * C), _check(qkv, "qkv", h, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_dq_f16(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_backward_dq_f16", _check(dqkv, "dqkv", h, B * T * 3 * C),
+          _check(D, "D", f, B * NH * T), _check(dout, "dout", h, B * T * C),
+          _check(qkv, "qkv", h, B * T * 3 * C), _check(out, "out", h, B * T * C),
+          _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
+
+
 def attn_forward_materialized(out, preatt, att, qkv, B, T, C, NH, causal) -> None:
     f = torch.float32
     M = B * NH * T * T
@@ -258,12 +300,12 @@ def _shape(qkv: torch.Tensor, NH: int):
 
 
 def forward(qkv: torch.Tensor, NH: int, causal: bool = True):
-    """Allocate (out, lse) with torch and run the fused forward (fp32 or
-    bf16 by qkv's dtype)."""
+    """Allocate (out, lse) with torch and run the fused forward (fp32, bf16
+    or fp16 by qkv's dtype)."""
     B, T, C = _shape(qkv, NH)
     out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
     lse = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
-    fn = attn_forward_bf16 if qkv.dtype == torch.bfloat16 else attn_forward
+    fn = {torch.bfloat16: attn_forward_bf16, torch.float16: attn_forward_f16}.get(qkv.dtype, attn_forward)
     fn(out, lse, qkv, B, T, C, NH, int(causal))
     return out, lse
 
@@ -272,7 +314,7 @@ def backward(dout, qkv, out, lse, NH: int, causal: bool = True):
     """Allocate dqkv with torch and run the fused backward."""
     B, T, C = _shape(qkv, NH)
     dqkv = torch.empty_like(qkv)
-    fn = attn_backward_bf16 if qkv.dtype == torch.bfloat16 else attn_backward
+    fn = {torch.bfloat16: attn_backward_bf16, torch.float16: attn_backward_f16}.get(qkv.dtype, attn_backward)
     fn(dqkv, dout, qkv, out, lse, B, T, C, NH, int(causal))
     return dqkv
 

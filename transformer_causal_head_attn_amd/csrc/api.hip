@@ -303,6 +303,80 @@ int attn_backward_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const 
                     "attn_backward_dq_bf16 launch");
 }
 
+int attn_forward_f16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C, int NH,
+                      int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, 2), "out"}, {lse, nbytes(BT * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 2), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    return launched(attn::launch_fwd_f16(out, lse, qkv, shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_forward_f16 launch");
+}
+
+int attn_backward_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                       const uint16_t* out, const float* lse, int B, int T, int C, int NH,
+                       int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {out, nbytes(BT * C, 2), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    float* D = nullptr;
+    rc = workspace(nbytes(BT * NH, 4), &D);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    hipError_t e = attn::launch_dq_f16(dqkv, D, dout, qkv, out, lse, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdv_f16(dqkv, dout, qkv, lse, D, s, g_stream);
+    return launched(e, "attn_backward_f16 launch");
+}
+
+int attn_backward_preprocess_f16(float* D, const uint16_t* dout, const uint16_t* out, int B,
+                                  int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{D, nbytes(BT * NH, 4), "D"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"}, {out, nbytes(BT * C, 2), "out"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 1, ins, 2, false);
+    if (rc) return rc;
+    return launched(attn::launch_prepass_f16(D, dout, out, shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_backward_preprocess_f16 launch");
+}
+
+int attn_backward_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                            const float* lse, const float* D, int B, int T, int C, int NH,
+                            int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dkdv_f16(dqkv, dout, qkv, lse, D, shape_of(B, T, C, NH, causal),
+                                           g_stream),
+                    "attn_backward_dkdv_f16 launch");
+}
+
+int attn_backward_dq_f16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                          const uint16_t* out, const float* lse, int B, int T, int C, int NH,
+                          int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}, {D, nbytes(BT * NH, 4), "D"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {out, nbytes(BT * C, 2), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dq_f16(dqkv, D, dout, qkv, out, lse,
+                                         shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_backward_dq_f16 launch");
+}
+
 int attn_forward_materialized(float* out, float* preatt, float* att, const float* qkv, int B,
                               int T, int C, int NH, int causal) {
     const long long BT = (long long)B * T;

@@ -112,6 +112,15 @@ hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t
                             const float* lse, const float* D, const Shape& s, hipStream_t st);
 hipError_t launch_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                           const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
+// fp16 fused path (IEEE half tensors as raw 16-bit patterns)
+hipError_t launch_fwd_f16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
+                          hipStream_t st);
+hipError_t launch_prepass_f16(float* D, const uint16_t* dout, const uint16_t* out, const Shape& s,
+                              hipStream_t st);
+hipError_t launch_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                           const float* lse, const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_f16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                         const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
 // materialised fp32 path
 hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
                                    const Shape& s, hipStream_t st);

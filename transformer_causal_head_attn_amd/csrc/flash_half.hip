@@ -1,5 +1,6 @@
-// flash_bf16.hip -- fused attention forward and backward with bfloat16
-// tensors and fp32 accumulation for gfx950 (v_mfma_f32_16x16x32_bf16).
+// flash_half.hip -- fused attention forward and backward with 16-bit
+// tensors (bfloat16 or IEEE half) and fp32 accumulation for gfx950
+// (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x32_f16).
 //
 // Same method as the fp32 kernels (flash_f32.hip): the self-attention of
 // "Umakini wa kujitegemea, kerneli za CUDA na FlashAttention" (section 1)
@@ -8,12 +9,17 @@
 // dev/cuda/attention_backward.cu with the closed-form softmax gradient of
 // its kernel 7.  Low-precision operands with higher-precision accumulation
 // follow the mixed-precision part of "LLM Systems 10 & 11: Accelerating
-// Transformer Training and Inference" (section 1): Q, K, V, dO are bf16,
-// every product accumulates in fp32, the softmax runs in fp32, and P and dS
-// are rounded to bf16 only to enter the matrix cores.  lse and D stay fp32.
+// Transformer Training and Inference" (section 1), which names both bf16 and
+// fp16: Q, K, V, dO are 16-bit, every product accumulates in fp32, the
+// softmax runs in fp32, and P and dS are rounded to the 16-bit type only to
+// enter the matrix cores.  lse and D stay fp32.  The two element types share
+// every kernel (the element traits BF16 and F16 below); only the matrix-core
+// instruction and the conversions differ.  In fp16 the forward's P stays
+// below 2^8 (lazy rescale) and the backward's P below 1, far inside its
+// range; dS, out and the gradients must stay below 65504 in magnitude.
 //
 // gfx950 mapping.
-//  * One bf16 MFMA contracts 32 k-values; lane group g = l/16 supplies eight.
+//  * One 16-bit MFMA contracts 32 k-values; lane group g = l/16 supplies eight.
 //    For Q.K and dO.V (contraction over hs) a lane takes k = 32s + 8g .. +7,
 //    one 16-byte LDS read of a row-major tile.
 //  * For the products that contract over keys or queries (P V, dO^T P,
@@ -55,6 +61,37 @@ struct Lane {
     }
 };
 
+// Element types of the 16-bit path.  Both fill the same 8-entry matrix-core
+// operand layout, accumulate in fp32 and round to nearest even when fp32
+// values are converted back (P, dS and the outputs).
+struct BF16 {   // bfloat16: v_mfma_f32_16x16x32_bf16
+    typedef __bf16 S;
+    typedef __bf16 V8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 V4 __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float bits_to_f32(uint32_t u) {   // low 16 bits
+        return __uint_as_float(u << 16);
+    }
+};
+struct F16 {   // IEEE half: v_mfma_f32_16x16x32_f16
+    typedef _Float16 S;
+    typedef _Float16 V8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 V4 __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float bits_to_f32(uint32_t u) {
+        const uint16_t h = (uint16_t)u;
+        _Float16 x;
+        __builtin_memcpy(&x, &h, 2);
+        return (float)x;
+    }
+};
+template <typename E>
+using V8 = typename E::V8;
+
 template <int HS>
 struct Geom {
     static constexpr int LDR = HS + 8;                  // LDS row stride (elements)
@@ -62,28 +99,30 @@ struct Geom {
     static constexpr int MB = HS / 16;
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-    bf16x8 r;
+template <typename E>
+__device__ __forceinline__ V8<E> as_v8(uint4 v) {
+    V8<E> r;
     __builtin_memcpy(&r, &v, 16);
     return r;
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(make_uint4(0u, 0u, 0u, 0u)); }
+template <typename E>
+__device__ __forceinline__ V8<E> zero_v8() { return as_v8<E>(make_uint4(0u, 0u, 0u, 0u)); }
 
 // Eight bf16 of one row for contraction step s: k = 32s + 8g .. +7; zeros
 // where that range lies beyond HS (only when HS = 16).
-template <int HS>
-__device__ __forceinline__ bf16x8 row_chunk_global(const uint16_t* rowp, bool valid, int s, int g) {
+template <typename E, int HS>
+__device__ __forceinline__ V8<E> row_chunk_global(const uint16_t* rowp, bool valid, int s, int g) {
     const int k0 = 32 * s + 8 * g;
-    if (!valid || k0 >= HS) return zero_bf16x8();
-    return as_bf16x8(*reinterpret_cast<const uint4*>(rowp + k0));
+    if (!valid || k0 >= HS) return zero_v8<E>();
+    return as_v8<E>(*reinterpret_cast<const uint4*>(rowp + k0));
 }
 
-template <int HS>
-__device__ __forceinline__ bf16x8 row_chunk_lds(const uint16_t* tile, int row, int s, int g) {
+template <typename E, int HS>
+__device__ __forceinline__ V8<E> row_chunk_lds(const uint16_t* tile, int row, int s, int g) {
     const int k0 = 32 * s + 8 * g;
-    if (k0 >= HS) return zero_bf16x8();
-    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + row * Geom<HS>::LDR + k0));
+    if (k0 >= HS) return zero_v8<E>();
+    return as_v8<E>(*reinterpret_cast<const uint4*>(tile + row * Geom<HS>::LDR + k0));
 }
 
 __device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
@@ -96,13 +135,13 @@ __device__ __forceinline__ s16x4 tr_read(const uint16_t* p) {
 // [col0 + j] for e >= 4.  Within a 16-lane group, ds_read_b64_tr_b16 hands
 // lane j element (j % 4) of the 8-byte blocks addressed by lanes 4e + j/4, so
 // lane i addresses row (.. + i/4), columns col0 + 4(i%4) .. +3.
-template <int HS>
-__device__ __forceinline__ bf16x8 col_operand(const uint16_t* tile, int base, int col0, int lane) {
+template <typename E, int HS>
+__device__ __forceinline__ V8<E> col_operand(const uint16_t* tile, int base, int col0, int lane) {
     const int j = lane & 15, g = lane >> 4;
     const uint16_t* p = tile + (base + 4 * g + (j >> 2)) * Geom<HS>::LDR + col0 + 4 * (j & 3);
     const s16x4 a = tr_read(p);
     const s16x4 b = tr_read(p + 16 * Geom<HS>::LDR);
-    bf16x8 r;
+    V8<E> r;
     __builtin_memcpy(&r, &a, 8);
     __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
     return r;
@@ -110,25 +149,27 @@ __device__ __forceinline__ bf16x8 col_operand(const uint16_t* tile, int base, in
 
 // Pack score-layout values of blocks n = 2t (x) and 2t+1 (y) into the
 // matching 8-entry bf16 operand.
-__device__ __forceinline__ bf16x8 pack_pair(const f32x4& x, const f32x4& y) {
-    bf16x8 r;
-    r[0] = (__bf16)x[0];
-    r[1] = (__bf16)x[1];
-    r[2] = (__bf16)x[2];
-    r[3] = (__bf16)x[3];
-    r[4] = (__bf16)y[0];
-    r[5] = (__bf16)y[1];
-    r[6] = (__bf16)y[2];
-    r[7] = (__bf16)y[3];
+template <typename E>
+__device__ __forceinline__ V8<E> pack_pair(const f32x4& x, const f32x4& y) {
+    V8<E> r;
+    r[0] = (typename E::S)x[0];
+    r[1] = (typename E::S)x[1];
+    r[2] = (typename E::S)x[2];
+    r[3] = (typename E::S)x[3];
+    r[4] = (typename E::S)y[0];
+    r[5] = (typename E::S)y[1];
+    r[6] = (typename E::S)y[2];
+    r[7] = (typename E::S)y[3];
     return r;
 }
 
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, const f32x4& v) {
-    bf16x4 r;
-    r[0] = (__bf16)v[0];
-    r[1] = (__bf16)v[1];
-    r[2] = (__bf16)v[2];
-    r[3] = (__bf16)v[3];
+template <typename E>
+__device__ __forceinline__ void store4(uint16_t* p, const f32x4& v) {
+    typename E::V4 r;
+    r[0] = (typename E::S)v[0];
+    r[1] = (typename E::S)v[1];
+    r[2] = (typename E::S)v[2];
+    r[3] = (typename E::S)v[3];
     __builtin_memcpy(p, &r, 8);
 }
 
@@ -193,8 +234,8 @@ __host__ __device__ inline int grid_tiles(int nt, bool paired) { return paired ?
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
 // stream through LDS 64 at a time (one buffer; the next tile's registers
 // are loaded while the current tile is used).
-template <int HS, int QB>
-__device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __restrict__ out,
+template <typename E, int HS, int QB>
+__device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __restrict__ out,
                                               float* __restrict__ lse,
                                               const uint16_t* __restrict__ qkv, int T, int C,
                                               int NH, int causal, float scale_log2) {
@@ -213,13 +254,13 @@ __device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __re
     const uint16_t* vbase = qbase + 2 * (size_t)C;
 
     const int r0 = qt * BM + L.w * R;   // this wave's first query row
-    bf16x8 qreg[QB][G::KSTEPS];
+    V8<E> qreg[QB][G::KSTEPS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = r0 + 16 * qb + L.r16;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s)
-            qreg[qb][s] = row_chunk_global<HS>(qbase + (size_t)q * C3, q < T, s, L.g);
+            qreg[qb][s] = row_chunk_global<E, HS>(qbase + (size_t)q * C3, q < T, s, L.g);
     }
 
     float m[QB], lsum[QB];
@@ -246,9 +287,9 @@ __device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __re
         for (int n = 0; n < 4; ++n) {
 #pragma unroll
             for (int st = 0; st < G::KSTEPS; ++st) {
-                const bf16x8 kc = row_chunk_lds<HS>(kt_lds, 16 * n + L.r16, st, L.g);
+                const V8<E> kc = row_chunk_lds<E, HS>(kt_lds, 16 * n + L.r16, st, L.g);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sc[qb][n] = mfma_bf16(kc, qreg[qb][st], sc[qb][n]);
+                for (int qb = 0; qb < QB; ++qb) sc[qb][n] = E::mfma(kc, qreg[qb][st], sc[qb][n]);
             }
         }
     };
@@ -299,14 +340,14 @@ __device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __re
         // O^T += V^T P^T, 32 keys per step
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            bf16x8 pb[QB];
+            V8<E> pb[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair(sc[qb][2 * t], sc[qb][2 * t + 1]);
+            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair<E>(sc[qb][2 * t], sc[qb][2 * t + 1]);
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                const bf16x8 vop = col_operand<HS>(vt_lds, 32 * t, 16 * mb, L.l);
+                const V8<E> vop = col_operand<E, HS>(vt_lds, 32 * t, 16 * mb, L.l);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) o[qb][mb] = mfma_bf16(vop, pb[qb], o[qb][mb]);
+                for (int qb = 0; qb < QB; ++qb) o[qb][mb] = E::mfma(vop, pb[qb], o[qb][mb]);
             }
         }
     };
@@ -339,15 +380,15 @@ __device__ __forceinline__ void fwd_bf16_tile(int tile_, int bh_, uint16_t* __re
             const float inv = 1.0f / ltot;
             uint16_t* orow = out + ((size_t)b * T + row) * C + (size_t)h * HS;
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(orow + 16 * mb + 4 * L.g, o[qb][mb] * inv);
+            for (int mb = 0; mb < G::MB; ++mb) store4<E>(orow + 16 * mb + 4 * L.g, o[qb][mb] * inv);
             if (L.g == 0) lse[(size_t)bh * T + row] = (m[qb] + __log2f(ltot)) * kLn2;
         }
     }
 }
 
 // ------------------------------------------------------ backward pre-pass
-template <int HS>
-__global__ __launch_bounds__(kThreads) void prepass_bf16_kernel(float* __restrict__ D,
+template <typename E, int HS>
+__global__ __launch_bounds__(kThreads) void prepass_half_kernel(float* __restrict__ D,
                                                                 const uint16_t* __restrict__ dout,
                                                                 const uint16_t* __restrict__ out,
                                                                 int T, int NH, long long rows) {
@@ -363,8 +404,8 @@ __global__ __launch_bounds__(kThreads) void prepass_bf16_kernel(float* __restric
         const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc += __uint_as_float(av[q] << 16) * __uint_as_float(cv[q] << 16);
-            acc += __uint_as_float(av[q] & 0xffff0000u) * __uint_as_float(cv[q] & 0xffff0000u);
+            acc += E::bits_to_f32(av[q]) * E::bits_to_f32(cv[q]);
+            acc += E::bits_to_f32(av[q] >> 16) * E::bits_to_f32(cv[q] >> 16);
         }
     }
 #pragma unroll
@@ -381,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void prepass_bf16_kernel(float* __restric
 // ----------------------------------------------------- backward dK / dV
 // Workgroup: a 4*R-row K/V tile of one head (R = 16*KB rows per wave, kept
 // in registers); Q and dO stream through LDS 64 rows at a time.
-template <int HS, int KB>
-__device__ __forceinline__ void bwd_dkdv_bf16_tile(
+template <typename E, int HS, int KB>
+__device__ __forceinline__ void bwd_dkdv_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
@@ -407,14 +448,14 @@ __device__ __forceinline__ void bwd_dkdv_bf16_tile(
     const float* drow = Dws + (size_t)bh * T;
 
     const int c0 = kvt * BN + L.w * R;   // this wave's first key row
-    bf16x8 kreg[KB][G::KSTEPS], vreg[KB][G::KSTEPS];
+    V8<E> kreg[KB][G::KSTEPS], vreg[KB][G::KSTEPS];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int kv = c0 + 16 * kb + L.r16;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
-            kreg[kb][s] = row_chunk_global<HS>(kbase + (size_t)kv * C3, kv < T, s, L.g);
-            vreg[kb][s] = row_chunk_global<HS>(vbase + (size_t)kv * C3, kv < T, s, L.g);
+            kreg[kb][s] = row_chunk_global<E, HS>(kbase + (size_t)kv * C3, kv < T, s, L.g);
+            vreg[kb][s] = row_chunk_global<E, HS>(vbase + (size_t)kv * C3, kv < T, s, L.g);
         }
     }
     f32x4 dk[KB][G::MB], dv[KB][G::MB];
@@ -472,12 +513,12 @@ __device__ __forceinline__ void bwd_dkdv_bf16_tile(
                 }
 #pragma unroll
                 for (int st = 0; st < G::KSTEPS; ++st) {
-                    const bf16x8 qc = row_chunk_lds<HS>(Qs, 16 * n + L.r16, st, L.g);
-                    const bf16x8 dc = row_chunk_lds<HS>(dOs, 16 * n + L.r16, st, L.g);
+                    const V8<E> qc = row_chunk_lds<E, HS>(Qs, 16 * n + L.r16, st, L.g);
+                    const V8<E> dc = row_chunk_lds<E, HS>(dOs, 16 * n + L.r16, st, L.g);
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        s[kb] = mfma_bf16(qc, kreg[kb][st], s[kb]);
-                        dp[kb] = mfma_bf16(dc, vreg[kb][st], dp[kb]);
+                        s[kb] = E::mfma(qc, kreg[kb][st], s[kb]);
+                        dp[kb] = E::mfma(dc, vreg[kb][st], dp[kb]);
                     }
                 }
 #pragma unroll
@@ -494,20 +535,20 @@ __device__ __forceinline__ void bwd_dkdv_bf16_tile(
                     }
                 }
             }
-            bf16x8 pb[KB], sb[KB];
+            V8<E> pb[KB], sb[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                pb[kb] = pack_pair(p[kb][0], p[kb][1]);
-                sb[kb] = pack_pair(ds[kb][0], ds[kb][1]);
+                pb[kb] = pack_pair<E>(p[kb][0], p[kb][1]);
+                sb[kb] = pack_pair<E>(ds[kb][0], ds[kb][1]);
             }
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                const bf16x8 dop = col_operand<HS>(dOs, 32 * t, 16 * mb, L.l);
-                const bf16x8 qop = col_operand<HS>(Qs, 32 * t, 16 * mb, L.l);
+                const V8<E> dop = col_operand<E, HS>(dOs, 32 * t, 16 * mb, L.l);
+                const V8<E> qop = col_operand<E, HS>(Qs, 32 * t, 16 * mb, L.l);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    dv[kb][mb] = mfma_bf16(dop, pb[kb], dv[kb][mb]);
-                    dk[kb][mb] = mfma_bf16(qop, sb[kb], dk[kb][mb]);
+                    dv[kb][mb] = E::mfma(dop, pb[kb], dv[kb][mb]);
+                    dk[kb][mb] = E::mfma(qop, sb[kb], dk[kb][mb]);
                 }
             }
         }
@@ -521,8 +562,8 @@ __device__ __forceinline__ void bwd_dkdv_bf16_tile(
             uint16_t* dvrow = dkrow + C;
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                store_bf16x4(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
-                store_bf16x4(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
+                store4<E>(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
+                store4<E>(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
             }
         }
     }
@@ -533,8 +574,8 @@ __device__ __forceinline__ void bwd_dkdv_bf16_tile(
 // registers); K and V stream through LDS 64 rows at a time.  It first forms
 // D = dO . O for its rows and writes it out for the dK/dV kernel, which runs
 // after it.
-template <int HS, int QB>
-__device__ __forceinline__ void bwd_dq_bf16_tile(
+template <typename E, int HS, int QB>
+__device__ __forceinline__ void bwd_dq_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, float* __restrict__ Dws,
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ qkv,
     const uint16_t* __restrict__ out, const float* __restrict__ lse, int T, int C, int NH,
@@ -555,7 +596,7 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
     const uint16_t* dobase = dout + (size_t)b * T * C + (size_t)h * HS;
 
     const int r0 = qt * BM + L.w * R;
-    bf16x8 qreg[QB][G::KSTEPS], doreg[QB][G::KSTEPS];
+    V8<E> qreg[QB][G::KSTEPS], doreg[QB][G::KSTEPS];
     float l2[QB], Dq[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -563,8 +604,8 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
         const bool v = q < T;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
-            qreg[qb][s] = row_chunk_global<HS>(qbase + (size_t)q * C3, v, s, L.g);
-            doreg[qb][s] = row_chunk_global<HS>(dobase + (size_t)q * C, v, s, L.g);
+            qreg[qb][s] = row_chunk_global<E, HS>(qbase + (size_t)q * C3, v, s, L.g);
+            doreg[qb][s] = row_chunk_global<E, HS>(dobase + (size_t)q * C, v, s, L.g);
         }
         l2[qb] = v ? lse[(size_t)bh * T + q] * kLog2e : INFINITY;
         // D = dO . O for this row (the pre-pass, fused): the lane's columns,
@@ -572,7 +613,7 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
         float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
-            const bf16x8 oc = row_chunk_global<HS>(out + ((size_t)b * T + q) * C + (size_t)h * HS, v, s, L.g);
+            const V8<E> oc = row_chunk_global<E, HS>(out + ((size_t)b * T + q) * C + (size_t)h * HS, v, s, L.g);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = fmaf((float)doreg[qb][s][e], (float)oc[e], acc);
         }
@@ -620,12 +661,12 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
                 }
 #pragma unroll
                 for (int st = 0; st < G::KSTEPS; ++st) {
-                    const bf16x8 kc = row_chunk_lds<HS>(Ks, 16 * n + L.r16, st, L.g);
-                    const bf16x8 vc = row_chunk_lds<HS>(Vs, 16 * n + L.r16, st, L.g);
+                    const V8<E> kc = row_chunk_lds<E, HS>(Ks, 16 * n + L.r16, st, L.g);
+                    const V8<E> vc = row_chunk_lds<E, HS>(Vs, 16 * n + L.r16, st, L.g);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) {
-                        s[qb] = mfma_bf16(kc, qreg[qb][st], s[qb]);
-                        dp[qb] = mfma_bf16(vc, doreg[qb][st], dp[qb]);
+                        s[qb] = E::mfma(kc, qreg[qb][st], s[qb]);
+                        dp[qb] = E::mfma(vc, doreg[qb][st], dp[qb]);
                     }
                 }
 #pragma unroll
@@ -641,14 +682,14 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
                     }
                 }
             }
-            bf16x8 sb[QB];
+            V8<E> sb[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sb[qb] = pack_pair(ds[qb][0], ds[qb][1]);
+            for (int qb = 0; qb < QB; ++qb) sb[qb] = pack_pair<E>(ds[qb][0], ds[qb][1]);
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                const bf16x8 kop = col_operand<HS>(Ks, 32 * t, 16 * mb, L.l);
+                const V8<E> kop = col_operand<E, HS>(Ks, 32 * t, 16 * mb, L.l);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) dq[qb][mb] = mfma_bf16(kop, sb[qb], dq[qb][mb]);
+                for (int qb = 0; qb < QB; ++qb) dq[qb][mb] = E::mfma(kop, sb[qb], dq[qb][mb]);
             }
         }
     }
@@ -659,7 +700,7 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
         if (q < T) {
             uint16_t* dqrow = dqkv + ((size_t)b * T + q) * C3 + (size_t)h * HS;
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb) store_bf16x4(dqrow + 16 * mb + 4 * L.g, dq[qb][mb] * scale);
+            for (int mb = 0; mb < G::MB; ++mb) store4<E>(dqrow + 16 * mb + 4 * L.g, dq[qb][mb] * scale);
         }
     }
 }
@@ -669,8 +710,8 @@ __device__ __forceinline__ void bwd_dq_bf16_tile(
 // ------------------------------------------------------------- kernels
 // Each runs its tile function on one tile, or on a balanced pair of causal
 // tiles (see pair_of_block).
-template <int HS, int QB>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict__ out,
+template <typename E, int HS, int QB>
+__global__ __launch_bounds__(kThreads) void fwd_half_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
@@ -678,15 +719,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(uint16_t* __restrict
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, ta, tb;
     pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
-    fwd_bf16_tile<HS, QB>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    fwd_half_tile<E, HS, QB>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
     if (tb >= 0) {
         __syncthreads();
-        fwd_bf16_tile<HS, QB>(tb, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+        fwd_half_tile<E, HS, QB>(tb, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
     }
 }
 
-template <int HS, int KB>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
+template <typename E, int HS, int KB>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_half_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
@@ -694,15 +735,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(
     const int nt = (T + 64 * KB - 1) / (64 * KB);
     int bh, ta, tb;
     pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
-    bwd_dkdv_bf16_tile<HS, KB>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    bwd_dkdv_half_tile<E, HS, KB>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
-        bwd_dkdv_bf16_tile<HS, KB>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+        bwd_dkdv_half_tile<E, HS, KB>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
     }
 }
 
-template <int HS, int QB>
-__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
+template <typename E, int HS, int QB>
+__global__ __launch_bounds__(kThreads) void bwd_dq_half_kernel(
     uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
@@ -710,10 +751,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, ta, tb;
     pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
-    bwd_dq_bf16_tile<HS, QB>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    bwd_dq_half_tile<E, HS, QB>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
-        bwd_dq_bf16_tile<HS, QB>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+        bwd_dq_half_tile<E, HS, QB>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
     }
 }
 
@@ -722,32 +763,32 @@ constexpr int kQB = 2;
 // registers, more resident waves; measured faster on the long-context shape)
 constexpr int kb_for(int hs) { return hs >= 128 ? 1 : 2; }
 
-template <int HS>
-hipError_t fwd_bf16_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
+template <typename E, int HS>
+hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                        hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nqt = (s.T + BM - 1) / BM;
     const bool paired = pair_tiles(nqt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
-    hipLaunchKernelGGL((fwd_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
+    hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
                        qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)paired);
     return hipGetLastError();
 }
 
-template <int HS>
-hipError_t prepass_bf16_hs(float* D, const uint16_t* dout, const uint16_t* out, const Shape& s,
+template <typename E, int HS>
+hipError_t prepass_half_hs(float* D, const uint16_t* dout, const uint16_t* out, const Shape& s,
                            hipStream_t st) {
     const long long rows = (long long)s.B * s.T * s.NH;
     const long long threads = rows * (HS / 8);
     const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(prepass_bf16_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, D, dout, out,
-                       s.T, s.NH, rows);
+    hipLaunchKernelGGL((prepass_half_kernel<E, HS>), dim3(grid), dim3(kThreads), 0, st, D, dout,
+                       out, s.T, s.NH, rows);
     return hipGetLastError();
 }
 
-template <int HS>
-hipError_t dkdv_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+template <typename E, int HS>
+hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                         const float* lse, const float* D, const Shape& s, hipStream_t st) {
     constexpr int KB = kb_for(HS);
     constexpr int BN = 64 * KB;
@@ -755,57 +796,61 @@ hipError_t dkdv_bf16_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qk
     const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+    hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
                        (int)paired);
     return hipGetLastError();
 }
 
-template <int HS>
-hipError_t dq_bf16_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+template <typename E, int HS>
+hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                       const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nt = (s.T + BM - 1) / BM;
     const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv, D,
-                       dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
+    hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+                       D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
                        (int)paired);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define ATTN_DISPATCH_HS(fn, ...)                         \
+#define ATTN_DISPATCH_HS(fn, E, ...)                      \
     switch (s.hs) {                                       \
-        case 16: return fn<16>(__VA_ARGS__);              \
-        case 32: return fn<32>(__VA_ARGS__);              \
-        case 64: return fn<64>(__VA_ARGS__);              \
-        case 128: return fn<128>(__VA_ARGS__);            \
+        case 16: return fn<E, 16>(__VA_ARGS__);           \
+        case 32: return fn<E, 32>(__VA_ARGS__);           \
+        case 64: return fn<E, 64>(__VA_ARGS__);           \
+        case 128: return fn<E, 128>(__VA_ARGS__);         \
         default: return hipErrorInvalidValue;             \
     }
 
-hipError_t launch_fwd_bf16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
-                           hipStream_t st) {
-    ATTN_DISPATCH_HS(fwd_bf16_hs, out, lse, qkv, s, st)
-}
+#define ATTN_HALF_LAUNCHERS(SFX, E)                                                                \
+    hipError_t launch_fwd_##SFX(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,  \
+                                hipStream_t st) {                                                 \
+        ATTN_DISPATCH_HS(fwd_half_hs, E, out, lse, qkv, s, st)                                     \
+    }                                                                                              \
+    hipError_t launch_prepass_##SFX(float* D, const uint16_t* dout, const uint16_t* out,          \
+                                    const Shape& s, hipStream_t st) {                             \
+        ATTN_DISPATCH_HS(prepass_half_hs, E, D, dout, out, s, st)                                  \
+    }                                                                                              \
+    hipError_t launch_dkdv_##SFX(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,       \
+                                 const float* lse, const float* D, const Shape& s,                \
+                                 hipStream_t st) {                                                 \
+        ATTN_DISPATCH_HS(dkdv_half_hs, E, dqkv, dout, qkv, lse, D, s, st)                          \
+    }                                                                                              \
+    hipError_t launch_dq_##SFX(uint16_t* dqkv, float* D, const uint16_t* dout,                    \
+                               const uint16_t* qkv, const uint16_t* out, const float* lse,        \
+                               const Shape& s, hipStream_t st) {                                  \
+        ATTN_DISPATCH_HS(dq_half_hs, E, dqkv, D, dout, qkv, out, lse, s, st)                       \
+    }
 
-hipError_t launch_prepass_bf16(float* D, const uint16_t* dout, const uint16_t* out,
-                               const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(prepass_bf16_hs, D, dout, out, s, st)
-}
+ATTN_HALF_LAUNCHERS(bf16, BF16)
+ATTN_HALF_LAUNCHERS(f16, F16)
 
-hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
-                            const float* lse, const float* D, const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(dkdv_bf16_hs, dqkv, dout, qkv, lse, D, s, st)
-}
-
-hipError_t launch_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
-                          const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(dq_bf16_hs, dqkv, D, dout, qkv, out, lse, s, st)
-}
-
+#undef ATTN_HALF_LAUNCHERS
 #undef ATTN_DISPATCH_HS
 
 }  // namespace attn

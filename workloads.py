@@ -8,8 +8,9 @@ Recipe (the same bytes go to the GPU and to the oracle):
   * qkv of shape (B, T, 3C) and dout of shape (B, T, C) are drawn on the host
     with ``torch.Generator('cpu').manual_seed(seed)`` and ``torch.randn`` in
     float32, dout then multiplied by its standard deviation (1 or 0.1);
-  * the bf16 workloads round those float32 samples to bfloat16 with torch's
-    round-to-nearest-even cast; the oracle then sees the rounded values;
+  * the bf16 workloads round those float32 samples to bfloat16 (and the fp16
+    runs to IEEE half) with torch's round-to-nearest-even cast; the oracle
+    then sees the rounded values;
   * seeds are 1000 + k for qkv and 2000 + k for dout, for workload k.
 
 The shapes are the ones the pages use: the GPT-2 small attention layer of the
@@ -71,7 +72,7 @@ WORKLOADS = {
 
 def randn(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tensor:
     """float32 N(0, std^2) samples from a seeded CPU generator, optionally
-    rounded to bfloat16 (round to nearest even)."""
+    rounded to bfloat16 or float16 (round to nearest even)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
@@ -79,6 +80,8 @@ def randn(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tenso
         x = x * std
     if dtype == "bf16":
         return x.to(torch.bfloat16)
+    if dtype == "f16":
+        return x.to(torch.float16)
     if dtype != "f32":
         raise ValueError(dtype)
     return x
