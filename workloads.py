@@ -87,6 +87,19 @@ def randn(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tenso
     return x
 
 
+def randn_device(shape, seed: int, std: float = 1.0, dtype: str = "f32",
+                 device: str = "cuda") -> torch.Tensor:
+    """Like randn, drawn on the device with a seeded device generator, for
+    inputs too large to draw on the host (the tests copy the slices they
+    check back to the host, so the oracle sees the same values)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if std != 1.0:
+        x = x * std
+    return x.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype])
+
+
 def make_inputs(B: int, T: int, C: int, dtype: str = "f32", seed: int = 0,
                 dout_std: float = 1.0):
     """(qkv (B,T,3C), dout (B,T,C)) on the host, seeds `seed` and `seed+1`."""
