@@ -185,15 +185,13 @@ def run_decode(la, torch, w, dtype, steps, warmup):
     are every key and value row of every head read once, plus the query row
     and the output."""
     from workloads import workload_inputs
-    if dtype == "f16":   # decode is built for fp32 and bf16 only
-        dtype = "bf16"
     qkv_c, _ = workload_inputs(w, dtype)
     qkv = qkv_c.cuda()
     B, T, C, NH = w.B, w.T, w.C, w.NH
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
     out = torch.empty((B, C), dtype=tdt, device="cuda")
     lse = torch.empty((B, NH), device="cuda")
-    fn = la.attn_decode_bf16 if dtype == "bf16" else la.attn_decode
+    fn = {"bf16": la.attn_decode_bf16, "f16": la.attn_decode_f16}.get(dtype, la.attn_decode)
     call = lambda: fn(out, lse, qkv, B, T, C, NH)
     for _ in range(warmup):
         call()
@@ -205,7 +203,7 @@ def run_decode(la, torch, w, dtype, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    esz = 2 if dtype == "bf16" else 4
+    esz = 4 if dtype == "f32" else 2
     nbytes = (2 * B * T * C + 2 * B * C) * esz + B * NH * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"decode over {w.name} {w.label()}", "dtype": dtype,

@@ -199,6 +199,10 @@ int attn_decode(float* out, float* lse, const float* qkv, int B, int T, int C, i
 int attn_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C,
                      int NH);
 
+/* Decode with fp16 (IEEE half) qkv and out (fp32 arithmetic, fp32 lse). */
+int attn_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C,
+                    int NH);
+
 /*
  * Merge of partial attention results over disjoint key sets: the rescale
  * the online softmax applies between key tiles (FlashAttention part of
@@ -217,6 +221,10 @@ int attn_merge(float* out, float* lse, const float* o_parts, const float* lse_pa
 /* Merge with a bf16 out (parts and lse stay fp32). */
 int attn_merge_bf16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
                     int nparts, int B, int T, int C, int NH);
+
+/* Merge with an fp16 out (parts and lse stay fp32). */
+int attn_merge_f16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
+                   int nparts, int B, int T, int C, int NH);
 
 /* Set the HIP stream (a hipStream_t, or NULL for the null stream) used by
  * the calling thread's subsequent calls.  Always returns ATTN_OK. */

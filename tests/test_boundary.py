@@ -168,8 +168,8 @@ def test_binding_rejects_host_tensors():
         la.forward(x, 4, True)
 
 
-DECODE = ["attn_decode", "attn_decode_bf16"]
-MERGE = ["attn_merge", "attn_merge_bf16"]
+DECODE = ["attn_decode", "attn_decode_bf16", "attn_decode_f16"]
+MERGE = ["attn_merge", "attn_merge_bf16", "attn_merge_f16"]
 
 
 @pytest.mark.parametrize("name", DECODE)
@@ -230,3 +230,34 @@ def test_forced_workspace_failure_decode():
     assert res.returncode == 0, res.stderr
     rc, msg = res.stdout.split(" ", 1)
     assert int(rc) == la.ATTN_EHIP and "forced" in msg
+
+
+def test_error_state_is_per_thread():
+    """attn_last_error and the stream are thread-local: a failure in one
+    thread leaves another thread's message untouched."""
+    import threading
+    lib = la.load()
+    seen = {}
+    ready = threading.Event()
+    go = threading.Event()
+
+    def failing():
+        call("attn_forward", 3, 0, 64, 64, 4, 1)       # B < 1
+        seen["a"] = lib.attn_last_error().decode()
+        ready.set()
+
+    def clean():
+        assert lib.attn_set_stream(None) == la.ATTN_OK  # clears this thread's message
+        go.wait(timeout=30)
+        seen["b"] = lib.attn_last_error().decode()
+
+    tb = threading.Thread(target=clean)
+    tb.start()
+    ta = threading.Thread(target=failing)
+    ta.start()
+    ready.wait(timeout=30)
+    go.set()
+    ta.join(timeout=30)
+    tb.join(timeout=30)
+    assert "B, T and NH" in seen["a"]
+    assert seen["b"] == ""

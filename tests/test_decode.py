@@ -40,7 +40,7 @@ DECODE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", DECODE_SHAPES)
 def test_decode_shapes(la, oracle_mod, shape, dtype):
     B, T, C, NH = shape
@@ -53,7 +53,7 @@ def test_decode_shapes(la, oracle_mod, shape, dtype):
     assert_close(lse.cpu(), rl, dtype, "decode lse")
 
 
-@pytest.mark.parametrize("key,dtype", [(3, "f32"), (3, "bf16"), (5, "bf16"), (4, "bf16")])
+@pytest.mark.parametrize("key,dtype", [(3, "f32"), (3, "bf16"), (5, "bf16"), (4, "bf16"), (5, "f16")])
 def test_decode_workload_caches(la, oracle_mod, key, dtype):
     """Decode over the full-size inputs of the GPT-2 layer, long-context and
     ViT workloads (every (b, h) row checked: one row per head is cheap)."""
@@ -101,14 +101,14 @@ MERGE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape,causal,edges", MERGE_CASES)
 def test_merge_recovers_forward(la, oracle_mod, shape, causal, edges, out_dtype):
     B, T, C, NH = shape
     _case(f"merge {out_dtype} B{B} T{T} C{C} NH{NH} causal={causal} edges={edges}")
     qkv, _ = make_inputs(B, T, C, "f32", seed=600 + T)
     o_parts, l_parts = _parts(oracle_mod, qkv, NH, causal, edges)
-    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(out_dtype, torch.float32)
     out, lse = la.merge(o_parts.cuda(), l_parts.cuda(), tdt)
     torch.cuda.synchronize()
     ro, rl = oracle_mod.forward(qkv, NH, causal)

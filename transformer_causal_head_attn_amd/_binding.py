@@ -31,7 +31,8 @@ EXPORTS = (
     "attn_forward_f16", "attn_backward_f16",
     "attn_backward_preprocess_f16", "attn_backward_dkdv_f16", "attn_backward_dq_f16",
     "attn_forward_materialized", "attn_backward_materialized",
-    "attn_decode", "attn_decode_bf16", "attn_merge", "attn_merge_bf16",
+    "attn_decode", "attn_decode_bf16", "attn_decode_f16",
+    "attn_merge", "attn_merge_bf16", "attn_merge_f16",
     "attn_set_stream", "attn_last_error", "attn_release",
 )
 
@@ -71,11 +72,11 @@ def load(path: str | None = None):
             fn.restype = i
         for name in ("attn_backward_preprocess", "attn_backward_preprocess_bf16",
                      "attn_backward_preprocess_f16",
-                     "attn_decode", "attn_decode_bf16"):
+                     "attn_decode", "attn_decode_bf16", "attn_decode_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
             fn.restype = i
-        for name in ("attn_merge", "attn_merge_bf16"):
+        for name in ("attn_merge", "attn_merge_bf16", "attn_merge_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 4 + [i] * 5
             fn.restype = i
@@ -257,6 +258,12 @@ def attn_decode_bf16(out, lse, qkv, B, T, C, NH) -> None:
           _check(qkv, "qkv", h, B * T * 3 * C), int(B), int(T), int(C), int(NH))
 
 
+def attn_decode_f16(out, lse, qkv, B, T, C, NH) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_decode_f16", _check(out, "out", h, B * C), _check(lse, "lse", f, B * NH),
+          _check(qkv, "qkv", h, B * T * 3 * C), int(B), int(T), int(C), int(NH))
+
+
 def attn_merge(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
     f = torch.float32
     _call("attn_merge", _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
@@ -268,6 +275,14 @@ def attn_merge(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
 def attn_merge_bf16(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
     h, f = torch.bfloat16, torch.float32
     _call("attn_merge_bf16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
+          _check(o_parts, "o_parts", f, nparts * B * T * C),
+          _check(lse_parts, "lse_parts", f, nparts * B * NH * T),
+          int(nparts), int(B), int(T), int(C), int(NH))
+
+
+def attn_merge_f16(out, lse, o_parts, lse_parts, nparts, B, T, C, NH) -> None:
+    h, f = torch.float16, torch.float32
+    _call("attn_merge_f16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
           _check(o_parts, "o_parts", f, nparts * B * T * C),
           _check(lse_parts, "lse_parts", f, nparts * B * NH * T),
           int(nparts), int(B), int(T), int(C), int(NH))
@@ -339,11 +354,11 @@ def backward_materialized(dout, qkv, att, NH: int, causal: bool = True):
 
 def decode(qkv: torch.Tensor, NH: int):
     """Allocate (out (B, C), lse (B, NH)) and run the decode for the last
-    position of each sequence (fp32 or bf16 by qkv's dtype)."""
+    position of each sequence (fp32, bf16 or fp16 by qkv's dtype)."""
     B, T, C = _shape(qkv, NH)
     out = torch.empty((B, C), dtype=qkv.dtype, device=qkv.device)
     lse = torch.empty((B, NH), dtype=torch.float32, device=qkv.device)
-    fn = attn_decode_bf16 if qkv.dtype == torch.bfloat16 else attn_decode
+    fn = {torch.bfloat16: attn_decode_bf16, torch.float16: attn_decode_f16}.get(qkv.dtype, attn_decode)
     fn(out, lse, qkv, B, T, C, NH)
     return out, lse
 
@@ -355,6 +370,6 @@ def merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torch.float3
     NH = lse_parts.shape[2]
     out = torch.empty((B, T, C), dtype=out_dtype, device=o_parts.device)
     lse = torch.empty((B, NH, T), dtype=torch.float32, device=o_parts.device)
-    fn = attn_merge_bf16 if out_dtype == torch.bfloat16 else attn_merge
+    fn = {torch.bfloat16: attn_merge_bf16, torch.float16: attn_merge_f16}.get(out_dtype, attn_merge)
     fn(out, lse, o_parts, lse_parts, P, B, T, C, NH)
     return out, lse

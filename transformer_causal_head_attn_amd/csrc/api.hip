@@ -439,6 +439,21 @@ int attn_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int 
                     "attn_decode_bf16 launch");
 }
 
+int attn_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes((long long)B * C, 2), "out"},
+                         {lse, nbytes((long long)B * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 2), "qkv"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, 0);
+    float* ws = nullptr;
+    rc = workspace(attn::decode_workspace_floats(s) * 4, &ws);
+    if (rc) return rc;
+    return launched(attn::launch_decode_f16(out, lse, qkv, ws, s, g_stream),
+                    "attn_decode_f16 launch");
+}
+
 namespace {
 int check_merge(void* out, size_t out_elem, float* lse, const float* o_parts,
                 const float* lse_parts, int nparts, int B, int T, int C, int NH) {
@@ -467,6 +482,15 @@ int attn_merge_bf16(uint16_t* out, float* lse, const float* o_parts, const float
     return launched(attn::launch_merge_bf16(out, lse, o_parts, lse_parts, nparts,
                                             shape_of(B, T, C, NH, 0), g_stream),
                     "attn_merge_bf16 launch");
+}
+
+int attn_merge_f16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
+                    int nparts, int B, int T, int C, int NH) {
+    int rc = check_merge(out, 2, lse, o_parts, lse_parts, nparts, B, T, C, NH);
+    if (rc) return rc;
+    return launched(attn::launch_merge_f16(out, lse, o_parts, lse_parts, nparts,
+                                            shape_of(B, T, C, NH, 0), g_stream),
+                    "attn_merge_f16 launch");
 }
 
 }  // extern "C"

@@ -140,5 +140,9 @@ hipError_t launch_merge_f32(float* out, float* lse, const float* o_parts, const 
                             int P, const Shape& s, hipStream_t st);
 hipError_t launch_merge_bf16(uint16_t* out, float* lse, const float* o_parts,
                              const float* lse_parts, int P, const Shape& s, hipStream_t st);
+hipError_t launch_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, float* ws,
+                             const Shape& s, hipStream_t st);
+hipError_t launch_merge_f16(uint16_t* out, float* lse, const float* o_parts,
+                            const float* lse_parts, int P, const Shape& s, hipStream_t st);
 
 }  // namespace attn

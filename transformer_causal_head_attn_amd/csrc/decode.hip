@@ -25,12 +25,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// 16-byte row chunks as fp32 values.
-template <typename E>
-struct Vec;
-template <>
-struct Vec<float> {
-    static constexpr int N = 4;
+// Element types: storage type T, VEC values per 16-byte chunk, a chunk as
+// fp32 values, and the rounding store of 4 fp32 values (nearest even).
+struct EF32 {
+    typedef float T;
+    static constexpr int VEC = 4;
     static __device__ __forceinline__ void load(float (&x)[4], const float* p) {
         const float4 v = *reinterpret_cast<const float4*>(p);
         x[0] = v.x;
@@ -38,20 +37,48 @@ struct Vec<float> {
         x[2] = v.z;
         x[3] = v.w;
     }
+    static __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
 };
-template <>
-struct Vec<uint16_t> {
-    static constexpr int N = 8;
+template <typename H>   // 16-bit types: H::to_f32 / H::from_f32 on bit patterns
+struct E16 {
+    typedef uint16_t T;
+    static constexpr int VEC = 8;
     static __device__ __forceinline__ void load(float (&x)[8], const uint16_t* p) {
         const uint4 v = *reinterpret_cast<const uint4*>(p);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            x[2 * i] = H::to_f32((uint16_t)(w[i] & 0xffffu));
+            x[2 * i + 1] = H::to_f32((uint16_t)(w[i] >> 16));
         }
     }
+    static __device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+        const uint32_t lo = (uint32_t)H::from_f32(v[0]) | ((uint32_t)H::from_f32(v[1]) << 16);
+        const uint32_t hi = (uint32_t)H::from_f32(v[2]) | ((uint32_t)H::from_f32(v[3]) << 16);
+        *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+    }
 };
+struct HBF16 {
+    static __device__ __forceinline__ float to_f32(uint16_t u) { return bf16_to_f32(u); }
+    static __device__ __forceinline__ uint16_t from_f32(float f) { return f32_to_bf16(f); }
+};
+struct HF16 {
+    static __device__ __forceinline__ float to_f32(uint16_t u) {
+        _Float16 h;
+        __builtin_memcpy(&h, &u, 2);
+        return (float)h;
+    }
+    static __device__ __forceinline__ uint16_t from_f32(float f) {
+        const _Float16 h = (_Float16)f;
+        uint16_t u;
+        __builtin_memcpy(&u, &h, 2);
+        return u;
+    }
+};
+typedef E16<HBF16> EBF16;
+typedef E16<HF16> EF16;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -72,10 +99,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int HS, typename E, int L>
 __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict__ o_part,
                                                                float* __restrict__ lse_part,
-                                                               const E* __restrict__ qkv, int B,
+                                                               const typename E::T* __restrict__ qkv, int B,
                                                                int T, int C, int NH, int nranges,
                                                                float scale_log2) {
-    constexpr int VEC = Vec<E>::N;
+    constexpr int VEC = E::VEC;
     constexpr int G = HS / VEC;          // threads per key row
     constexpr int KPP = kThreads / G;    // key rows per pass
     constexpr int NP = L / KPP;          // passes over the range
@@ -91,11 +118,11 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const int kg = tid / G, sub = tid - (tid / G) * G;
     const size_t C3 = 3 * (size_t)C;
-    const E* base = qkv + (size_t)b * T * C3 + (size_t)h * HS + sub * VEC;
+    const typename E::T* base = qkv + (size_t)b * T * C3 + (size_t)h * HS + sub * VEC;
     const int k0 = r * L;
 
     float q[VEC];
-    Vec<E>::load(q, base + (size_t)(T - 1) * C3);
+    E::load(q, base + (size_t)(T - 1) * C3);
 
     // K rows of the range, and its V rows too when they fit in registers
     // (then both loads are in flight together instead of one after the
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
         const int j = k0 + p * KPP + kg;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) kx[p][i] = 0.f;
-        if (j < T) Vec<E>::load(kx[p], base + C + (size_t)j * C3);
+        if (j < T) E::load(kx[p], base + C + (size_t)j * C3);
     }
     if constexpr (kEarlyV) {
 #pragma unroll
@@ -116,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
             const int j = k0 + p * KPP + kg;
 #pragma unroll
             for (int i = 0; i < VEC; ++i) vx[p][i] = 0.f;
-            if (j < T) Vec<E>::load(vx[p], base + 2 * (size_t)C + (size_t)j * C3);
+            if (j < T) E::load(vx[p], base + 2 * (size_t)C + (size_t)j * C3);
         }
     }
 
@@ -166,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) v[i] = vx[p][i];
             } else {
-                Vec<E>::load(v, base + 2 * (size_t)C + (size_t)j * C3);
+                E::load(v, base + 2 * (size_t)C + (size_t)j * C3);
             }
             const float w = sc[p * KPP + kg];
 #pragma unroll
@@ -197,20 +224,7 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(float* __restrict
 // sets: o_parts (P, B, T, C) fp32 normalised per part, lse_parts (P, B, NH, T).
 // A row whose parts all have lse = -inf (no key at all) gets out 0, lse -inf.
 template <typename OUT>
-__device__ __forceinline__ void store4(OUT* p, const float (&v)[4]);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&v)[4]) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
-}
-
-template <typename OUT>
-__global__ __launch_bounds__(kThreads) void merge_kernel(OUT* __restrict__ out,
+__global__ __launch_bounds__(kThreads) void merge_kernel(typename OUT::T* __restrict__ out,
                                                          float* __restrict__ lse,
                                                          const float* __restrict__ o_parts,
                                                          const float* __restrict__ lse_parts,
@@ -269,13 +283,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(OUT* __restrict__ out,
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[k] *= inv;
     }
-    store4<OUT>(out + (size_t)row * C + c, acc);
+    OUT::store4(out + (size_t)row * C + c, acc);
     if (c % hs == 0)
         lse[((size_t)b * NH + h) * T + t] = (m == -INFINITY) ? -INFINITY : m + __logf(wsum);
 }
 
 template <typename OUT>
-hipError_t merge_launch(OUT* out, float* lse, const float* o_parts, const float* lse_parts, int P,
+hipError_t merge_launch(typename OUT::T* out, float* lse, const float* o_parts, const float* lse_parts, int P,
                         const Shape& s, hipStream_t st) {
     const long long n4 = (long long)s.B * s.T * (s.C / 4);
     const unsigned grid = (unsigned)((n4 + kThreads - 1) / kThreads);
@@ -285,7 +299,7 @@ hipError_t merge_launch(OUT* out, float* lse, const float* o_parts, const float*
 }
 
 template <int HS, typename E, int L>
-hipError_t decode_part_launch(float* o_part, float* lse_part, const E* qkv, int nranges,
+hipError_t decode_part_launch(float* o_part, float* lse_part, const typename E::T* qkv, int nranges,
                               const Shape& s, hipStream_t st) {
     const unsigned grid = (unsigned)((long long)nranges * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
@@ -295,7 +309,7 @@ hipError_t decode_part_launch(float* o_part, float* lse_part, const E* qkv, int 
 }
 
 template <typename E, int L>
-hipError_t decode_part_hs(float* o_part, float* lse_part, const E* qkv, int nranges,
+hipError_t decode_part_hs(float* o_part, float* lse_part, const typename E::T* qkv, int nranges,
                           const Shape& s, hipStream_t st) {
     switch (s.hs) {
         case 16: return decode_part_launch<16, E, L>(o_part, lse_part, qkv, nranges, s, st);
@@ -306,8 +320,9 @@ hipError_t decode_part_hs(float* o_part, float* lse_part, const E* qkv, int nran
     }
 }
 
-template <typename E, typename OUT>
-hipError_t decode_launch(OUT* out, float* lse, const E* qkv, float* ws, const Shape& s,
+template <typename E>
+hipError_t decode_launch(typename E::T* out, float* lse, const typename E::T* qkv, float* ws,
+                         const Shape& s,
                          hipStream_t st) {
     const int L = decode_range_len(s);
     const int nr = (s.T + L - 1) / L;
@@ -318,7 +333,7 @@ hipError_t decode_launch(OUT* out, float* lse, const E* qkv, float* ws, const Sh
     if (e != hipSuccess) return e;
     Shape one = s;
     one.T = 1;
-    return merge_launch<OUT>(out, lse, o_part, lse_part, nr, one, st);
+    return merge_launch<E>(out, lse, o_part, lse_part, nr, one, st);
 }
 
 }  // namespace
@@ -335,22 +350,32 @@ size_t decode_workspace_floats(const Shape& s) {
 
 hipError_t launch_decode_f32(float* out, float* lse, const float* qkv, float* ws, const Shape& s,
                              hipStream_t st) {
-    return decode_launch<float, float>(out, lse, qkv, ws, s, st);
+    return decode_launch<EF32>(out, lse, qkv, ws, s, st);
 }
 
 hipError_t launch_decode_bf16(uint16_t* out, float* lse, const uint16_t* qkv, float* ws,
                               const Shape& s, hipStream_t st) {
-    return decode_launch<uint16_t, uint16_t>(out, lse, qkv, ws, s, st);
+    return decode_launch<EBF16>(out, lse, qkv, ws, s, st);
 }
 
 hipError_t launch_merge_f32(float* out, float* lse, const float* o_parts, const float* lse_parts,
                             int P, const Shape& s, hipStream_t st) {
-    return merge_launch<float>(out, lse, o_parts, lse_parts, P, s, st);
+    return merge_launch<EF32>(out, lse, o_parts, lse_parts, P, s, st);
 }
 
 hipError_t launch_merge_bf16(uint16_t* out, float* lse, const float* o_parts,
                              const float* lse_parts, int P, const Shape& s, hipStream_t st) {
-    return merge_launch<uint16_t>(out, lse, o_parts, lse_parts, P, s, st);
+    return merge_launch<EBF16>(out, lse, o_parts, lse_parts, P, s, st);
+}
+
+hipError_t launch_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, float* ws,
+                             const Shape& s, hipStream_t st) {
+    return decode_launch<EF16>(out, lse, qkv, ws, s, st);
+}
+
+hipError_t launch_merge_f16(uint16_t* out, float* lse, const float* o_parts,
+                            const float* lse_parts, int P, const Shape& s, hipStream_t st) {
+    return merge_launch<EF16>(out, lse, o_parts, lse_parts, P, s, st);
 }
 
 }  // namespace attn
