@@ -275,8 +275,10 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
 
     const int nkt_all = (T + kStream - 1) / kStream;
     const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
-    // last key tile with a key <= some row of this wave
-    const int last = causal ? min(nkt - 1, (r0 + R - 1) / kStream) : nkt - 1;
+    // last key tile with a key <= some row of this wave; none when the
+    // wave has no row below T (its stores are skipped anyway)
+    int last = causal ? min(nkt - 1, (r0 + R - 1) / kStream) : nkt - 1;
+    if (r0 >= T) last = -1;
 
     auto scores = [&](const uint16_t* kt_lds, f32x4 (&sc)[QB][4]) {
 #pragma unroll
@@ -498,7 +500,8 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
         __syncthreads();
         if (qt + 1 < nqt) fetch(qt + 1);
         const int q0 = qt * kStream;
-        if (causal && q0 + kStream - 1 < c0) continue;   // every query before every key here
+        // every query before every key here, or no key row of this wave below T
+        if (c0 >= T || (causal && q0 + kStream - 1 < c0)) continue;
         const bool diag = causal && (q0 < c0 + R - 1);
 
         // Two 16-query blocks n = 2t, 2t+1 at a time: scores and dP, then P and
@@ -647,7 +650,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
             rv.fetch(vbase, C3, (kt + 1) * kStream, T, L.tid);
         }
         const int k0 = kt * kStream;
-        if (causal && k0 > r0 + R - 1) continue;
+        if (r0 >= T || (causal && k0 > r0 + R - 1)) continue;   // no row of this wave sees a key here
         const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 
         // Two 16-key blocks n = 2t, 2t+1 at a time: S^T and dP^T, then dS packed
