@@ -1,7 +1,7 @@
 """fp64 CPU oracle for multi-head scaled-dot-product self-attention.
 
 TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline
-leg of the benchmark import this module to judge the HIP library.  The library
+leg of the benchmark import this module to check the HIP library.  The library
 and its Python binding never import it, and the two share no code.
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over

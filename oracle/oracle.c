@@ -3,7 +3,7 @@
  * self-attention, forward and analytic backward, causal or not.
  *
  * TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the
- * CPU-baseline leg of the benchmark call it to judge the HIP library.  The
+ * CPU-baseline leg of the benchmark call it to check the HIP library.  The
  * library never links, loads or calls it, and the two share no code.
  *
  * Sources (cited by page title and the part of the page followed):
