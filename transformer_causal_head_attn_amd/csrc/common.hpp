@@ -46,6 +46,14 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): wait until every global load the wave has issued has
+// returned (immediate: vmcnt field 0, expcnt 7 and lgkmcnt 15, i.e. no wait on
+// those).  Placed after a kernel's prologue loads, it also tells the
+// compiler's wait-count tracking that no load is outstanding when the main
+// loop starts, so the loop's first uses of the prologue's registers need no
+// wait that would also cover the next tile's loads issued in the loop.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // D += A * B on the fp32 matrix cores, one 16x16 output block per wave.
 // Lane l supplies A[l%16][l/16] and B[l/16][l%16] (K = 4); the result
 // register i of lane l is D[4*(l/16) + i][l%16].

@@ -173,22 +173,43 @@ __device__ __forceinline__ void store4(uint16_t* p, const f32x4& v) {
     __builtin_memcpy(p, &r, 8);
 }
 
-// A kStream x HS bf16 tile held in registers between its global load and
+// Buffer descriptor over rows row0 .. min(row0 + kStream, T) - 1 of one head's
+// slice (rows ld_bytes apart, row_bytes used per row).  A raw buffer load
+// whose offset lies at or past num_records returns zeros instead of reading
+// memory, so the 16-byte loads of rows >= T need no predicate and read
+// nothing past the tensor; every chunk is either wholly inside (rows < T) or
+// wholly outside (rows >= T, offsets >= (T - row0) * ld_bytes), because
+// ld_bytes >= row_bytes.  Word 3 is the gfx9 raw-buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, uint32_t ld_bytes,
+                                                            int row0, int T, uint32_t row_bytes) {
+    const int valid = min(T - row0, kStream);
+    const uint32_t num = valid > 0 ? (uint32_t)(valid - 1) * ld_bytes + row_bytes : 0u;
+    const char* p = reinterpret_cast<const char*>(base) + (size_t)row0 * ld_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, (int)num, 0x00020000);
+}
+
+// A kStream x HS 16-bit tile held in registers between its global load and
 // its LDS store (row-major, stride LDR); rows >= T are zero.
 template <int HS>
 struct TileRegs {
     static constexpr int CH = HS / 8;                        // 16-byte chunks per row
     static constexpr int TOTAL = kStream * CH;
     static constexpr int N = (TOTAL + kThreads - 1) / kThreads;
+    static constexpr bool FULL = TOTAL % kThreads == 0;      // every thread holds N chunks
     uint4 v[N];
     __device__ __forceinline__ void fetch(const uint16_t* base, size_t ld, int row0, int T, int tid) {
+        const uint32_t ldb = (uint32_t)(ld * 2);
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, ldb, row0, T, HS * 2);
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             const int e = tid + k * kThreads;
             const int row = e / CH, c = e - (e / CH) * CH;
-            const int j = row0 + row;
+            const uint32_t off = (uint32_t)row * ldb + 16u * (uint32_t)c;
             v[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (e < TOTAL && j < T) v[k] = *reinterpret_cast<const uint4*>(base + (size_t)j * ld + 8 * c);
+            if (FULL || e < TOTAL) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+                __builtin_memcpy(&v[k], &x, 16);
+            }
         }
     }
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -196,7 +217,7 @@ struct TileRegs {
         for (int k = 0; k < N; ++k) {
             const int e = tid + k * kThreads;
             const int row = e / CH, c = e - (e / CH) * CH;
-            if (e < TOTAL) *reinterpret_cast<uint4*>(lds + row * Geom<HS>::LDR + 8 * c) = v[k];
+            if (FULL || e < TOTAL) *reinterpret_cast<uint4*>(lds + row * Geom<HS>::LDR + 8 * c) = v[k];
         }
     }
 };
@@ -365,6 +386,7 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
         f32x4 sc[QB][4];
         rk.fetch(kbase, C3, 0, T, L.tid);
         rv.fetch(vbase, C3, 0, T, L.tid);
+        wait_global_loads();
         for (int j = 0; j < nkt; ++j) {
             __syncthreads();
             rk.store(Ks, L.tid);
@@ -479,23 +501,27 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
     const int qt0 = causal ? (kvt * BN) / kStream : 0;
     TileRegs<HS> rq, rd;
     float rl = 0.f, rD = 0.f;
+    // lse and D of the tile's rows are loaded raw and only transformed when
+    // stored, so nothing waits for them before the next step
     auto fetch = [&](int qt) {
         rq.fetch(qbase, C3, qt * kStream, T, L.tid);
         rd.fetch(dobase, (size_t)C, qt * kStream, T, L.tid);
         if (L.tid < kStream) {
-            const int q = qt * kStream + L.tid;
-            rl = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
-            rD = (q < T) ? drow[q] : 0.f;
+            const int q = min(qt * kStream + L.tid, T - 1);
+            rl = lrow[q];
+            rD = drow[q];
         }
     };
     fetch(qt0);
+    wait_global_loads();
     for (int qt = qt0; qt < nqt; ++qt) {
         __syncthreads();
         rq.store(Qs, L.tid);
         rd.store(dOs, L.tid);
         if (L.tid < kStream) {
-            Ls[L.tid] = rl;
-            Dl[L.tid] = rD;
+            const bool in = qt * kStream + L.tid < T;
+            Ls[L.tid] = in ? rl * kLog2e : INFINITY;   // +inf -> P = 0
+            Dl[L.tid] = in ? rD : 0.f;
         }
         __syncthreads();
         if (qt + 1 < nqt) fetch(qt + 1);
@@ -640,6 +666,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     TileRegs<HS> rk, rv;
     rk.fetch(kbase, C3, 0, T, L.tid);
     rv.fetch(vbase, C3, 0, T, L.tid);
+    wait_global_loads();
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
         rk.store(Ks, L.tid);
@@ -720,7 +747,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
 // Each runs its tile function on one tile, or on a balanced pair of causal
 // tiles (see pair_of_block).
 template <typename E, int HS, int QB>
-__global__ __launch_bounds__(kThreads) void fwd_half_kernel(uint16_t* __restrict__ out,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void fwd_half_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
@@ -736,7 +763,7 @@ __global__ __launch_bounds__(kThreads) void fwd_half_kernel(uint16_t* __restrict
 }
 
 template <typename E, int HS, int KB>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_half_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_half_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
@@ -752,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_half_kernel(
 }
 
 template <typename E, int HS, int QB>
-__global__ __launch_bounds__(kThreads) void bwd_dq_half_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void bwd_dq_half_kernel(
     uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
