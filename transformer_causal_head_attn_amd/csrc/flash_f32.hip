@@ -58,14 +58,24 @@ struct TileRegs {
     static constexpr int C4 = HS / 4;
     static constexpr int N = kTile * C4 / kThreads;   // float4 per thread
     float4 v[N];
+    // Raw buffer loads over rows row0 .. min(row0 + kTile, T) - 1: a load at
+    // or past num_records returns zeros instead of reading memory, so rows
+    // >= T need no predicate (each 16-byte chunk lies wholly inside or wholly
+    // past that bound, as ld >= HS).  Word 3 is the gfx9 raw-buffer format word.
     __device__ __forceinline__ void fetch(const float* base, size_t ld, int row0, int T, int tid) {
+        const uint32_t ldb = (uint32_t)(ld * 4);
+        const int valid = min(T - row0, kTile);
+        const uint32_t num = valid > 0 ? (uint32_t)(valid - 1) * ldb + HS * 4u : 0u;
+        const float* p = base + (size_t)row0 * ld;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, (int)num, 0x00020000);
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             const int e = tid + k * kThreads;
             const int row = e / C4, c4 = e % C4;
-            const int j = row0 + row;
-            v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < T) v[k] = *reinterpret_cast<const float4*>(base + (size_t)j * ld + 4 * c4);
+            const uint32_t off = (uint32_t)row * ldb + 16u * (uint32_t)c4;
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+            __builtin_memcpy(&v[k], &x, 16);
         }
     }
     template <int LDK>
@@ -158,6 +168,7 @@ __device__ __forceinline__ void fwd_f32_tile(int tile_, int bh_, float* __restri
     TileRegs<HS> rk, rv;
     rk.fetch(kbase, C3, 0, T, L.tid);
     rv.fetch(vbase, C3, 0, T, L.tid);
+    wait_global_loads();
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
         rk.template store<LDK>(Ks, L.tid);
@@ -329,20 +340,24 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     auto fetch = [&](int qt) {
         rq.fetch(qbase, C3, qt * kTile, T, L.tid);
         rd.fetch(dobase, (size_t)C, qt * kTile, T, L.tid);
+        // lse and D are loaded raw and transformed when stored, so nothing
+        // waits for them before the next step
         if (L.tid < kTile) {
-            const int q = qt * kTile + L.tid;
-            rl = (q < T) ? lrow[q] * kLog2e : INFINITY;   // +inf -> P = 0
-            rD = (q < T) ? drow[q] : 0.f;
+            const int q = min(qt * kTile + L.tid, T - 1);
+            rl = lrow[q];
+            rD = drow[q];
         }
     };
     fetch(qt0);
+    wait_global_loads();
     for (int qt = qt0; qt < nt; ++qt) {
         __syncthreads();
         rq.template store<LDK>(Qs, L.tid);
         rd.template store<LDK>(dOs, L.tid);
         if (L.tid < kTile) {
-            Ls[L.tid] = rl;
-            Dl[L.tid] = rD;
+            const bool in = qt * kTile + L.tid < T;
+            Ls[L.tid] = in ? rl * kLog2e : INFINITY;   // +inf -> P = 0
+            Dl[L.tid] = in ? rD : 0.f;
         }
         __syncthreads();
         if (qt + 1 < nt) fetch(qt + 1);
@@ -458,6 +473,7 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
     TileRegs<HS> rk, rv;
     rk.fetch(kbase, C3, 0, T, L.tid);
     rv.fetch(vbase, C3, 0, T, L.tid);
+    wait_global_loads();
     for (int kt = 0; kt < nkt; ++kt) {
         __syncthreads();
         rk.template store<LDK>(Ks, L.tid);
