@@ -44,7 +44,7 @@ struct Lane {
     int tid, w, l, r16, g;
     __device__ Lane() {
         tid = threadIdx.x;
-        w = tid >> 6;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: per-wave tests branch on scalars
         l = tid & 63;
         r16 = l & 15;
         g = l >> 4;

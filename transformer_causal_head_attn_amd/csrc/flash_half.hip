@@ -54,7 +54,7 @@ struct Lane {
     int tid, w, l, r16, g;
     __device__ Lane() {
         tid = threadIdx.x;
-        w = tid >> 6;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: per-wave tests branch on scalars
         l = tid & 63;
         r16 = l & 15;
         g = l >> 4;
@@ -74,6 +74,12 @@ struct BF16 {   // bfloat16: v_mfma_f32_16x16x32_bf16
     static __device__ __forceinline__ float bits_to_f32(uint32_t u) {   // low 16 bits
         return __uint_as_float(u << 16);
     }
+    static __device__ __forceinline__ V8 ones() {   // eight 1.0 (0x3F80)
+        const uint4 u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        V8 r;
+        __builtin_memcpy(&r, &u, 16);
+        return r;
+    }
 };
 struct F16 {   // IEEE half: v_mfma_f32_16x16x32_f16
     typedef _Float16 S;
@@ -87,6 +93,12 @@ struct F16 {   // IEEE half: v_mfma_f32_16x16x32_f16
         _Float16 x;
         __builtin_memcpy(&x, &h, 2);
         return (float)x;
+    }
+    static __device__ __forceinline__ V8 ones() {   // eight 1.0 (0x3C00)
+        const uint4 u = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+        V8 r;
+        __builtin_memcpy(&r, &u, 16);
+        return r;
     }
 };
 template <typename E>
@@ -284,12 +296,16 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
             qreg[qb][s] = row_chunk_global<E, HS>(qbase + (size_t)q * C3, q < T, s, L.g);
     }
 
-    float m[QB], lsum[QB];
-    f32x4 o[QB][G::MB];
+    // lsum[qb]: the row sums of the 16-bit P that enter P V, formed on the
+    // matrix cores as ones^T P^T (every entry of the block holds the sum of
+    // the lane's query row), so the softmax spends no VALU add on them
+    float m[QB];
+    f32x4 o[QB][G::MB], lsum[QB];
+    const V8<E> ones = E::ones();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = -INFINITY;
-        lsum[qb] = 0.f;
+        lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb) o[qb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -330,14 +346,14 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int row = r0 + 16 * qb + L.r16;
-            if (edge) {   // keys >= lim are masked (select, not branch)
+            if (edge) {   // keys >= lim are masked: key k0 + 4g + 16n + i stays iff 16n + i < d
                 const int lim = causal ? min(T, row + 1) : T;
-                const int kb0 = k0 + 4 * L.g;
+                const int d = lim - (k0 + 4 * L.g);
 #pragma unroll
                 for (int n = 0; n < 4; ++n)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        sc[qb][n][i] = (kb0 + 16 * n + i < lim) ? sc[qb][n][i] : -INFINITY;
+                        sc[qb][n][i] = (16 * n + i < d) ? sc[qb][n][i] : -INFINITY;
             }
             float mloc = -INFINITY;
 #pragma unroll
@@ -360,9 +376,7 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
             for (int n = 0; n < 4; ++n) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(fmaf(sc[qb][n][i], scale_log2, nm));
-                    sc[qb][n][i] = p;
-                    lsum[qb] += p;
+                    sc[qb][n][i] = fast_exp2(fmaf(sc[qb][n][i], scale_log2, nm));
                 }
             }
         }
@@ -371,7 +385,10 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
         for (int t = 0; t < 2; ++t) {
             V8<E> pb[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pb[qb] = pack_pair<E>(sc[qb][2 * t], sc[qb][2 * t + 1]);
+            for (int qb = 0; qb < QB; ++qb) {
+                pb[qb] = pack_pair<E>(sc[qb][2 * t], sc[qb][2 * t + 1]);
+                lsum[qb] = E::mfma(ones, pb[qb], lsum[qb]);
+            }
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
                 const V8<E> vop = col_operand<E, HS>(vt_lds, 32 * t, 16 * mb, L.l);
@@ -405,7 +422,7 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = r0 + 16 * qb + L.r16;
-        const float ltot = group4_sum(lsum[qb]);
+        const float ltot = lsum[qb][0];
         if (row < T) {
             const float inv = 1.0f / ltot;
             uint16_t* orow = out + ((size_t)b * T + row) * C + (size_t)h * HS;
@@ -556,15 +573,21 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
                         dp[kb] = E::mfma(dc, vreg[kb][st], dp[kb]);
                     }
                 }
+                if (diag) {   // query q0 + 16n + 4g + i sees key c0 + 16kb + r16 iff i >= d
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const int d = c0 + 16 * kb + L.r16 - (q0 + 16 * n + 4 * L.g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[kb][i] = (i >= d) ? s[kb][i] : -INFINITY;
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ql = 16 * n + 4 * L.g + i;
                     const float l2 = Ls[ql], dd = Dl[ql];
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
-                        // causal: query q0 + ql sees key c0 + 16kb + r16 only if q >= kv
-                        pv = (!diag || q0 + ql >= c0 + 16 * kb + L.r16) ? pv : 0.f;
+                        const float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
                         p[kb][u][i] = pv;
                         ds[kb][u][i] = pv * (dp[kb][i] - dd);
                     }
@@ -707,13 +730,15 @@ __device__ __forceinline__ void bwd_dq_half_tile(
                 }
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const int row = r0 + 16 * qb + L.r16;
-                    const int lim = edge ? (causal ? min(T, row + 1) : T) : 0x7fffffff;
-                    const int kb0 = k0 + 16 * n + 4 * L.g;
+                    if (edge) {   // key k0 + 16n + 4g + i stays iff i < d (else P = 0)
+                        const int row = r0 + 16 * qb + L.r16;
+                        const int d = (causal ? min(T, row + 1) : T) - (k0 + 16 * n + 4 * L.g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[qb][i] = (i < d) ? s[qb][i] : -INFINITY;
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
-                        pv = (kb0 + i < lim) ? pv : 0.f;
+                        const float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
                         ds[qb][u][i] = pv * (dp[qb][i] - Dq[qb]);
                     }
                 }
