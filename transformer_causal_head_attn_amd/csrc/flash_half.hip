@@ -243,19 +243,35 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // the grid, so it is used only while at least two paired workgroups per CU
 // remain (pair_tiles on the host).  Otherwise tiles run one per workgroup,
 // heaviest first (the longest-first order of kernel 8 in llm.c's
-// attention_backward.cu).
+// attention_backward.cu), dealt to the CUs like a snake draft: workgroups
+// that are resident together (ids c, c + ncu, c + 2 ncu, ... share a CU when
+// the whole round fits) take the sorted list in alternating directions, so
+// a CU that got one of the heaviest tiles in the first round gets one of the
+// lightest of the second.  The reversal keeps id % 8, the XCD a workgroup
+// is dispatched to, and a wrong guess about placement only costs balance.
 // Consecutive workgroup ids walk the heads, so all tiles of a head land on
 // one XCD (one L2) whenever B*NH is a multiple of 8.
+struct Deal {
+    int ncu;      // compute units (a multiple of 8 for the snake)
+    int rounds;   // workgroups per CU resident at once
+};
 __device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool heavy_high,
-                                              int& bh, int& ta, int& tb) {
-    const int bid = blockIdx.x;
-    const int rank = bid / BH;
-    bh = bid - rank * BH;
+                                              Deal deal, int& bh, int& ta, int& tb) {
+    int idx = blockIdx.x;
+    if (!paired && (deal.ncu & 7) == 0) {
+        const int r = idx / deal.ncu;
+        if ((r & 1) && r < deal.rounds && (r + 1) * deal.ncu <= (int)gridDim.x) {
+            const int c = idx - r * deal.ncu;
+            idx = r * deal.ncu + (deal.ncu - 8 - (c & ~7) + (c & 7));
+        }
+    }
+    const int rank = idx / BH;
+    bh = idx - rank * BH;
     if (paired) {
         ta = rank;
         tb = nt - 1 - rank;
         if (tb == ta) tb = -1;
-    } else {   // heaviest tile first, so the last workgroups to start are short
+    } else {
         ta = heavy_high ? nt - 1 - rank : rank;
         tb = -1;
     }
@@ -776,10 +792,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
-                                                            float scale_log2, int paired) {
+                                                            float scale_log2, int paired, Deal deal) {
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
     fwd_half_tile<E, HS, QB>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
     if (tb >= 0) {
         __syncthreads();
@@ -792,10 +808,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
-    float scale_log2, int paired) {
+    float scale_log2, int paired, Deal deal) {
     const int nt = (T + 64 * KB - 1) / (64 * KB);
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, deal, bh, ta, tb);
     bwd_dkdv_half_tile<E, HS, KB>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
@@ -808,15 +824,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
     uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
-    float scale_log2, int paired) {
+    float scale_log2, int paired, Deal deal) {
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
     bwd_dq_half_tile<E, HS, QB>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
         bwd_dq_half_tile<E, HS, QB>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
     }
+}
+
+// CUs and resident workgroups per CU for a kernel (one occupancy query per
+// kernel, repeated when the current device changes).
+template <auto Kernel>
+Deal deal_for() {
+    static int cached_dev = -1, cached_rounds = 1;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != cached_dev) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
+        cached_rounds = n;
+        cached_dev = dev;
+    }
+    return Deal{device_cu_count(), cached_rounds};
 }
 
 constexpr int kQB = 2;
@@ -832,8 +864,9 @@ hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Sha
     const bool paired = pair_tiles(nqt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
+    const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>();
     hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
-                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)paired);
+                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)paired, deal);
     return hipGetLastError();
 }
 
@@ -857,9 +890,10 @@ hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qk
     const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
+    const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB>>();
     hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
-                       (int)paired);
+                       (int)paired, deal);
     return hipGetLastError();
 }
 
@@ -871,9 +905,10 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
     const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
+    const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB>>();
     hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
-                       (int)paired);
+                       (int)paired, deal);
     return hipGetLastError();
 }
 
