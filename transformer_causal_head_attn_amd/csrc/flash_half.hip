@@ -106,7 +106,9 @@ using V8 = typename E::V8;
 
 template <int HS>
 struct Geom {
-    static constexpr int LDR = HS + 8;                  // LDS row stride (elements)
+    // LDS row stride (elements; a multiple of 8 keeps 16-byte rows aligned).
+    // +16 for hs >= 64 measured faster than +8 (dK/dV at hs = 128: -9%).
+    static constexpr int LDR = HS >= 64 ? HS + 16 : HS + 8;
     static constexpr int KSTEPS = HS >= 32 ? HS / 32 : 1;
     static constexpr int MB = HS / 16;
 };
