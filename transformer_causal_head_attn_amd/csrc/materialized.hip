@@ -183,43 +183,74 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
     float4 ra[NA4];
     float4 rbv[NB4];
     const bool vecA = (T % 4) == 0;
+    // Loads are raw buffer loads over the rows of the block that lie below T
+    // (a load at or past num_records returns zeros), so none is predicated;
+    // the causal and column masks are selects, applied only to blocks that
+    // hold the diagonal or columns past T.  Word 3 is the gfx9 raw-buffer
+    // format word.
     auto fetch = [&](int kt) {
         const int R0 = TRANS ? kt * kTile : row0;   // A rows of the block
         const int C0 = TRANS ? row0 : kt * kTile;   // A columns of the block
         constexpr int CQ = ACOLS / 4;               // float4 per block row
+        if (vecA) {
+            const uint32_t rowb = (uint32_t)T * 4u;
+            const int valid = min(T - R0, AROWS);
+            // uniform values: readfirstlane keeps the descriptor in scalar registers
+            const uint32_t num = __builtin_amdgcn_readfirstlane(valid > 0 ? (uint32_t)valid * rowb : 0u);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(Ah + (size_t)R0 * T), (short)0, (int)num, 0x00020000);
 #pragma unroll
-        for (int k = 0; k < NA4; ++k) {
-            const int e = L.tid + k * kThreads;
-            const int gr = R0 + e / CQ, gc = C0 + 4 * (e % CQ);
-            float v[4];
-            if (vecA) {
-                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (gr < T && gc < T && (!causal || gc <= gr))
-                    q = *reinterpret_cast<const float4*>(Ah + (size_t)gr * T + gc);
-                v[0] = q.x;
-                v[1] = q.y;
-                v[2] = q.z;
-                v[3] = q.w;
-            } else {
+            for (int k = 0; k < NA4; ++k) {
+                const int e = L.tid + k * kThreads;
+                const int rr = e / CQ, cc = 4 * (e % CQ);
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (int)((uint32_t)rr * rowb + (uint32_t)(C0 + cc) * 4u), 0, 0);
+                __builtin_memcpy(&ra[k], &x, 16);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NA4; ++k) {
+                const int e = L.tid + k * kThreads;
+                const int gr = R0 + e / CQ, gc = C0 + 4 * (e % CQ);
+                float v[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    v[u] = (gr < T && gc + u < T) ? Ah[(size_t)gr * T + gc + u] : 0.f;
+                    v[u] = (gr < T && gc + u < T && (!causal || gc + u <= gr)) ? Ah[(size_t)gr * T + gc + u]
+                                                                              : 0.f;
+                ra[k] = make_float4(v[0], v[1], v[2], v[3]);
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = (!causal || gc + u <= gr) ? v[u] : 0.f;
-            ra[k] = make_float4(v[0], v[1], v[2], v[3]);
         }
+        const uint32_t ldbb = (uint32_t)(ldb * 4);
+        const int bvalid = min(T - kt * kTile, kTile);
+        const uint32_t bnum =
+            __builtin_amdgcn_readfirstlane(bvalid > 0 ? (uint32_t)(bvalid - 1) * ldbb + HS * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(bb + (size_t)kt * kTile * ldb), (short)0, (int)bnum, 0x00020000);
 #pragma unroll
         for (int k = 0; k < NB4; ++k) {
             const int e = L.tid + k * kThreads;
-            const int kk = kt * kTile + e / C4;
-            rbv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kk < T) rbv[k] = *reinterpret_cast<const float4*>(bb + (size_t)kk * ldb + 4 * (e % C4));
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+                rb, (int)((uint32_t)(e / C4) * ldbb + 16u * (uint32_t)(e % C4)), 0, 0);
+            __builtin_memcpy(&rbv[k], &x, 16);
         }
     };
-    auto store = [&]() {
-        // LDS holds the A block as it lies in memory: As[r][c] = A[R0 + r][C0 + c]
+    auto store = [&](int kt) {
+        // LDS holds the A block as it lies in memory: As[r][c] = A[R0 + r][C0 + c].
+        // The masks are applied here, when the loads have landed anyway.
         constexpr int CQ = ACOLS / 4;
+        const int R0 = TRANS ? kt * kTile : row0;
+        const int C0 = TRANS ? row0 : kt * kTile;
+        if (vecA && ((C0 + ACOLS > T) || (causal && C0 + ACOLS - 1 > R0))) {
+#pragma unroll
+            for (int k = 0; k < NA4; ++k) {
+                const int e = L.tid + k * kThreads;
+                const int gr = R0 + e / CQ, gc = C0 + 4 * (e % CQ);
+                ra[k].x = (gc + 0 < T && (!causal || gc + 0 <= gr)) ? ra[k].x : 0.f;
+                ra[k].y = (gc + 1 < T && (!causal || gc + 1 <= gr)) ? ra[k].y : 0.f;
+                ra[k].z = (gc + 2 < T && (!causal || gc + 2 <= gr)) ? ra[k].z : 0.f;
+                ra[k].w = (gc + 3 < T && (!causal || gc + 3 <= gr)) ? ra[k].w : 0.f;
+            }
+        }
 #pragma unroll
         for (int k = 0; k < NA4; ++k) {
             const int e = L.tid + k * kThreads;
@@ -240,9 +271,10 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
         }
     };
     if (k0 < k1) fetch(k0);
+    wait_global_loads();
     for (int kt = k0; kt < k1; ++kt) {
         __syncthreads();
-        store();
+        store(kt);
         __syncthreads();
         if (kt + 1 < k1) fetch(kt + 1);
         // C^T[d][row] += sum_kk Bm[kk][d] * op(A)[row][kk],  kk = 16g + s
