@@ -28,6 +28,10 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kThreads = 256;
+// apply_kernel: 16-row output blocks per wave, and output rows per workgroup
+// (the launchers size the grid with the same constant)
+constexpr int kApplyRB = 1;
+constexpr int kApplyRows = 4 * 16 * kApplyRB;
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -145,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
                                                          int NH, int causal, size_t ldb,
                                                          size_t ldc, size_t batch_b,
                                                          size_t batch_c) {
-    constexpr int RB = 1;                        // 16-row output blocks per wave
-    constexpr int BR = 4 * 16 * RB;              // output rows per workgroup (64)
+    constexpr int RB = kApplyRB;                 // 16-row output blocks per wave
+    constexpr int BR = kApplyRows;               // output rows per workgroup (64)
     // LDS A block: op(A) = A: BR rows x 64 contraction columns (stride 68);
     // op(A) = A^T: 64 contraction rows x BR output columns (stride BR + 1).
     constexpr int AROWS = TRANS ? kTile : BR;
@@ -296,11 +300,20 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
                 }
             }
 #pragma unroll
-            for (int s2 = 0; s2 < 16; ++s2) {
-                const int kk = 16 * L.g + s2;
+            for (int s4 = 0; s4 < 16; s4 += 4) {
+                float bv[4][MB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    o[rb][mb] = mfma_f32(Bs[kk * LDB + 16 * mb + L.r16], av[s2], o[rb][mb]);
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) bv[u][mb] = Bs[(16 * L.g + s4 + u) * LDB + 16 * mb + L.r16];
+                // the 4 x MB reads (paired into ds_read2) ahead of their MFMAs,
+                // so one wait covers a group instead of one wait per pair
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * MB / 2, 0);   // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB, 0);       // MFMAs
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) o[rb][mb] = mfma_f32(bv[u][mb], av[s4 + u], o[rb][mb]);
             }
         }
     }
@@ -514,7 +527,7 @@ hipError_t fwd_hs(float* out, float* preatt, float* att, const float* qkv, const
     const float scale = (float)(1.0 / sqrt((double)HS));
     e = launch_softmax_rows(att, preatt, s.T, rows, s.causal, scale * kLog2e, st);
     if (e != hipSuccess) return e;
-    const unsigned ga = (unsigned)(BH * nt);
+    const unsigned ga = (unsigned)(BH * ((s.T + kApplyRows - 1) / kApplyRows));
     hipLaunchKernelGGL((apply_kernel<HS, false>), dim3(ga), dim3(kThreads), 0, st, out, att,
                        qkv + 2 * s.C, s.T, s.NH, s.causal, C3, (size_t)s.C, bstride,
                        (size_t)s.T * s.C);
@@ -538,7 +551,7 @@ hipError_t bwd_hs(float* dqkv, float* dpreatt, float* datt, const float* dout, c
     const float scale = (float)(1.0 / sqrt((double)HS));
     e = launch_softmax_bwd_rows(dpreatt, att, datt, s.T, rows, s.causal, scale, st);
     if (e != hipSuccess) return e;
-    const unsigned g = (unsigned)(BH * nt);
+    const unsigned g = (unsigned)(BH * ((s.T + kApplyRows - 1) / kApplyRows));
     // dv = att^T dO
     hipLaunchKernelGGL((apply_kernel<HS, true>), dim3(g), dim3(kThreads), 0, st, dqkv + 2 * C, att,
                        dout, s.T, s.NH, s.causal, C, C3, bo, bq);
