@@ -394,12 +394,16 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 s = mfma_f32(qa.w, kreg[4 * c + 3], s);
                 dp = mfma_f32(da.w, vreg[4 * c + 3], dp);
             }
+            if (diag) {   // causal: query qt*64 + 16n + 4g + i sees kvrow iff i >= d
+                const int d = kvrow - (qt * kTile + 16 * n + 4 * L.g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = (i >= d) ? s[i] : -INFINITY;
+            }
             float p[4], ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ql = 16 * n + 4 * L.g + i;
-                float pv = fast_exp2(s[i] * scale_log2 - Ls[ql]);
-                pv = (!diag || qt * kTile + ql >= kvrow) ? pv : 0.f;   // causal: q >= kv
+                const float pv = fast_exp2(fmaf(s[i], scale_log2, -Ls[ql]));
                 p[i] = pv;
                 ds[i] = pv * (dp[i] - Dl[ql]);
             }
@@ -495,7 +499,8 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
             rk.fetch(kbase, C3, (kt + 1) * kTile, T, L.tid);
             rv.fetch(vbase, C3, (kt + 1) * kTile, T, L.tid);
         }
-        const int lim = (kt == nkt - 1) ? (causal ? min(T, qrow + 1) : T) : 0x7fffffff;
+        const bool edge = kt == nkt - 1;   // the tile that holds the diagonal and the T tail
+        const int lim = causal ? min(T, qrow + 1) : T;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
             // s[i] = S[qrow][kv = kt*64 + 16n + 4g + i], dp likewise
@@ -515,12 +520,15 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
                 s = mfma_f32(ka.w, qreg[4 * c + 3], s);
                 dp = mfma_f32(va.w, doreg[4 * c + 3], dp);
             }
+            if (edge) {   // key kt*64 + 16n + 4g + i stays iff i < d (else P = 0)
+                const int d = lim - (kt * kTile + 16 * n + 4 * L.g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = (i < d) ? s[i] : -INFINITY;
+            }
             float ds[4];
-            const int kb0 = kt * kTile + 16 * n + 4 * L.g;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float pv = fast_exp2(s[i] * scale_log2 - l2);
-                pv = (kb0 + i < lim) ? pv : 0.f;
+                const float pv = fast_exp2(fmaf(s[i], scale_log2, -l2));
                 ds[i] = pv * (dp[i] - Dq);
             }
 #pragma unroll
