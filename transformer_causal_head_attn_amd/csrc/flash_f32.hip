@@ -24,10 +24,11 @@
 //  * the contraction index k of every Q.K product is numbered
 //    k = (hs/4)*g + s for lane group g and step s, so each lane's operand
 //    values are contiguous and move with 16-byte loads;
-//  * causal work skips every key tile beyond the diagonal; in the backward
-//    kernels a workgroup runs a light and a heavy causal tile back to back so
-//    all workgroups carry equal work (no tail), while the forward, which
-//    holds more workgroups per CU, runs its tiles heaviest first;
+//  * causal work skips every key tile beyond the diagonal; in the dQ kernel
+//    a workgroup runs a light and a heavy causal tile back to back so all
+//    workgroups carry equal work (no tail), while the forward and dK/dV
+//    kernels run their tiles heaviest first (measured faster: their
+//    occupancy does not divide the paired grid into whole rounds);
 //    consecutive workgroup ids walk the heads so that all tiles of a head
 //    land on one XCD (one L2) whenever B*NH is a multiple of 8;
 //  * the forward raises a row's running maximum only when a tile's maximum
@@ -629,7 +630,11 @@ template <int HS>
 hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
                        const float* D, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
-    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
+    // Two workgroups fit per CU, so equal pairs left the last half round of
+    // the GPT-2 layer's grid (768 pairs on 512 slots) running one per CU;
+    // unpaired tiles, heaviest first, let the hardware fill freed slots with
+    // lighter ones (GPT-2 layer dK/dV -3.4%, long context unchanged).
+    const bool paired = false;
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
