@@ -71,7 +71,8 @@ extern "C" {
 #define ATTN_OK 0
 /* null pointer, B/T/NH < 1, C < NH, C % NH != 0, causal not 0/1, misaligned
  * or overlapping buffers, or a tensor too large for 32-bit in-batch offsets
- * (T*3C >= 2^31, or T*T >= 2^31 for the materialised calls) */
+ * (T*3C >= 2^31, 64*3C*4 >= 2^32 bytes for one tile, or T*T >= 2^31 for the
+ * materialised calls) */
 #define ATTN_EINVAL (-1)
 /* head size hs = C/NH not in {16, 32, 64, 128} */
 #define ATTN_EUNSUPPORTED (-2)

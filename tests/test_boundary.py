@@ -132,6 +132,11 @@ def test_too_large_for_32bit_offsets():
     assert rc == la.ATTN_EINVAL and "32-bit" in msg
     rc, msg = call("attn_forward_materialized", 4, 1, 1 << 16, 64, 4, 1)
     assert rc == la.ATTN_EINVAL and "T*T" in msg
+    # T*3C fits in 31 bits, but one 64-row tile of fp32 rows does not fit 32-bit byte offsets
+    C = 64 * 98304
+    for name, nptr in [("attn_forward", 3), ("attn_backward_bf16", 5)]:
+        rc, msg = call(name, nptr, 1, 1, C, C // 64, 1)
+        assert rc == la.ATTN_EINVAL and "buffer offset" in msg
 
 
 def test_forced_workspace_failure():

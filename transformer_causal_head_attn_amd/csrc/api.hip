@@ -59,6 +59,10 @@ int check_args(int B, int T, int C, int NH, int causal, const Span* outs, int no
     if ((long long)T * 3 * C >= (1LL << 31))
         return fail(ATTN_EINVAL, "T*3C = %lld exceeds the 32-bit in-batch offset range",
                     (long long)T * 3 * C);
+    // the kernels' buffer loads address one 64-row tile of fp32 rows (3C
+    // floats apart) with 32-bit byte offsets
+    if ((long long)64 * 3 * C * 4 >= (1LL << 32))
+        return fail(ATTN_EINVAL, "C=%d too large: a 64-row tile of (B,T,3C) rows exceeds the 32-bit buffer offset range", C);
     if (mat && (long long)T * T >= (1LL << 31))
         return fail(ATTN_EINVAL, "T*T = %lld exceeds the 32-bit offset range", (long long)T * T);
     if ((long long)B * NH * (long long)((T + 63) / 64) >= (1LL << 31))
