@@ -87,6 +87,21 @@ def test_vit_workload_sampled_heads(la, oracle_mod):
     _sampled_heads(la, oracle_mod, w, [(0, 0), (17, 3), (64, 11), (127, 5), (127, 11)])
 
 
+def test_partial_deal_round(la, oracle_mod):
+    """B*NH = 80 heads of 8 causal 128-row tiles: 640 unpaired workgroups, so
+    the snake deal reverses the second resident round and leaves the third
+    partial; every head is checked against the oracle."""
+    B, T, C, NH = 8, 1024, 640, 10
+    _case(f"bf16 B{B} T{T} C{C} NH{NH} causal, all heads")
+    qkv, dout = make_inputs(B, T, C, "bf16", seed=910)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, NH, True)
+    ro, rl = oracle_mod.forward(qkv, NH, True)
+    rd = oracle_mod.backward(qkv, dout, NH, True)
+    assert_close(out, ro, "bf16", "out")
+    assert_close(lse, rl, "bf16", "lse")
+    assert_close(dqkv, rd, "bf16", "dqkv")
+
+
 def test_long_context_sampled_heads(la, oracle_mod):
     w = WORKLOADS[5]
     _case(f"bf16 workload 5, sampled heads: {w.label()}")
