@@ -28,6 +28,16 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kThreads = 256;
+
+// A pointer the whole wave shares, read from lane 0 so that a buffer
+// descriptor built from it stays in scalar registers.
+template <typename P>
+__device__ __forceinline__ P* wave_uniform(P* p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 // apply_kernel: 16-row output blocks per wave, and output rows per workgroup
 // (the launchers size the grid with the same constant)
 constexpr int kApplyRB = 1;
@@ -50,7 +60,13 @@ struct Lane {
 // per 64-row strip of M: each wave keeps 16 rows of X in registers and the
 // workgroup walks the column tiles, staging Y through LDS with the next
 // tile's registers loaded while the current one is used.
-template <int HS>
+// VEC (T % 4 == 0): Y loads and M stores are raw buffer operations whose
+// descriptors end at row T (loads past it return zeros, stores past it are
+// dropped), and a store whose columns lie past T gets an offset past the
+// descriptor's end, so no load or store is predicated.  That lets the wait
+// for the next tile's loads leave this step's M stores in flight: with
+// predicated stores the compiler waited for all of them every step.
+template <int HS, bool VEC>
 __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
                                                           const float* __restrict__ X,
                                                           const float* __restrict__ Y, int T,
@@ -69,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
     const float* xb = X + (size_t)b * batch_x + (size_t)h * HS;
     const float* yb = Y + (size_t)b * batch_y + (size_t)h * HS;
 
-    const int t = rt * kTile + 16 * L.w + L.r16;
+    const int t0 = rt * kTile + 16 * L.w;   // this wave's first row
+    const int t = t0 + L.r16;
     float xr[KS];
 #pragma unroll
     for (int c = 0; c < KS / 4; ++c) {
@@ -81,18 +98,61 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
         xr[4 * c + 3] = v.w;
     }
     float4 ry[NY];
+    const uint32_t ldyb = (uint32_t)(ldy * 4);
     auto fetch = [&](int ct) {
+        if constexpr (VEC) {
+            const int valid = min(T - ct * kTile, kTile);
+            const uint32_t num = __builtin_amdgcn_readfirstlane((uint32_t)(valid - 1) * ldyb + HS * 4u);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                wave_uniform(const_cast<float*>(yb + (size_t)ct * kTile * ldy)), (short)0, (int)num,
+                0x00020000);
 #pragma unroll
-        for (int k = 0; k < NY; ++k) {
-            const int e = L.tid + k * kThreads;
-            const int j = ct * kTile + e / C4;
-            ry[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < T) ry[k] = *reinterpret_cast<const float4*>(yb + (size_t)j * ldy + 4 * (e % C4));
+            for (int k = 0; k < NY; ++k) {
+                const int e = L.tid + k * kThreads;
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (int)((uint32_t)(e / C4) * ldyb + 16u * (uint32_t)(e % C4)), 0, 0);
+                __builtin_memcpy(&ry[k], &x, 16);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NY; ++k) {
+                const int e = L.tid + k * kThreads;
+                const int j = ct * kTile + e / C4;
+                ry[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (j < T) ry[k] = *reinterpret_cast<const float4*>(yb + (size_t)j * ldy + 4 * (e % C4));
+            }
         }
     };
     float* mrow = M + ((size_t)bh * T + t) * T;
-    const bool vec = (T % 4) == 0;
+    // VEC: this wave's 16 rows of M (fewer below T; none past it)
+    const int wrows = __builtin_amdgcn_readfirstlane(max(0, min(16, T - t0)));
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        wave_uniform(M + ((size_t)bh * T + (size_t)min(t0, T)) * T), (short)0,
+        (int)__builtin_amdgcn_readfirstlane((uint32_t)wrows * (uint32_t)T * 4u), 0x00020000);
+    // acc[n][i] = M[t][ct*64 + 16n + 4g + i]
+    auto store_m = [&](int ct, const f32x4 (&acc)[kTile / 16]) {
+#pragma unroll
+        for (int n = 0; n < kTile / 16; ++n) {
+            const int j0 = ct * kTile + 16 * n + 4 * L.g;
+            if constexpr (VEC) {
+                // columns j0..j0+3 lie wholly below T or wholly past it (T % 4 == 0)
+                const uint32_t off = j0 < T ? ((uint32_t)L.r16 * (uint32_t)T + (uint32_t)j0) * 4u : 0xFFFFFFF0u;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, acc[n]), rm, (int)off, 0,
+                    0);
+            } else if (t < T) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (j0 + i < T) mrow[j0 + i] = acc[n][i];
+            }
+        }
+    };
+    // A tile's M columns are stored during the next step, right after that
+    // step's loads are issued: the wait for a tile's loads also waits for
+    // every store issued before it, so the stores get a whole step to land.
+    f32x4 prev[kTile / 16];
     fetch(0);
+    wait_global_loads();
     for (int ct = 0; ct < nt; ++ct) {
         __syncthreads();
 #pragma unroll
@@ -102,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
         }
         __syncthreads();
         if (ct + 1 < nt) fetch(ct + 1);
+        if (ct > 0) store_m(ct - 1, prev);
 #pragma unroll
         for (int n = 0; n < kTile / 16; ++n) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -114,19 +175,10 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(float* __restrict__ M,
                 acc = mfma_f32(yy.z, xr[4 * c + 2], acc);
                 acc = mfma_f32(yy.w, xr[4 * c + 3], acc);
             }
-            // acc[i] = M[t][ct*64 + 16n + 4g + i]
-            const int j0 = ct * kTile + 16 * n + 4 * L.g;
-            if (t < T) {
-                if (vec && j0 + 3 < T) {
-                    *reinterpret_cast<float4*>(mrow + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (j0 + i < T) mrow[j0 + i] = acc[i];
-                }
-            }
+            prev[n] = acc;
         }
     }
+    store_m(nt - 1, prev);
 }
 
 // ------------------------------------------ C = op(A) Bm per head (T x hs)
@@ -519,8 +571,12 @@ hipError_t fwd_hs(float* out, float* preatt, float* att, const float* qkv, const
     const size_t C3 = 3 * (size_t)s.C;
     const size_t bstride = (size_t)s.T * C3;
     const long long BH = (long long)s.B * s.NH;
-    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
-                       preatt, qkv, qkv + s.C, s.T, s.NH, C3, C3, bstride, bstride);
+    if (s.T % 4 == 0)
+        hipLaunchKernelGGL((scores_kernel<HS, true>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
+                           preatt, qkv, qkv + s.C, s.T, s.NH, C3, C3, bstride, bstride);
+    else
+        hipLaunchKernelGGL((scores_kernel<HS, false>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0,
+                           st, preatt, qkv, qkv + s.C, s.T, s.NH, C3, C3, bstride, bstride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = BH * s.T;
@@ -543,8 +599,12 @@ hipError_t bwd_hs(float* dqkv, float* dpreatt, float* datt, const float* dout, c
     const size_t bq = (size_t)s.T * C3, bo = (size_t)s.T * C;
     const long long BH = (long long)s.B * s.NH;
     // datt = dO V^T
-    hipLaunchKernelGGL(scores_kernel<HS>, dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
-                       datt, dout, qkv + 2 * C, s.T, s.NH, C, C3, bo, bq);
+    if (s.T % 4 == 0)
+        hipLaunchKernelGGL((scores_kernel<HS, true>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0, st,
+                           datt, dout, qkv + 2 * C, s.T, s.NH, C, C3, bo, bq);
+    else
+        hipLaunchKernelGGL((scores_kernel<HS, false>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0,
+                           st, datt, dout, qkv + 2 * C, s.T, s.NH, C, C3, bo, bq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = BH * s.T;
