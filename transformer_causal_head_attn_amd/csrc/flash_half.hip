@@ -239,28 +239,27 @@ struct TileRegs {
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Causal tiles carry unequal work (tile i of a Q-tile kernel sees i+1 key
-// tiles, tile j of a K/V-tile kernel nt-j query tiles), so when the grid is
-// large enough one workgroup runs tiles i and nt-1-i back to back: every
-// workgroup then does nt+1 units and the grid has no tail.  Pairing halves
-// the grid, so it is used only while at least two paired workgroups per CU
-// remain (pair_tiles on the host).  Otherwise tiles run one per workgroup,
-// heaviest first (the longest-first order of kernel 8 in llm.c's
+// tiles, tile j of a K/V-tile kernel nt-j query tiles).  Tiles run one per
+// workgroup, heaviest first (the longest-first order of kernel 8 in llm.c's
 // attention_backward.cu), dealt to the CUs like a snake draft: workgroups
 // that are resident together (ids c, c + ncu, c + 2 ncu, ... share a CU when
 // the whole round fits) take the sorted list in alternating directions, so
 // a CU that got one of the heaviest tiles in the first round gets one of the
 // lightest of the second.  The reversal keeps id % 8, the XCD a workgroup
 // is dispatched to, and a wrong guess about placement only costs balance.
-// Consecutive workgroup ids walk the heads, so all tiles of a head land on
-// one XCD (one L2) whenever B*NH is a multiple of 8.
+// Workgroups beyond the resident rounds take the lighter tiles as slots
+// free.  (Running tiles i and nt-1-i back to back in one workgroup, which
+// equalises the work, measured no better on the GPT-2 layer and 2% slower
+// at long context.)  Consecutive workgroup ids walk the heads, so all tiles
+// of a head land on one XCD (one L2) whenever B*NH is a multiple of 8.
 struct Deal {
     int ncu;      // compute units (a multiple of 8 for the snake)
     int rounds;   // workgroups per CU resident at once
 };
-__device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool heavy_high,
-                                              Deal deal, int& bh, int& ta, int& tb) {
+__device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal deal, int& bh,
+                                          int& tile) {
     int idx = blockIdx.x;
-    if (!paired && (deal.ncu & 7) == 0) {
+    if ((deal.ncu & 7) == 0) {
         const int r = idx / deal.ncu;
         if ((r & 1) && r < deal.rounds && (r + 1) * deal.ncu <= (int)gridDim.x) {
             const int c = idx - r * deal.ncu;
@@ -269,17 +268,8 @@ __device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool 
     }
     const int rank = idx / BH;
     bh = idx - rank * BH;
-    if (paired) {
-        ta = rank;
-        tb = nt - 1 - rank;
-        if (tb == ta) tb = -1;
-    } else {
-        ta = heavy_high ? nt - 1 - rank : rank;
-        tb = -1;
-    }
+    tile = heavy_high ? nt - 1 - rank : rank;
 }
-
-__host__ __device__ inline int grid_tiles(int nt, bool paired) { return paired ? (nt + 1) / 2 : nt; }
 
 // ------------------------------------------------------------------ forward
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
@@ -787,22 +777,17 @@ __device__ __forceinline__ void bwd_dq_half_tile(
 // 16-row blocks per wave in the forward and dQ kernels (measured on the
 // GPT-2, ViT and long-context shapes: 2 beats 1 and 4)
 // ------------------------------------------------------------- kernels
-// Each runs its tile function on one tile, or on a balanced pair of causal
-// tiles (see pair_of_block).
+// Each runs its tile function on the tile deal_tile gives it.
 template <typename E, int HS, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void fwd_half_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
-                                                            float scale_log2, int paired, Deal deal) {
+                                                            float scale_log2, Deal deal) {
     const int nt = (T + 64 * QB - 1) / (64 * QB);
-    int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
-    fwd_half_tile<E, HS, QB>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
-    if (tb >= 0) {
-        __syncthreads();
-        fwd_half_tile<E, HS, QB>(tb, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
-    }
+    int bh, t;
+    deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
+    fwd_half_tile<E, HS, QB>(t, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
 }
 
 template <typename E, int HS, int KB>
@@ -810,15 +795,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
-    float scale_log2, int paired, Deal deal) {
+    float scale_log2, Deal deal) {
     const int nt = (T + 64 * KB - 1) / (64 * KB);
-    int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, deal, bh, ta, tb);
-    bwd_dkdv_half_tile<E, HS, KB>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
-    if (tb >= 0) {
-        __syncthreads();
-        bwd_dkdv_half_tile<E, HS, KB>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
-    }
+    int bh, t;
+    deal_tile(gridDim.x / nt, nt, false, deal, bh, t);
+    bwd_dkdv_half_tile<E, HS, KB>(t, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
 }
 
 template <typename E, int HS, int QB>
@@ -826,15 +807,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
     uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
-    float scale_log2, int paired, Deal deal) {
+    float scale_log2, Deal deal) {
     const int nt = (T + 64 * QB - 1) / (64 * QB);
-    int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
-    bwd_dq_half_tile<E, HS, QB>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
-    if (tb >= 0) {
-        __syncthreads();
-        bwd_dq_half_tile<E, HS, QB>(tb, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
-    }
+    int bh, t;
+    deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
+    bwd_dq_half_tile<E, HS, QB>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
 }
 
 // CUs and resident workgroups per CU for a kernel (one occupancy query per
@@ -863,12 +840,11 @@ hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Sha
                        hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nqt = (s.T + BM - 1) / BM;
-    const bool paired = pair_tiles(nqt, s.causal, (long long)s.B * s.NH);
-    const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
+    const unsigned grid = (unsigned)(nqt * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
     const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>();
     hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
-                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)paired, deal);
+                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, deal);
     return hipGetLastError();
 }
 
@@ -889,13 +865,12 @@ hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qk
     constexpr int KB = kb_for(HS);
     constexpr int BN = 64 * KB;
     const int nt = (s.T + BN - 1) / BN;
-    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
-    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
+    const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB>>();
     hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
-                       (int)paired, deal);
+                       deal);
     return hipGetLastError();
 }
 
@@ -904,13 +879,12 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
                       const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
     constexpr int BM = 64 * kQB;
     const int nt = (s.T + BM - 1) / BM;
-    const bool paired = pair_tiles(nt, s.causal, (long long)s.B * s.NH);
-    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
+    const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB>>();
     hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
-                       (int)paired, deal);
+                       deal);
     return hipGetLastError();
 }
 
