@@ -96,8 +96,9 @@ inline int device_cu_count() {
     return cached[dev];
 }
 
-// Whether causal tiles should run in balanced pairs (one light, one heavy per
-// workgroup): only while the paired grid keeps >= 2 workgroups per CU.
+// Whether the fp32 dQ kernel's causal tiles should run in balanced pairs (one
+// light, one heavy per workgroup): only while the paired grid keeps >= 2
+// workgroups per CU.  The other kernels run one tile per workgroup.
 inline bool pair_tiles(int ntiles, int causal, long long BH) {
     return causal && ntiles > 1 && BH * ((ntiles + 1) / 2) >= 2LL * device_cu_count();
 }
