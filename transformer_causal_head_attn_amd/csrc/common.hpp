@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 // Problem description handed from the C ABI to the launchers.
@@ -81,19 +83,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; host threads
+// may race to fill an entry, all with the same value).  A failed query is
+// cleared and reads as 256.
 inline int device_cu_count() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64];   // 0: not queried yet
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev] = n;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
     }
-    return cached[dev];
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Whether the fp32 dQ kernel's causal tiles should run in balanced pairs (one

@@ -815,19 +815,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
 }
 
 // CUs and resident workgroups per CU for a kernel (one occupancy query per
-// kernel, repeated when the current device changes).
+// kernel and device, cached; host threads may race to fill an entry, all
+// with the same value).  A failed query is cleared and treated as one round.
 template <auto Kernel>
 Deal deal_for() {
-    static int cached_dev = -1, cached_rounds = 1;
+    static std::atomic<int> cached[64];   // 0: not queried yet
     int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (dev != cached_dev) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
-        cached_rounds = n;
-        cached_dev = dev;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return Deal{device_cu_count(), 1};
     }
-    return Deal{device_cu_count(), cached_rounds};
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) {
+            (void)hipGetLastError();
+            n = 1;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return Deal{device_cu_count(), n};
 }
 
 constexpr int kQB = 2;
