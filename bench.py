@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention path on one MI355X.
 
-One step = one forward (attn_forward) plus one backward (dQ kernel, which
-also forms D = rowsum(dO*O), then dK/dV kernel) over the workload's
-synthetic batch, inputs resident in device memory.  Prints one JSON line.
+One step = one forward (attn_forward) plus one backward over the workload's
+synthetic batch, inputs resident in device memory.  The fp32 backward is the
+one attn_backward runs: the D = rowsum(dO*O) pre-pass, the dK/dV kernel that
+also stores dS, and the dQ kernel that reads it.  The 16-bit backward is the
+dQ kernel (which also forms D, recomputing S and dP) then the dK/dV kernel.
+Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16]
 
@@ -66,13 +69,24 @@ def calibrate_copy(torch, mb):
                       "launches": 3}), flush=True)
 
 
-def kernel_flops(w):
+def kernel_flops(w, dtype):
     """Algorithmic flops of each kernel for one launch: 2*hs per unmasked
     (query, key) pair per contraction it performs."""
     u = 2 * w.hs * w.pairs * w.B * w.NH
-    return {"fwd": 2 * u,       # S = Q K^T, O = P V
-            "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
-            "dq": 3 * u}        # S, dP, dQ = dS K (plus the D = dO.O row sums)
+    if dtype == "f32":
+        return {"fwd": 2 * u,       # S = Q K^T, O = P V
+                "prepass": 0,       # D = dO.O per row (HBM-bound)
+                "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q (+ dS stored)
+                "dq": u}            # dQ = dS K from the stored dS
+    return {"fwd": 2 * u,
+            "dkdv": 4 * u,
+            "dq": 3 * u}            # S, dP, dQ = dS K (plus the D = dO.O row sums)
+
+
+def ds_path(la, w):
+    """Whether attn_backward (fp32) takes the dS block store order for this
+    shape (the store fits under the library's 4 GiB cap)."""
+    return 0 < la.attn_backward_ds_bytes(w.B, w.T, w.C, w.NH, int(w.causal)) <= 4 << 30
 
 
 def source_sha(dtype):
@@ -110,9 +124,20 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     dkdv = getattr(la, "attn_backward_dkdv" + sfx)
     dq = getattr(la, "attn_backward_dq" + sfx)
     c = int(w.causal)
-    stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
-              ("dq", lambda: dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c)),
-              ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
+    if dtype == "f32":
+        if not ds_path(la, w):
+            raise SystemExit("bench.py: this shape's dS block store exceeds the fused "
+                             "backward's cap; the bench times the dS order only")
+        dS = torch.empty((la.attn_backward_ds_bytes(B, T, C, NH, c) // 4,), device="cuda")
+        stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
+                  ("prepass", lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH)),
+                  ("dkdv", lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D,
+                                                            B, T, C, NH, c)),
+                  ("dq", lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c))]
+    else:
+        stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
+                  ("dq", lambda: dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c)),
+                  ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
 
     for _ in range(warmup):
         for _, fn in stages:
@@ -261,12 +286,17 @@ def main():
     value = flops / (total_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
 
-    kf = kernel_flops(w)
+    kf = kernel_flops(w, dtype)
     kernels = {}
     for name, ms in per_kernel.items():
         rec = {"ms": round(ms, 5)}
-        rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
-        rec["frac_peak"] = round(rec["tflops"] / peak, 4)
+        if kf[name]:
+            rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
+            rec["frac_peak"] = round(rec["tflops"] / peak, 4)
+        else:   # the D pre-pass: reads out and dout, writes D
+            nb = 2 * w.B * w.T * w.C * (4 if dtype == "f32" else 2) + 4 * w.B * w.NH * w.T
+            rec["gbs"] = round(nb / (ms * 1e-3) / 1e9, 1)
+            rec["frac_hbm_peak"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
         kernels[name] = rec
     dom = max(per_kernel, key=per_kernel.get)
     achieved = kf[dom] / (per_kernel[dom] * 1e-3) / 1e12

@@ -88,9 +88,16 @@ int attn_forward(float* out, float* lse, const float* qkv,
 
 /*
  * Fused backward, fp32.  Reads dout (B,T,C), qkv, and the forward's out and
- * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  Runs a dQ kernel (which also
- * forms D = rowsum(dout*out)) and then a dK/dV kernel, both recomputing the
- * probabilities from lse.
+ * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  When the dS block store of the
+ * shape (attn_backward_ds_bytes) is at most 4 GiB it runs the D pre-pass, a
+ * dK/dV kernel that recomputes the probabilities from lse and also writes dS,
+ * and a dQ kernel that forms dq = scale * dS K from the stored blocks (the
+ * three stages attn_backward_preprocess, attn_backward_dkdv_ds and
+ * attn_backward_dq_ds below, with the dS blocks in the library workspace).
+ * Otherwise it runs a dQ kernel that recomputes S and dP itself (and also
+ * forms D = rowsum(dout*out)) and then the dK/dV kernel
+ * (attn_backward_dq, attn_backward_dkdv).  Both orders give the same result
+ * up to the rounding of fp32 sums.
  */
 int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   const float* out, const float* lse,
@@ -115,6 +122,35 @@ int attn_backward_dq(float* dqkv, float* D, const float* dout, const float* qkv,
 int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv,
                        const float* lse, const float* D,
                        int B, int T, int C, int NH, int causal);
+
+/*
+ * The dS block store stages of the fp32 backward.  dS[t,j] = att[t,j] *
+ * (datt[t,j] - D[t]) (unscaled: dpreatt = scale * dS) is the closed-form
+ * softmax gradient of softmax_autoregressive_backward_kernel7 in llm.c
+ * dev/cuda/attention_backward.cu; dq_t = scale * sum_j dS[t,j] k_j is the
+ * dq product of attention_backward_cpu there.  Storing dS once, while the
+ * dK/dV kernel has it, saves the dQ kernel two of its three fp32
+ * contractions (recomputing S and dP).
+ *   attn_backward_ds_bytes: bytes of the dS block store for this shape: one
+ *       64x64 fp32 block per (64-query tile, 64-key tile) pair the mask
+ *       keeps (the lower triangle of tiles when causal, all of them
+ *       otherwise), per head.  B*NH*ntile*(ntile+1)/2*16 KiB causal, ntile =
+ *       ceil(T/64).  Returns 0 for arguments the other calls would reject.
+ *   attn_backward_dkdv_ds: as attn_backward_dkdv (reads D from
+ *       attn_backward_preprocess), and also writes every block of dS into
+ *       dS (caller-owned device memory of attn_backward_ds_bytes bytes; its
+ *       layout is internal to libattn and only attn_backward_dq_ds reads it).
+ *   attn_backward_dq_ds: reads dS written by attn_backward_dkdv_ds for the
+ *       same shape and qkv, writes the dq third of dqkv.
+ * Neither allocates.  Errors as for the other calls (dS is checked like any
+ * tensor argument: non-null, 16-byte aligned, no overlap).
+ */
+uint64_t attn_backward_ds_bytes(int B, int T, int C, int NH, int causal);
+int attn_backward_dkdv_ds(float* dqkv, float* dS, const float* dout, const float* qkv,
+                          const float* lse, const float* D,
+                          int B, int T, int C, int NH, int causal);
+int attn_backward_dq_ds(float* dqkv, const float* dS, const float* qkv,
+                        int B, int T, int C, int NH, int causal);
 
 /*
  * Fused forward and backward with bfloat16 inputs and outputs and fp32

@@ -69,7 +69,8 @@ ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_forward_bf16", 3),
          ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
          ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6),
          ("attn_forward_f16", 3), ("attn_backward_f16", 5),
-         ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6)]
+         ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6),
+         ("attn_backward_dkdv_ds", 6), ("attn_backward_dq_ds", 3)]
 STAGE0 = [("attn_backward_preprocess", 3), ("attn_backward_preprocess_bf16", 3),
           ("attn_backward_preprocess_f16", 3)]
 
@@ -137,6 +138,35 @@ def test_too_large_for_32bit_offsets():
     for name, nptr in [("attn_forward", 3), ("attn_backward_bf16", 5)]:
         rc, msg = call(name, nptr, 1, 1, C, C // 64, 1)
         assert rc == la.ATTN_EINVAL and "buffer offset" in msg
+
+
+def test_ds_store_bytes():
+    """One 64x64 fp32 block per kept (query tile, key tile) pair and head."""
+    blk = 64 * 64 * 4
+    assert la.attn_backward_ds_bytes(8, 1024, 768, 12, 1) == 96 * (16 * 17 // 2) * blk
+    assert la.attn_backward_ds_bytes(8, 1024, 768, 12, 0) == 96 * 16 * 16 * blk
+    assert la.attn_backward_ds_bytes(1, 65, 64, 4, 1) == 4 * 3 * blk
+    assert la.attn_backward_ds_bytes(2, 1, 128, 2, 0) == 4 * blk
+    assert la.attn_backward_ds_bytes(1, 64, 66, 4, 1) == 0
+    assert la.attn_backward_ds_bytes(1, 64, 96, 4, 1) == 0   # hs = 24
+    assert la.attn_backward_ds_bytes(0, 64, 64, 4, 1) == 0
+
+
+def test_ds_store_overlaps():
+    """The dS store's whole extent is checked against the other tensors."""
+    size = la.attn_backward_ds_bytes(1, 64, 64, 4, 1)
+    # dS (argument 1) runs into D (argument 5)
+    rc, msg = call("attn_backward_dkdv_ds", 6, 1, 64, 64, 4, 1,
+                   override={5: BASE + STEP + size - 16})
+    assert rc == la.ATTN_EINVAL and "overlaps" in msg
+    # dS (argument 1) starts inside dqkv (argument 0)
+    for name, nptr in (("attn_backward_dkdv_ds", 6), ("attn_backward_dq_ds", 3)):
+        rc, msg = call(name, nptr, 1, 64, 64, 4, 1, override={1: BASE + 16})
+        assert rc == la.ATTN_EINVAL and "overlaps" in msg, (name, msg)
+    # dqkv (argument 0) ends inside dS
+    rc, msg = call("attn_backward_dq_ds", 3, 1, 64, 64, 4, 1,
+                   override={0: BASE + STEP - 64 * 192 * 4 + 16})
+    assert rc == la.ATTN_EINVAL and "overlaps" in msg
 
 
 def test_forced_workspace_failure():

@@ -148,3 +148,80 @@ def test_respects_torch_stream(la, oracle_mod):
     s.synchronize()
     ro, _ = oracle_mod.forward(qkv_c, NH, True)
     assert_close(out, ro, "f32", "out")
+
+
+def test_stages_equal_fused_backward(la):
+    """attn_backward (fp32) is the pre-pass, dK/dV with the dS block store
+    and dQ from it: the three stage calls give the same bits.  The other
+    order (dQ recomputing S and dP, writing D, then dK/dV) agrees up to fp32
+    summation order, and dK/dV from the pre-pass D gives the same dk and dv
+    bits with or without the dS store."""
+    B, T, C, NH = 2, 190, 256, 4
+    _case(f"f32 stages B{B} T{T} C{C} NH{NH}")
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=33)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    out, lse = la.forward(qkv, NH, True)
+    ref = la.backward(dout, qkv, out, lse, NH, True)
+    nan = float("nan")
+    D = torch.full((B, NH, T), nan, device="cuda")
+    dS = torch.full((la.attn_backward_ds_bytes(B, T, C, NH, 1) // 4,), nan, device="cuda")
+    g = torch.full_like(qkv, nan)
+    la.attn_backward_preprocess(D, dout, out, B, T, C, NH)
+    la.attn_backward_dkdv_ds(g, dS, dout, qkv, lse, D, B, T, C, NH, 1)
+    la.attn_backward_dq_ds(g, dS, qkv, B, T, C, NH, 1)
+    D2 = torch.full((B, NH, T), nan, device="cuda")
+    g2 = torch.full_like(qkv, nan)
+    la.attn_backward_dq(g2, D2, dout, qkv, out, lse, B, T, C, NH, 1)
+    la.attn_backward_dkdv(g2, dout, qkv, lse, D2, B, T, C, NH, 1)
+    g3 = torch.full_like(qkv, nan)
+    la.attn_backward_dkdv(g3, dout, qkv, lse, D, B, T, C, NH, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(g, ref)
+    torch.testing.assert_close(D2, D, rtol=1e-5, atol=1e-5)
+    torch.testing.assert_close(g2, ref, rtol=1e-5, atol=1e-5)
+    assert torch.equal(g3[:, :, C:], ref[:, :, C:])
+
+
+RECOMPUTE_SHAPES = [(1, 1, 64, 4), (2, 65, 128, 2), (1, 100, 96, 3), (1, 129, 512, 4),
+                    (1, 333, 256, 2)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", RECOMPUTE_SHAPES)
+def test_recompute_stages_ragged(la, oracle_mod, shape, causal):
+    """The dQ kernel that recomputes S and dP (the fused backward's path for
+    shapes whose dS block store would exceed its cap), then dK/dV, against
+    the oracle."""
+    B, T, C, NH = shape
+    _case(f"f32 recompute stages B{B} T{T} C{C} NH{NH} causal={causal}")
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=200 + T)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    c = int(causal)
+    out, lse = la.forward(qkv, NH, causal)
+    D = torch.empty((B, NH, T), device="cuda")
+    g = torch.full_like(qkv, float("nan"))
+    la.attn_backward_dq(g, D, dout, qkv, out, lse, B, T, C, NH, c)
+    la.attn_backward_dkdv(g, dout, qkv, lse, D, B, T, C, NH, c)
+    torch.cuda.synchronize()
+    assert_close(g, oracle_mod.backward(qkv_c, dout_c, NH, causal), "f32", "dqkv")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ds_stages_ragged(la, oracle_mod, causal):
+    """The dS block store stages called directly, on a ragged shape with a
+    tail tile (keys >= T in the last tile must carry dS = 0)."""
+    B, T, C, NH = 2, 161, 256, 4
+    _case(f"f32 dS stages B{B} T{T} C{C} NH{NH} causal={causal}")
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=61)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    c = int(causal)
+    out, lse = la.forward(qkv, NH, causal)
+    D = torch.empty((B, NH, T), device="cuda")
+    dS = torch.full((la.attn_backward_ds_bytes(B, T, C, NH, c) // 4,), float("nan"), device="cuda")
+    g = torch.full_like(qkv, float("nan"))
+    la.attn_backward_preprocess(D, dout, out, B, T, C, NH)
+    la.attn_backward_dkdv_ds(g, dS, dout, qkv, lse, D, B, T, C, NH, c)
+    la.attn_backward_dq_ds(g, dS, qkv, B, T, C, NH, c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dS).all()
+    assert_close(g, oracle_mod.backward(qkv_c, dout_c, NH, causal), "f32", "dqkv")

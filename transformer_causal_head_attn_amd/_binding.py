@@ -26,6 +26,7 @@ ATTN_EHIP = -3
 EXPORTS = (
     "attn_forward", "attn_backward",
     "attn_backward_preprocess", "attn_backward_dkdv", "attn_backward_dq",
+    "attn_backward_ds_bytes", "attn_backward_dkdv_ds", "attn_backward_dq_ds",
     "attn_forward_bf16", "attn_backward_bf16",
     "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
     "attn_forward_f16", "attn_backward_f16",
@@ -76,6 +77,12 @@ def load(path: str | None = None):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
             fn.restype = i
+        lib.attn_backward_ds_bytes.argtypes = [i] * 5
+        lib.attn_backward_ds_bytes.restype = ctypes.c_uint64
+        lib.attn_backward_dkdv_ds.argtypes = [vp] * 6 + [i] * 5
+        lib.attn_backward_dkdv_ds.restype = i
+        lib.attn_backward_dq_ds.argtypes = [vp] * 3 + [i] * 5
+        lib.attn_backward_dq_ds.restype = i
         for name in ("attn_merge", "attn_merge_bf16", "attn_merge_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 4 + [i] * 5
@@ -153,6 +160,27 @@ def attn_backward_dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
           _check(D, "D", f, B * NH * T), _check(dout, "dout", f, B * T * C),
           _check(qkv, "qkv", f, B * T * 3 * C), _check(out, "out", f, B * T * C),
           _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_ds_bytes(B, T, C, NH, causal) -> int:
+    """Bytes of the dS block store for this shape (0 for invalid arguments)."""
+    return int(load().attn_backward_ds_bytes(*_dims(B, T, C, NH, causal)))
+
+
+def attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    nds = attn_backward_ds_bytes(B, T, C, NH, causal) // 4
+    _call("attn_backward_dkdv_ds", _check(dqkv, "dqkv", f, B * T * 3 * C), _check(dS, "dS", f, nds),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    nds = attn_backward_ds_bytes(B, T, C, NH, causal) // 4
+    _call("attn_backward_dq_ds", _check(dqkv, "dqkv", f, B * T * 3 * C), _check(dS, "dS", f, nds),
+          _check(qkv, "qkv", f, B * T * 3 * C), *_dims(B, T, C, NH, causal))
 
 
 def attn_forward_bf16(out, lse, qkv, B, T, C, NH, causal) -> None:

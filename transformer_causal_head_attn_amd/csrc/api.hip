@@ -138,6 +138,10 @@ int workspace(size_t bytes, float** out) {
 
 size_t nbytes(long long elems, size_t elem) { return (size_t)elems * elem; }
 
+// Largest dS block store the fused fp32 backward keeps in the workspace;
+// larger shapes run the dQ kernel that recomputes S and dP instead.
+constexpr size_t kMaxDsStoreBytes = (size_t)4 << 30;
+
 }  // namespace
 
 extern "C" {
@@ -183,13 +187,70 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
                         {lse, nbytes(BT * NH, 4), "lse"}};
     int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
     if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const size_t dbytes = (nbytes(BT * NH, 4) + 255) & ~(size_t)255;
+    const size_t dsbytes = attn::ds_store_floats(s) * 4;
     float* D = nullptr;
+    if (dsbytes <= kMaxDsStoreBytes) {
+        // D pre-pass, dK/dV writing dS, dQ from dS
+        rc = workspace(dbytes + dsbytes, &D);
+        if (rc) return rc;
+        float* dS = D + dbytes / 4;
+        hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
+        if (e == hipSuccess) e = attn::launch_dkdv_ds_f32(dqkv, dS, dout, qkv, lse, D, s, g_stream);
+        if (e == hipSuccess) e = attn::launch_dq_ds_f32(dqkv, dS, qkv, s, g_stream);
+        return launched(e, "attn_backward launch");
+    }
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
-    const attn::Shape s = shape_of(B, T, C, NH, causal);
     hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward launch");
+}
+
+uint64_t attn_backward_ds_bytes(int B, int T, int C, int NH, int causal) {
+    // the same checks as the calls that use the store, on placeholder pointers
+    static const float dummy[4] __attribute__((aligned(16))) = {};
+    const Span none[] = {{dummy, 0, "none"}};
+    if (check_args(B, T, C, NH, causal, none, 0, none, 0, false) != ATTN_OK) return 0;
+    ok();
+    return (uint64_t)attn::ds_store_floats(shape_of(B, T, C, NH, causal)) * 4;
+}
+
+int attn_backward_dkdv_ds(float* dqkv, float* dS, const float* dout, const float* qkv,
+                          const float* lse, const float* D, int B, int T, int C, int NH,
+                          int causal) {
+    const long long BT = (long long)B * T;
+    // dS enters the shared checks with size 0 (null and alignment); its
+    // extent is known, and checked for overlaps, once the dimensions pass
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}, {dS, 0, "dS"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 4, false);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const Span ds = {dS, attn::ds_store_floats(s) * 4, "dS"};
+    if (overlaps(ds, outs[0])) return fail(ATTN_EINVAL, "dS overlaps dqkv");
+    for (const Span& in : ins)
+        if (overlaps(ds, in)) return fail(ATTN_EINVAL, "output dS overlaps input %s", in.name);
+    return launched(attn::launch_dkdv_ds_f32(dqkv, dS, dout, qkv, lse, D, s, g_stream),
+                    "attn_backward_dkdv_ds launch");
+}
+
+int attn_backward_dq_ds(float* dqkv, const float* dS, const float* qkv, int B, int T, int C,
+                        int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dS, 0, "dS"}, {qkv, nbytes(BT * 3 * C, 4), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 2, false);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const Span ds = {dS, attn::ds_store_floats(s) * 4, "dS"};
+    if (overlaps(outs[0], ds)) return fail(ATTN_EINVAL, "output dqkv overlaps input dS");
+    return launched(attn::launch_dq_ds_f32(dqkv, dS, qkv, s, g_stream),
+                    "attn_backward_dq_ds launch");
 }
 
 int attn_backward_preprocess(float* D, const float* dout, const float* out, int B, int T, int C,

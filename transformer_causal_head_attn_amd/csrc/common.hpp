@@ -121,6 +121,12 @@ hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, con
                            const float* D, const Shape& s, hipStream_t st);
 hipError_t launch_dq_f32(float* dqkv, float* D, const float* dout, const float* qkv,
                          const float* out, const float* lse, const Shape& s, hipStream_t st);
+// dS block store variant of the fp32 backward: dK/dV also writes dS, dQ reads it
+size_t ds_store_floats(const Shape& s);
+hipError_t launch_dkdv_ds_f32(float* dqkv, float* dS, const float* dout, const float* qkv,
+                              const float* lse, const float* D, const Shape& s, hipStream_t st);
+hipError_t launch_dq_ds_f32(float* dqkv, const float* dS, const float* qkv, const Shape& s,
+                            hipStream_t st);
 // bf16 fused path (bf16 tensors as raw 16-bit patterns)
 hipError_t launch_fwd_bf16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                            hipStream_t st);

@@ -138,6 +138,24 @@ __device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool 
 
 __host__ __device__ inline int grid_tiles(int nt, bool paired) { return paired ? (nt + 1) / 2 : nt; }
 
+// dS block store.  The dK/dV kernel can write dS = P * (dP - D) (unscaled)
+// for every (64-query tile qt, 64-key tile kt) block it computes, and the dQ
+// kernel bwd_dq_ds_f32_tile then forms dQ = scale * dS K from it, instead of
+// recomputing S and dP (two of the three contractions of bwd_dq_f32_tile).
+// Blocks of one head: kt <= qt in causal mode (row-major lower triangle,
+// index qt(qt+1)/2 + kt), all nt^2 otherwise (qt*nt + kt); heads follow each
+// other.  Inside a block the 4096 values are in the dQ kernel's operand
+// order: [query/16][key/16][lane][4] with lane = query%16 + 16*((key%16)/4)
+// and the 4 consecutive keys 4*(key%16/4) .. +3 last, so each wave of the
+// dQ kernel loads its matrix-core operands with contiguous 16-byte loads.
+constexpr int kDsBlock = kTile * kTile;
+__host__ __device__ inline size_t ds_blocks_per_head(int nt, int causal) {
+    return causal ? (size_t)nt * (nt + 1) / 2 : (size_t)nt * nt;
+}
+__host__ __device__ inline size_t ds_block_floats(int qt, int kt, int nt, int causal) {
+    return (causal ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * nt + kt) * kDsBlock;
+}
+
 // ------------------------------------------------------------------ forward
 template <int HS>
 __device__ __forceinline__ void fwd_f32_tile(int tile_, int bh_, float* __restrict__ out,
@@ -309,11 +327,14 @@ __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict
 // One workgroup per (64-row K/V tile, head); loops over the Q tiles that see
 // it.  Per Q tile: S = Q K^T, P = exp(scale*S - lse), dV^T += dO^T P,
 // dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS (scale applied at the end).
-template <int HS>
+// With STORE_DS it also writes each 64x64 block of dS (unscaled) to the dS
+// block store, for the dQ kernel that consumes it (bwd_dq_ds_f32_tile).
+template <int HS, bool STORE_DS>
 __device__ __forceinline__ void bwd_dkdv_f32_tile(
-    int tile_, int bh_, float* __restrict__ dqkv, const float* __restrict__ dout,
-    const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
-    int T, int C, int NH, int causal, float scale, float scale_log2) {
+    int tile_, int bh_, float* __restrict__ dqkv, float* __restrict__ dsw,
+    const float* __restrict__ dout, const float* __restrict__ qkv, const float* __restrict__ lse,
+    const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
+    float scale_log2) {
     constexpr int LDK = HS + 4;
     constexpr int KS = HS / 4;
     constexpr int NB = kTile / 16;
@@ -363,6 +384,11 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     };
     fetch(qt0);
     wait_global_loads();
+    // dS store: this lane's entries of block (qt, kt) sit at
+    // ds_lane + ds_block_floats(qt, kt) + (n * 4 + w) * 256 + 4 * (4g + i)
+    [[maybe_unused]] const size_t ds_head = (size_t)bh * ds_blocks_per_head(nt, causal) * kDsBlock;
+    [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + (L.r16 & 3);
+    [[maybe_unused]] const bool kv_in = kvrow < T;
     for (int qt = qt0; qt < nt; ++qt) {
         __syncthreads();
         rq.template store<LDK>(Qs, L.tid);
@@ -407,6 +433,15 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 const float pv = fast_exp2(fmaf(s[i], scale_log2, -Ls[ql]));
                 p[i] = pv;
                 ds[i] = pv * (dp[i] - Dl[ql]);
+            }
+            if constexpr (STORE_DS) {
+                // entry (query 16n + 4g + i, key 16w + r16) of the block;
+                // keys past T are stored as 0 (their scores are not masked
+                // in a non-causal ragged tile)
+                float* blk = dsw + ds_head + ds_block_floats(qt, kt, nt, causal) +
+                             (size_t)((n * 4 + L.w) * 256 + ds_lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) blk[4 * (4 * L.g + i)] = kv_in ? ds[i] : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -551,6 +586,85 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
     }
 }
 
+// ------------------------------------------------- backward dQ from dS
+// One workgroup per (64-row Q tile, head); loops over the key tiles it sees
+// and forms dQ^T += K^T dS^T from the stored dS blocks (the third
+// contraction of bwd_dq_f32_tile, with S and dP not recomputed).  K tiles
+// stream through LDS; each lane loads its dS operands (4 consecutive keys of
+// its query row per 16-key block) straight from the block store, one tile
+// ahead.  Rows >= T are not stored; keys >= T carry dS = 0 and zero K rows.
+template <int HS>
+__device__ __forceinline__ void bwd_dq_ds_f32_tile(int tile_, int bh_, float* __restrict__ dqkv,
+                                                   const float* __restrict__ dsw,
+                                                   const float* __restrict__ qkv, int T, int C,
+                                                   int NH, int causal, float scale) {
+    constexpr int LDK = HS + 4;
+    constexpr int MB = HS / 16;
+    __shared__ float Ks[kTile * LDK];
+
+    const Lane L;
+    const int nt = (T + kTile - 1) / kTile;
+    const int qt = tile_, bh = bh_;
+    const int b = bh / NH, h = bh - (bh / NH) * NH;
+    const size_t C3 = 3 * (size_t)C;
+    const float* kbase = qkv + (size_t)b * T * C3 + C + (size_t)h * HS;
+    const int qrow = qt * kTile + 16 * L.w + L.r16;
+
+    // this lane's operands of block (qt, kt): row + kt * kDsBlock + n * 256
+    const float* dsrow = dsw + (size_t)bh * ds_blocks_per_head(nt, causal) * kDsBlock +
+                         ds_block_floats(qt, 0, nt, causal) + (size_t)(L.w * 1024 + 4 * L.l);
+
+    f32x4 dq[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dq[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nkt = causal ? (qt + 1) : nt;
+    TileRegs<HS> rk;
+    float4 dcur[4], dnext[4];   // dS operands of the current and the next key tile
+    auto fetch_ds = [&](int kt) {
+        const float* p = dsrow + (size_t)kt * kDsBlock;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dnext[n] = *reinterpret_cast<const float4*>(p + n * 256);
+    };
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    fetch_ds(0);
+    wait_global_loads();
+    for (int kt = 0; kt < nkt; ++kt) {
+        __syncthreads();
+        rk.template store<LDK>(Ks, L.tid);
+        // taken over before the next prefetch is issued (pinned there, so
+        // that waiting for these loads never waits for the prefetch too)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dcur[n] = dnext[n];
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            rk.fetch(kbase, C3, (kt + 1) * kTile, T, L.tid);
+            fetch_ds(kt + 1);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const float dsv[4] = {dcur[n].x, dcur[n].y, dcur[n].z, dcur[n].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // dS[qrow][key 16n + 4g + i] against K row 16n + 4g + i
+                const float* kr2 = Ks + (16 * n + 4 * L.g + i) * LDK + L.r16;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) dq[mb] = mfma_f32(kr2[16 * mb], dsv[i], dq[mb]);
+            }
+        }
+    }
+
+    if (qrow < T) {
+        float* dqrow = dqkv + ((size_t)b * T + qrow) * C3 + (size_t)h * HS;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const f32x4 a = dq[mb] * scale;
+            *reinterpret_cast<float4*>(dqrow + 16 * mb + 4 * L.g) = make_float4(a[0], a[1], a[2], a[3]);
+        }
+    }
+}
+
 // ------------------------------------------------------------- kernels
 // Each runs its tile function on one tile, or on a balanced pair of causal
 // tiles (see pair_of_block).
@@ -570,19 +684,33 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
     }
 }
 
-template <int HS>
+template <int HS, bool STORE_DS>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ Dws, int T, int C, int NH,
-    int causal, float scale, float scale_log2, int paired) {
+    float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
+    const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
+    int T, int C, int NH, int causal, float scale, float scale_log2, int paired) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
     pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
-    bwd_dkdv_f32_tile<HS>(ta, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    bwd_dkdv_f32_tile<HS, STORE_DS>(ta, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
+                                    scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
-        bwd_dkdv_f32_tile<HS>(tb, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+        bwd_dkdv_f32_tile<HS, STORE_DS>(tb, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
+                                        scale, scale_log2);
     }
+}
+
+template <int HS>
+__global__ __launch_bounds__(kThreads) void bwd_dq_ds_f32_kernel(float* __restrict__ dqkv,
+                                                                 const float* __restrict__ dsw,
+                                                                 const float* __restrict__ qkv,
+                                                                 int T, int C, int NH, int causal,
+                                                                 float scale) {
+    const int nt = (T + kTile - 1) / kTile;
+    int bh, ta, tb;
+    pair_of_block(gridDim.x / nt, nt, false, causal != 0, bh, ta, tb);
+    bwd_dq_ds_f32_tile<HS>(ta, bh, dqkv, dsw, qkv, T, C, NH, causal, scale);
 }
 
 template <int HS>
@@ -627,8 +755,8 @@ hipError_t prepass_f32_hs(float* D, const float* dout, const float* out, const S
 }
 
 template <int HS>
-hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
-                       const float* D, const Shape& s, hipStream_t st) {
+hipError_t dkdv_f32_hs(float* dqkv, float* dsw, const float* dout, const float* qkv,
+                       const float* lse, const float* D, const Shape& s, hipStream_t st) {
     const int nt = (s.T + kTile - 1) / kTile;
     // Two workgroups fit per CU, so equal pairs left the last half round of
     // the GPT-2 layer's grid (768 pairs on 512 slots) running one per CU;
@@ -637,8 +765,26 @@ hipError_t dkdv_f32_hs(float* dqkv, const float* dout, const float* qkv, const f
     const bool paired = false;
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dout, qkv,
-                       lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e, (int)paired);
+    if (dsw)
+        hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HS, true>), dim3(grid), dim3(kThreads), 0, st, dqkv,
+                           dsw, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
+                           scale * kLog2e, (int)paired);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HS, false>), dim3(grid), dim3(kThreads), 0, st,
+                           dqkv, dsw, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
+                           scale * kLog2e, (int)paired);
+    return hipGetLastError();
+}
+
+template <int HS>
+hipError_t dq_ds_f32_hs(float* dqkv, const float* dsw, const float* qkv, const Shape& s,
+                        hipStream_t st) {
+    const int nt = (s.T + kTile - 1) / kTile;
+    // one Q tile per workgroup, heaviest first in causal mode
+    const unsigned grid = (unsigned)((long long)nt * s.B * s.NH);
+    const float scale = (float)(1.0 / sqrt((double)HS));
+    hipLaunchKernelGGL(bwd_dq_ds_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dsw, qkv,
+                       s.T, s.C, s.NH, s.causal, scale);
     return hipGetLastError();
 }
 
@@ -677,7 +823,22 @@ hipError_t launch_prepass_f32(float* D, const float* dout, const float* out, con
 
 hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
                            const float* D, const Shape& s, hipStream_t st) {
-    ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, dout, qkv, lse, D, s, st)
+    ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, nullptr, dout, qkv, lse, D, s, st)
+}
+
+hipError_t launch_dkdv_ds_f32(float* dqkv, float* dS, const float* dout, const float* qkv,
+                              const float* lse, const float* D, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, dS, dout, qkv, lse, D, s, st)
+}
+
+hipError_t launch_dq_ds_f32(float* dqkv, const float* dS, const float* qkv, const Shape& s,
+                            hipStream_t st) {
+    ATTN_DISPATCH_HS(dq_ds_f32_hs, dqkv, dS, qkv, s, st)
+}
+
+size_t ds_store_floats(const Shape& s) {
+    const int nt = (s.T + kTile - 1) / kTile;
+    return (size_t)s.B * s.NH * ds_blocks_per_head(nt, s.causal) * kDsBlock;
 }
 
 hipError_t launch_dq_f32(float* dqkv, float* D, const float* dout, const float* qkv,
