@@ -95,6 +95,33 @@ struct TileRegs {
     }
 };
 
+// 4x4 transpose over the four lanes of a quad (lanes 4c .. 4c + 3, b = lane
+// % 4): on entry lane b holds x[i] = M[i][b], on exit x[j] = M[b][j].  Two
+// exchange rounds with DPP quad permutations (lane ^ 2, then lane ^ 1), each
+// moving the half of the values the partner needs.
+__device__ __forceinline__ float quad_xchg(float v, int ctrl_xor) {
+    const int iv = __float_as_int(v);
+    const int r = ctrl_xor == 2 ? __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false)    // [2,3,0,1]
+                                : __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+    return __int_as_float(r);
+}
+__device__ __forceinline__ void quad_transpose4(float (&x)[4], int b) {
+    const bool hi = (b & 2) != 0;   // round 1: rows 0,1 <-> rows 2,3 of the other column pair
+    const float s0 = quad_xchg(hi ? x[0] : x[2], 2);
+    const float s1 = quad_xchg(hi ? x[1] : x[3], 2);
+    x[0] = hi ? s0 : x[0];
+    x[1] = hi ? s1 : x[1];
+    x[2] = hi ? x[2] : s0;
+    x[3] = hi ? x[3] : s1;
+    const bool odd = (b & 1) != 0;   // round 2: within each 2x2 block
+    const float u0 = quad_xchg(odd ? x[0] : x[1], 1);
+    const float u1 = quad_xchg(odd ? x[2] : x[3], 1);
+    x[0] = odd ? u0 : x[0];
+    x[1] = odd ? x[1] : u0;
+    x[2] = odd ? u1 : x[2];
+    x[3] = odd ? x[3] : u1;
+}
+
 // Load this lane's HS/4 contiguous values of one row (k = (HS/4)*g + s).
 template <int HS>
 __device__ __forceinline__ void load_row_part(float (&r)[HS / 4], const float* rowp, bool valid,
@@ -384,10 +411,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     };
     fetch(qt0);
     wait_global_loads();
-    // dS store: this lane's entries of block (qt, kt) sit at
-    // ds_lane + ds_block_floats(qt, kt) + (n * 4 + w) * 256 + 4 * (4g + i)
+    // dS store: after the quad transpose this lane's 4 entries of block
+    // (qt, kt) sit at ds_block_floats(qt, kt) + (n * 4 + w) * 256 + ds_lane + 16g
     [[maybe_unused]] const size_t ds_head = (size_t)bh * ds_blocks_per_head(nt, causal) * kDsBlock;
-    [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + (L.r16 & 3);
+    [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + 4 * (L.r16 & 3);
     [[maybe_unused]] const bool kv_in = kvrow < T;
     for (int qt = qt0; qt < nt; ++qt) {
         __syncthreads();
@@ -435,13 +462,19 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 ds[i] = pv * (dp[i] - Dl[ql]);
             }
             if constexpr (STORE_DS) {
-                // entry (query 16n + 4g + i, key 16w + r16) of the block;
-                // keys past T are stored as 0 (their scores are not masked
-                // in a non-causal ragged tile)
-                float* blk = dsw + ds_head + ds_block_floats(qt, kt, nt, causal) +
-                             (size_t)((n * 4 + L.w) * 256 + ds_lane);
+                // ds[i] is entry (query 16n + 4g + i, key 16w + 4a + b) of the
+                // block, a = r16 / 4, b = r16 % 4; keys past T are stored as
+                // 0 (their scores are not masked in a non-causal ragged
+                // tile).  A 4x4 transpose over the four lanes b = 0..3 of a
+                // quad gives lane b the entries (query 4g + b, keys 4a ..
+                // 4a + 3), one 16-byte store of the operand layout.
+                float x[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) blk[4 * (4 * L.g + i)] = kv_in ? ds[i] : 0.f;
+                for (int i = 0; i < 4; ++i) x[i] = kv_in ? ds[i] : 0.f;
+                quad_transpose4(x, L.r16 & 3);
+                float* blk = dsw + ds_head + ds_block_floats(qt, kt, nt, causal) +
+                             (size_t)((n * 4 + L.w) * 256 + ds_lane + 4 * (4 * L.g));
+                *reinterpret_cast<float4*>(blk) = make_float4(x[0], x[1], x[2], x[3]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
