@@ -416,6 +416,7 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     [[maybe_unused]] const size_t ds_head = (size_t)bh * ds_blocks_per_head(nt, causal) * kDsBlock;
     [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + 4 * (L.r16 & 3);
     [[maybe_unused]] const bool kv_in = kvrow < T;
+    [[maybe_unused]] const bool kv_full = (kt + 1) * kTile <= T;   // no key of the tile past T
     for (int qt = qt0; qt < nt; ++qt) {
         __syncthreads();
         rq.template store<LDK>(Qs, L.tid);
@@ -469,8 +470,13 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 // quad gives lane b the entries (query 4g + b, keys 4a ..
                 // 4a + 3), one 16-byte store of the operand layout.
                 float x[4];
+                if (kv_full) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = kv_in ? ds[i] : 0.f;
+                    for (int i = 0; i < 4; ++i) x[i] = ds[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = kv_in ? ds[i] : 0.f;
+                }
                 quad_transpose4(x, L.r16 & 3);
                 float* blk = dsw + ds_head + ds_block_floats(qt, kt, nt, causal) +
                              (size_t)((n * 4 + L.w) * 256 + ds_lane + 4 * (4 * L.g));
@@ -653,31 +659,30 @@ __device__ __forceinline__ void bwd_dq_ds_f32_tile(int tile_, int bh_, float* __
 
     const int nkt = causal ? (qt + 1) : nt;
     TileRegs<HS> rk;
-    float4 dcur[4], dnext[4];   // dS operands of the current and the next key tile
-    auto fetch_ds = [&](int kt) {
+    // two register sets for the dS operands, used in turn: copying a
+    // prefetch set into a working set costs 16 moves per tile, which do not
+    // overlap the fp32 matrix-core ops
+    float4 dA[4], dB[4];
+    auto fetch_ds = [&](float4 (&d)[4], int kt) {
         const float* p = dsrow + (size_t)kt * kDsBlock;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) dnext[n] = *reinterpret_cast<const float4*>(p + n * 256);
+        for (int n = 0; n < 4; ++n) d[n] = *reinterpret_cast<const float4*>(p + n * 256);
     };
-    rk.fetch(kbase, C3, 0, T, L.tid);
-    fetch_ds(0);
-    wait_global_loads();
-    for (int kt = 0; kt < nkt; ++kt) {
+    // one key tile: K to LDS, then the prefetch of key tile kn (K and dS,
+    // into nx; kn = kt itself on the last tile, so that no branch separates
+    // the two steps of the loop below and the compiler cannot sink the loads
+    // past the products), then the products with the dS operands in cur
+    auto step = [&](int kt, int kn, const float4 (&cur)[4], float4 (&nx)[4]) {
         __syncthreads();
         rk.template store<LDK>(Ks, L.tid);
-        // taken over before the next prefetch is issued (pinned there, so
-        // that waiting for these loads never waits for the prefetch too)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) dcur[n] = dnext[n];
-        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        if (kt + 1 < nkt) {
-            rk.fetch(kbase, C3, (kt + 1) * kTile, T, L.tid);
-            fetch_ds(kt + 1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        rk.fetch(kbase, C3, kn * kTile, T, L.tid);
+        fetch_ds(nx, kn);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-            const float dsv[4] = {dcur[n].x, dcur[n].y, dcur[n].z, dcur[n].w};
+            const float dsv[4] = {cur[n].x, cur[n].y, cur[n].z, cur[n].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // dS[qrow][key 16n + 4g + i] against K row 16n + 4g + i
@@ -686,7 +691,16 @@ __device__ __forceinline__ void bwd_dq_ds_f32_tile(int tile_, int bh_, float* __
                 for (int mb = 0; mb < MB; ++mb) dq[mb] = mfma_f32(kr2[16 * mb], dsv[i], dq[mb]);
             }
         }
+    };
+    rk.fetch(kbase, C3, 0, T, L.tid);
+    fetch_ds(dA, 0);
+    wait_global_loads();
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+        step(kt, kt + 1, dA, dB);
+        step(kt + 1, min(kt + 2, nkt - 1), dB, dA);
     }
+    if (kt < nkt) step(kt, kt, dA, dB);
 
     if (qrow < T) {
         float* dqrow = dqkv + ((size_t)b * T + qrow) * C3 + (size_t)h * HS;
