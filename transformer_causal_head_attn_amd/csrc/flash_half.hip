@@ -422,7 +422,13 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
                 rv.fetch(vbase, C3, (j + 1) * kStream, T, L.tid);
             }
             if (j > last) continue;
+            // hs = 128: the score products run at raised issue priority, so a
+            // wave entering them is not held behind the softmax of the other
+            // waves on its SIMD (long-context forward -7%; at hs = 64 +4%, so
+            // only there)
+            if constexpr (HS >= 128) __builtin_amdgcn_s_setprio(2);
             scores(Ks, sc);
+            if constexpr (HS >= 128) __builtin_amdgcn_s_setprio(0);
             consume(j, sc, Vs);
         }
     }
