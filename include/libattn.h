@@ -46,8 +46,9 @@
  * Results are deterministic: no atomics, fixed reduction order.
  *
  * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need B*NH*T floats of
- * scratch for D, attn_decode and attn_decode_bf16 room for their partial
- * results; libattn keeps one grow-only buffer per device, allocated with
+ * scratch for D, attn_backward (fp32) also the dS block store of up to 4 GiB
+ * (attn_backward_ds_bytes), attn_decode and attn_decode_bf16 room for their
+ * partial results; libattn keeps one grow-only buffer per device, allocated with
  * hipMalloc on first need, and frees it in attn_release().  Calls that use
  * it share it, so such calls on one device must not overlap in time (calls
  * on one stream never do).  With the environment variable
@@ -110,9 +111,11 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
  *       (D[t] = sum_j att[t,j] datt[t,j], the row term of the closed-form
  *       softmax gradient) and the dq third of dqkv;
  *   attn_backward_dkdv: reads that D, writes the dk and dv thirds of dqkv.
- * attn_backward runs dq then dkdv on the same stream.  attn_backward_preprocess
- * computes D alone (the same value attn_backward_dq writes), for callers that
- * run dkdv first or need D by itself.
+ * attn_backward runs dq then dkdv on the same stream for shapes whose dS
+ * block store would exceed 4 GiB (below: the dS store stages).
+ * attn_backward_preprocess computes D alone (the same value attn_backward_dq
+ * writes, up to summation order), for callers that run dkdv first or need D
+ * by itself.
  */
 int attn_backward_preprocess(float* D, const float* dout, const float* out,
                              int B, int T, int C, int NH);

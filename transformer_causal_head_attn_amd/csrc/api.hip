@@ -192,14 +192,17 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
     const size_t dsbytes = attn::ds_store_floats(s) * 4;
     float* D = nullptr;
     if (dsbytes <= kMaxDsStoreBytes) {
-        // D pre-pass, dK/dV writing dS, dQ from dS
+        // D pre-pass, dK/dV writing dS, dQ from dS; if the store cannot be
+        // allocated, the recompute order below needs only D
         rc = workspace(dbytes + dsbytes, &D);
-        if (rc) return rc;
-        float* dS = D + dbytes / 4;
-        hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
-        if (e == hipSuccess) e = attn::launch_dkdv_ds_f32(dqkv, dS, dout, qkv, lse, D, s, g_stream);
-        if (e == hipSuccess) e = attn::launch_dq_ds_f32(dqkv, dS, qkv, s, g_stream);
-        return launched(e, "attn_backward launch");
+        if (rc == ATTN_OK) {
+            float* dS = D + dbytes / 4;
+            hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
+            if (e == hipSuccess) e = attn::launch_dkdv_ds_f32(dqkv, dS, dout, qkv, lse, D, s, g_stream);
+            if (e == hipSuccess) e = attn::launch_dq_ds_f32(dqkv, dS, qkv, s, g_stream);
+            return launched(e, "attn_backward launch");
+        }
+        (void)hipGetLastError();   // a failed hipMalloc must not surface at the next launch
     }
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
