@@ -33,7 +33,12 @@
 //    land on one XCD (one L2) whenever B*NH is a multiple of 8;
 //  * the forward raises a row's running maximum only when a tile's maximum
 //    exceeds it by more than 2^kLazyMax (log2 domain), as the 16-bit forward
-//    does, and folds the scale into the exponent's FMA.
+//    does, and folds the scale into the exponent's FMA;
+//  * the fused backward runs dK/dV first and lets it store dS, so that the
+//    dQ kernel (bwd_dq_ds_f32_tile) performs one contraction instead of
+//    three: on the fp32 matrix cores recomputing S and dP costs more than
+//    writing dS once and reading it back.  bwd_dq_f32_tile (recompute, D
+//    fused) serves shapes whose dS store would be too large.
 #include "common.hpp"
 
 namespace attn {
