@@ -100,33 +100,6 @@ struct TileRegs {
     }
 };
 
-// 4x4 transpose over the four lanes of a quad (lanes 4c .. 4c + 3, b = lane
-// % 4): on entry lane b holds x[i] = M[i][b], on exit x[j] = M[b][j].  Two
-// exchange rounds with DPP quad permutations (lane ^ 2, then lane ^ 1), each
-// moving the half of the values the partner needs.
-__device__ __forceinline__ float quad_xchg(float v, int ctrl_xor) {
-    const int iv = __float_as_int(v);
-    const int r = ctrl_xor == 2 ? __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false)    // [2,3,0,1]
-                                : __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
-    return __int_as_float(r);
-}
-__device__ __forceinline__ void quad_transpose4(float (&x)[4], int b) {
-    const bool hi = (b & 2) != 0;   // round 1: rows 0,1 <-> rows 2,3 of the other column pair
-    const float s0 = quad_xchg(hi ? x[0] : x[2], 2);
-    const float s1 = quad_xchg(hi ? x[1] : x[3], 2);
-    x[0] = hi ? s0 : x[0];
-    x[1] = hi ? s1 : x[1];
-    x[2] = hi ? x[2] : s0;
-    x[3] = hi ? x[3] : s1;
-    const bool odd = (b & 1) != 0;   // round 2: within each 2x2 block
-    const float u0 = quad_xchg(odd ? x[0] : x[1], 1);
-    const float u1 = quad_xchg(odd ? x[2] : x[3], 1);
-    x[0] = odd ? u0 : x[0];
-    x[1] = odd ? x[1] : u0;
-    x[2] = odd ? u1 : x[2];
-    x[3] = odd ? x[3] : u1;
-}
-
 // Load this lane's HS/4 contiguous values of one row (k = (HS/4)*g + s).
 template <int HS>
 __device__ __forceinline__ void load_row_part(float (&r)[HS / 4], const float* rowp, bool valid,
@@ -375,6 +348,9 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     __shared__ float dOs[kTile * LDK];
     __shared__ float Ls[kTile];
     __shared__ float Dl[kTile];
+    // per-wave 16 x 16 transpose scratch for the dS store (kTrLd floats a row)
+    constexpr int kTrLd = 20, kTrWave = 16 * kTrLd;
+    __shared__ __attribute__((aligned(16))) float Tr[STORE_DS ? 4 * kTrWave : 4];
 
     const Lane L;
     const int nt = (T + kTile - 1) / kTile;
@@ -416,8 +392,8 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     };
     fetch(qt0);
     wait_global_loads();
-    // dS store: after the quad transpose this lane's 4 entries of block
-    // (qt, kt) sit at ds_block_floats(qt, kt) + (n * 4 + w) * 256 + ds_lane + 16g
+    // dS store: after the transpose this lane's 4 entries of block (qt, kt)
+    // sit at ds_block_floats(qt, kt) + (n * 4 + w) * 256 + ds_lane + 16g
     [[maybe_unused]] const size_t ds_head = (size_t)bh * ds_blocks_per_head(nt, causal) * kDsBlock;
     [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + 4 * (L.r16 & 3);
     [[maybe_unused]] const bool kv_in = kvrow < T;
@@ -471,9 +447,12 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 // ds[i] is entry (query 16n + 4g + i, key 16w + 4a + b) of the
                 // block, a = r16 / 4, b = r16 % 4; keys past T are stored as
                 // 0 (their scores are not masked in a non-causal ragged
-                // tile).  A 4x4 transpose over the four lanes b = 0..3 of a
-                // quad gives lane b the entries (query 4g + b, keys 4a ..
-                // 4a + 3), one 16-byte store of the operand layout.
+                // tile).  The wave's 16 x 16 entries pass through its LDS
+                // scratch (row = query, stride 20: conflict-free writes), so
+                // that lane (a, b, g) reads back (query 4g + b, keys 4a ..
+                // 4a + 3), one 16-byte store of the operand layout.  A wave
+                // executes its LDS operations in order; the wave barriers
+                // keep the compiler from moving them across each other.
                 float x[4];
                 if (kv_full) {
 #pragma unroll
@@ -482,10 +461,16 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) x[i] = kv_in ? ds[i] : 0.f;
                 }
-                quad_transpose4(x, L.r16 & 3);
+                float* trw = Tr + L.w * kTrWave;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) trw[(4 * L.g + i) * kTrLd + L.r16] = x[i];
+                __builtin_amdgcn_wave_barrier();
+                const float4 y = *reinterpret_cast<const float4*>(
+                    trw + (4 * L.g + (L.r16 & 3)) * kTrLd + 4 * (L.r16 >> 2));
+                __builtin_amdgcn_wave_barrier();
                 float* blk = dsw + ds_head + ds_block_floats(qt, kt, nt, causal) +
                              (size_t)((n * 4 + L.w) * 256 + ds_lane + 4 * (4 * L.g));
-                *reinterpret_cast<float4*>(blk) = make_float4(x[0], x[1], x[2], x[3]);
+                *reinterpret_cast<float4*>(blk) = y;
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
