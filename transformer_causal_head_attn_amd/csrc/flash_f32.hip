@@ -346,8 +346,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     constexpr int MB = HS / 16;
     __shared__ float Qs[kTile * LDK];
     __shared__ float dOs[kTile * LDK];
-    __shared__ float Ls[kTile];
-    __shared__ float Dl[kTile];
+    // per query row of the streamed tile: -lse*log2e and -D, the starting
+    // values of the S and dP products (so P = exp2(S) and dS = P * dP)
+    __shared__ __attribute__((aligned(16))) float Ls[kTile];
+    __shared__ __attribute__((aligned(16))) float Dl[kTile];
     // per-wave 16 x 16 transpose scratch for the dS store (kTrLd floats a row)
     constexpr int kTrLd = 20, kTrWave = 16 * kTrLd;
     __shared__ __attribute__((aligned(16))) float Tr[STORE_DS ? 4 * kTrWave : 4];
@@ -368,6 +370,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     float kreg[KS], vreg[KS];
     load_row_part<HS>(kreg, kbase + (size_t)kvrow * C3, kvrow < T, L.g);
     load_row_part<HS>(vreg, vbase + (size_t)kvrow * C3, kvrow < T, L.g);
+    // K enters only S: scaled once by scale*log2e, S comes out in the log2
+    // domain of the exponent
+#pragma unroll
+    for (int k = 0; k < KS; ++k) kreg[k] *= scale_log2;
 
     f32x4 dk[MB], dv[MB];
 #pragma unroll
@@ -404,8 +410,8 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
         rd.template store<LDK>(dOs, L.tid);
         if (L.tid < kTile) {
             const bool in = qt * kTile + L.tid < T;
-            Ls[L.tid] = in ? rl * kLog2e : INFINITY;   // +inf -> P = 0
-            Dl[L.tid] = in ? rD : 0.f;
+            Ls[L.tid] = in ? -rl * kLog2e : -INFINITY;   // -inf -> P = 0
+            Dl[L.tid] = in ? -rD : 0.f;
         }
         __syncthreads();
         if (qt + 1 < nt) fetch(qt + 1);
@@ -413,8 +419,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
 
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-            // s[i] = S[q = qt*64 + 16n + 4g + i][kvrow], dp likewise
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            // query qt*64 + 16n + 4g + i, key kvrow: s[i] = (scale*S - lse)*log2e
+            // and dp[i] = dP - D (the products start from -lse*log2e and -D)
+            f32x4 s = *reinterpret_cast<const f32x4*>(Ls + 16 * n + 4 * L.g);
+            f32x4 dp = *reinterpret_cast<const f32x4*>(Dl + 16 * n + 4 * L.g);
             const float* qr = Qs + (16 * n + L.r16) * LDK + KS * L.g;
             const float* dr = dOs + (16 * n + L.r16) * LDK + KS * L.g;
 #pragma unroll
@@ -438,10 +446,9 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
             float p[4], ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int ql = 16 * n + 4 * L.g + i;
-                const float pv = fast_exp2(fmaf(s[i], scale_log2, -Ls[ql]));
+                const float pv = fast_exp2(s[i]);
                 p[i] = pv;
-                ds[i] = pv * (dp[i] - Dl[ql]);
+                ds[i] = pv * dp[i];
             }
             if constexpr (STORE_DS) {
                 // ds[i] is entry (query 16n + 4g + i, key 16w + 4a + b) of the
@@ -549,6 +556,11 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
     f32x4 dq[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) dq[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Q enters only S: scaled by scale*log2e, and the S and dP products start
+    // from -lse*log2e and -D, so P = exp2(S) and dS = P * dP
+#pragma unroll
+    for (int k = 0; k < KS; ++k) qreg[k] *= scale_log2;
+    const f32x4 s0 = {-l2, -l2, -l2, -l2}, dp0 = {-Dq, -Dq, -Dq, -Dq};
 
     const int nkt = causal ? (qt + 1) : nt;
     TileRegs<HS> rk, rv;
@@ -568,8 +580,8 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
         const int lim = causal ? min(T, qrow + 1) : T;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-            // s[i] = S[qrow][kv = kt*64 + 16n + 4g + i], dp likewise
-            f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            // s[i] = (scale*S - lse)*log2e, dp[i] = dP - D for qrow and key kt*64 + 16n + 4g + i
+            f32x4 s = s0, dp = dp0;
             const float* kr = Ks + (16 * n + L.r16) * LDK + KS * L.g;
             const float* vr = Vs + (16 * n + L.r16) * LDK + KS * L.g;
 #pragma unroll
@@ -593,8 +605,7 @@ __device__ __forceinline__ void bwd_dq_f32_tile(
             float ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = fast_exp2(fmaf(s[i], scale_log2, -l2));
-                ds[i] = pv * (dp[i] - Dq);
+                ds[i] = fast_exp2(s[i]) * dp[i];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

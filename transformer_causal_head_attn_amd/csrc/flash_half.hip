@@ -495,7 +495,7 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
     __shared__ uint16_t Qs[kStream * G::LDR];
     __shared__ uint16_t dOs[kStream * G::LDR];
     __shared__ float Ls[kStream];
-    __shared__ float Dl[kStream];
+    __shared__ __attribute__((aligned(16))) float Dl[kStream];   // -D per query row
 
     const Lane L;
     const int kvt = tile_, bh = bh_;
@@ -552,7 +552,7 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
         if (L.tid < kStream) {
             const bool in = qt * kStream + L.tid < T;
             Ls[L.tid] = in ? rl * kLog2e : INFINITY;   // +inf -> P = 0
-            Dl[L.tid] = in ? rD : 0.f;
+            Dl[L.tid] = in ? -rD : 0.f;
         }
         __syncthreads();
         if (qt + 1 < nqt) fetch(qt + 1);
@@ -570,12 +570,15 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int n = 2 * t + u;
-                // s[kb][i], dp[kb][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16
+                // s[kb][i], dp[kb][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16;
+                // the dP products start from -D of their query rows, so they
+                // end at dP - D and dS = P * (dP - D) needs no subtraction
+                const f32x4 dneg = *reinterpret_cast<const f32x4*>(Dl + 16 * n + 4 * L.g);
                 f32x4 s[KB], dp[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dp[kb] = dneg;
                 }
 #pragma unroll
                 for (int st = 0; st < G::KSTEPS; ++st) {
@@ -598,12 +601,12 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ql = 16 * n + 4 * L.g + i;
-                    const float l2 = Ls[ql], dd = Dl[ql];
+                    const float l2 = Ls[ql];
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
                         const float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
                         p[kb][u][i] = pv;
-                        ds[kb][u][i] = pv * (dp[kb][i] - dd);
+                        ds[kb][u][i] = pv * dp[kb][i];
                     }
                 }
             }
@@ -692,11 +695,13 @@ __device__ __forceinline__ void bwd_dq_half_tile(
         Dq[qb] = group4_sum(acc);
         if (v && L.g == 0) Dws[(size_t)bh * T + q] = Dq[qb];
     }
-    f32x4 dq[QB][G::MB];
+    f32x4 dq[QB][G::MB], dneg[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+        dneg[qb] = f32x4{-Dq[qb], -Dq[qb], -Dq[qb], -Dq[qb]};
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb) dq[qb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int nkt_all = (T + kStream - 1) / kStream;
     const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
@@ -725,12 +730,14 @@ __device__ __forceinline__ void bwd_dq_half_tile(
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int n = 2 * t + u;
-                // s[qb][i], dp[qb][i] for q = r0 + 16qb + r16, kv = k0 + 16n + 4g + i
+                // s[qb][i], dp[qb][i] for q = r0 + 16qb + r16, kv = k0 + 16n + 4g + i;
+                // dP starts from -D of the lane's row (dS = P * (dP - D) then
+                // needs no subtraction)
                 f32x4 s[QB], dp[QB];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     s[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    dp[qb] = dneg[qb];
                 }
 #pragma unroll
                 for (int st = 0; st < G::KSTEPS; ++st) {
@@ -753,7 +760,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float pv = fast_exp2(fmaf(s[qb][i], scale_log2, -l2[qb]));
-                        ds[qb][u][i] = pv * (dp[qb][i] - Dq[qb]);
+                        ds[qb][u][i] = pv * dp[qb][i];
                     }
                 }
             }
