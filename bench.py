@@ -13,8 +13,11 @@ Prints one JSON line.
 value = useful fwd+bwd TFLOP/s = (4 + 10) * hs * pairs * B * NH / step time,
 pairs = T(T+1)/2 for causal (masked pairs are not counted; the backward's
 recomputation of the scores is counted, as one of its five contractions).
-Each kernel is timed with HIP events recorded on the stream it runs on
-(torch's current stream, which the binding hands to libattn).
+The step time is that of K steps of the C-ABI calls launched one by one,
+each kernel between HIP events recorded on the stream it runs on (torch's
+current stream, which the binding hands to libattn).  The same step captured
+once in a HIP graph (the stage calls allocate nothing) and replayed K times
+is reported beside it (graph_ms_per_step).
 """
 from __future__ import annotations
 
@@ -50,7 +53,8 @@ def parse_args():
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="CPU seconds the oracle baseline may spend on its sample")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the secondary measurements (other dtype)")
+                   help="skip the secondary measurements (other dtypes, the other workloads, "
+                        "materialised mode, decode)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes (3 times), "
                         "to calibrate the HBM byte counters of a profiler run")
@@ -157,8 +161,26 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     per_kernel = {}
     for i, (name, _) in enumerate(stages):
         per_kernel[name] = sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps
-    total_ms = ev[0][0].elapsed_time(ev[-1][-1]) / steps
-    return total_ms, wall * 1e3 / steps, per_kernel
+    eager_ms = ev[0][0].elapsed_time(ev[-1][-1]) / steps
+
+    # The same step captured once in a HIP graph (the stage calls allocate
+    # nothing) and replayed K times: the kernels then follow each other
+    # without host launch gaps.  The per-kernel times above stay eager.
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in stages:
+            fn()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    return eager_ms, graph_ms, wall * 1e3 / steps, per_kernel
 
 
 def run_materialized(la, torch, w, steps, warmup):
@@ -281,7 +303,7 @@ def main():
     la.load()
     w = WORKLOADS[args.workload]
     dtype = args.dtype or w.dtype
-    total_ms, wall_ms, per_kernel = run_gpu(la, torch, w, dtype, args.steps, args.warmup)
+    total_ms, graph_ms, wall_ms, per_kernel = run_gpu(la, torch, w, dtype, args.steps, args.warmup)
     flops = w.flops_fwd + w.flops_bwd
     value = flops / (total_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
@@ -315,6 +337,11 @@ def main():
         "config": {"workload": f"{w.name} {w.label()}", "B": w.B, "T": w.T, "C": w.C,
                    "NH": w.NH, "hs": w.hs, "causal": w.causal},
         "frac_mfma_peak": round(value / peak, 4),
+        "timing": "ms_per_step and kernels: the C-ABI calls launched one by one, each kernel "
+                  "between HIP events; graph_ms_per_step: K replays of the step captured in "
+                  "one HIP graph",
+        "graph_ms_per_step": round(graph_ms, 5),
+        "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3),
         "wall_ms_per_step": round(wall_ms, 5),
         "kernels": kernels,
         "roofline": roofline,
@@ -324,12 +351,34 @@ def main():
         for other in ("f32", "bf16", "f16"):
             if other == dtype:
                 continue
-            o_total, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
+            o_total, o_graph, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
             o_val = flops / (o_total * 1e-3) / 1e12
             line["same_workload_" + other] = {
                 "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
+                "graph_ms_per_step": round(o_graph, 5),
+                "graph_tflops": round(flops / (o_graph * 1e-3) / 1e12, 3),
                 "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
                 "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
+
+    if not args.no_extra:
+        # the other workloads of the parity suite, each in its own dtype (fewer
+        # warm-up steps: they only place the headline among its neighbours)
+        others = []
+        for key in sorted(WORKLOADS):
+            if key == args.workload:
+                continue
+            wo = WORKLOADS[key]
+            o_total, o_graph, _, o_kernels = run_gpu(la, torch, wo, wo.dtype, args.steps,
+                                                     min(args.warmup, 150))
+            o_flops = wo.flops_fwd + wo.flops_bwd
+            o_val = o_flops / (o_total * 1e-3) / 1e12
+            others.append({"workload": f"{wo.name} {wo.label()}", "dtype": wo.dtype,
+                           "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
+                           "graph_ms_per_step": round(o_graph, 5),
+                           "graph_tflops": round(o_flops / (o_graph * 1e-3) / 1e12, 3),
+                           "frac_mfma_peak": round(o_val / PEAK_TFLOPS[wo.dtype], 4),
+                           "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}})
+        line["other_workloads"] = others
 
     if not args.no_extra and dtype == "f32":
         line["materialized_f32"] = run_materialized(la, torch, w, min(args.steps, 10), 2)

@@ -1,0 +1,71 @@
+"""The stage entry points under HIP graph capture: a captured forward +
+backward, replayed several times with eager work and synchronisations in
+between, gives bitwise the results of the same calls made eagerly (the
+kernels are deterministic, and none of these calls allocates or clears
+memory with a memset)."""
+import sys
+
+import pytest
+import torch
+
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import transformer_causal_head_attn_amd as m
+    m.load()
+    return m
+
+
+def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
+    if dtype == "f32":
+        return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
+                lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH),
+                lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D, B, T, C, NH, c),
+                lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c)]
+    return [lambda: la.attn_forward_bf16(out, lse, qkv, B, T, C, NH, c),
+            lambda: la.attn_backward_dq_bf16(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c),
+            lambda: la.attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_graph_replays_equal_eager(la, dtype):
+    B, T, C, NH, c = 2, 150, 256, 4, 1
+    print(f"\n[case] graph replay {dtype} B{B} T{T} C{C} NH{NH}", flush=True)
+    sys.stdout.flush()
+    qkv_c, dout_c = make_inputs(B, T, C, dtype, seed=71)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = torch.empty((B, T, C), dtype=tdt, device="cuda")
+    lse = torch.empty((B, NH, T), device="cuda")
+    D = torch.empty((B, NH, T), device="cuda")
+    dqkv = torch.empty_like(qkv)
+    dS = torch.empty((max(la.attn_backward_ds_bytes(B, T, C, NH, c) // 4, 1),), device="cuda")
+    stages = _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c)
+    for fn in stages:
+        fn()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), dqkv.clone())
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in stages:
+            fn()
+    other = torch.randn_like(qkv_c).cuda()
+    for r in range(3):
+        for t in (out, lse, dqkv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone(), dqkv.clone())
+        for name, a, b in zip(("out", "lse", "dqkv"), got, ref):
+            assert torch.equal(a, b), f"replay {r}: {name} differs from the eager result"
+        # eager work between replays, on the same library state
+        o2, l2 = la.forward(other, NH, True)
+        la.backward(dout, other, o2, l2, NH, True)
+        torch.cuda.synchronize()
