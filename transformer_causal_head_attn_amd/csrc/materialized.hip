@@ -218,8 +218,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
     const Lane L;
     const int nrt = (T + BR - 1) / BR;
     const int nkt = (T + kTile - 1) / kTile;
-    const int rt = blockIdx.x % nrt;
-    const int bh = blockIdx.x / nrt;
+    // causal: heaviest row tiles first (op(A) = A: row tile rt sees rt + 1
+    // blocks; A^T: nkt - rt), heads fastest, so that the last workgroups to
+    // start are the lightest (forward 410 -> 380 us, backward 693 -> 595 us on
+    // the GPT-2 layer against row tiles in order)
+    const int nbh = gridDim.x / nrt;
+    const int rank = blockIdx.x / nbh;
+    const int bh = blockIdx.x - rank * nbh;
+    const int rt = (causal && !TRANS) ? nrt - 1 - rank : rank;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const float* Ah = A + (size_t)bh * T * T;
     const float* bb = Bm + (size_t)b * batch_b + (size_t)h * HS;
