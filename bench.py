@@ -55,6 +55,8 @@ def parse_args():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the secondary measurements (other dtypes, the other workloads, "
                         "materialised mode, decode)")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the other workloads (keep only the chosen workload's shape)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes (3 times), "
                         "to calibrate the HBM byte counters of a profiler run")
@@ -360,7 +362,7 @@ def main():
                 "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
                 "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}}
 
-    if not args.no_extra:
+    if not args.no_extra and not args.no_others:
         # the other workloads of the parity suite, each in its own dtype (fewer
         # warm-up steps: they only place the headline among its neighbours)
         others = []
