@@ -48,6 +48,7 @@ SHAPES = [
     (1, 129, 512, 4),
     (3, 200, 64, 4),
     (1, 333, 256, 2),
+    (2, 150, 64, 4),      # hs = 16 over several tiles
 ]
 
 
@@ -183,7 +184,7 @@ def test_stages_equal_fused_backward(la):
 
 
 RECOMPUTE_SHAPES = [(1, 1, 64, 4), (2, 65, 128, 2), (1, 100, 96, 3), (1, 129, 512, 4),
-                    (1, 333, 256, 2)]
+                    (1, 333, 256, 2), (2, 150, 64, 4)]
 
 
 @pytest.mark.parametrize("causal", [True, False])
