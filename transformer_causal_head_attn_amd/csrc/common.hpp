@@ -105,6 +105,53 @@ inline int device_cu_count() {
     return n;
 }
 
+// Dealing causal tiles to CUs like a snake draft.  Workgroups that are
+// resident together (ids c, c + ncu, c + 2 ncu, ... share a CU when a whole
+// round fits on the chip) take a heaviest-first list in alternating
+// directions, so a CU that got one of the heaviest tiles in one round gets
+// one of the lightest of the next.  The reversal keeps id % 8, the XCD a
+// workgroup is dispatched to, and a wrong guess about placement only costs
+// balance.  Ids past the resident rounds keep their order.
+struct Deal {
+    int ncu;      // compute units (a multiple of 8 for the snake)
+    int rounds;   // workgroups per CU resident at once (0: no snake)
+};
+__device__ __forceinline__ int snake_block(Deal deal) {
+    int idx = blockIdx.x;
+    if ((deal.ncu & 7) == 0 && deal.ncu > 0) {
+        const int r = idx / deal.ncu;
+        if ((r & 1) && r < deal.rounds && (r + 1) * deal.ncu <= (int)gridDim.x) {
+            const int c = idx - r * deal.ncu;
+            idx = r * deal.ncu + (deal.ncu - 8 - (c & ~7) + (c & 7));
+        }
+    }
+    return idx;
+}
+
+// CUs and resident workgroups per CU of `threads`-thread workgroups for a
+// kernel (one occupancy query per kernel and device, cached; host threads may
+// race to fill an entry, all with the same value).  A failed query is
+// cleared and treated as one round.
+template <auto Kernel>
+Deal deal_for(int threads) {
+    static std::atomic<int> cached[64];   // 0: not queried yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return Deal{device_cu_count(), 1};
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, threads, 0) != hipSuccess ||
+            n < 1) {
+            (void)hipGetLastError();
+            n = 1;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return Deal{device_cu_count(), n};
+}
+
 // Whether the fp32 dQ kernel's causal tiles should run in balanced pairs (one
 // light, one heavy per workgroup): only while the paired grid keeps >= 2
 // workgroups per CU.  The other kernels run one tile per workgroup.

@@ -123,12 +123,13 @@ __device__ __forceinline__ void load_row_part(float (&r)[HS / 4], const float* r
 // the grid, so it is used only while at least two paired workgroups per CU
 // remain (pair_tiles on the host).  Otherwise tiles run one per workgroup,
 // heaviest first (the longest-first order of kernel 8 in llm.c's
-// attention_backward.cu).
+// attention_backward.cu), dealt to the CUs like a snake draft (snake_block;
+// the dQ kernel that reads dS -4%, the forward -0.5% on the GPT-2 layer).
 // Consecutive workgroup ids walk the heads, so all tiles of a head land on
 // one XCD (one L2) whenever B*NH is a multiple of 8.
 __device__ __forceinline__ void pair_of_block(int BH, int nt, bool paired, bool heavy_high,
-                                              int& bh, int& ta, int& tb) {
-    const int bid = blockIdx.x;
+                                              Deal deal, int& bh, int& ta, int& tb) {
+    const int bid = paired ? (int)blockIdx.x : snake_block(deal);
     const int rank = bid / BH;
     bh = bid - rank * BH;
     if (paired) {
@@ -726,10 +727,10 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
                                                               float* __restrict__ lse,
                                                               const float* __restrict__ qkv,
                                                               int T, int C, int NH, int causal,
-                                                              float scale_log2, int paired) {
+                                                              float scale_log2, int paired, Deal deal) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
     fwd_f32_tile<HS>(ta, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
     if (tb >= 0) {
         __syncthreads();
@@ -741,10 +742,10 @@ template <int HS, bool STORE_DS>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
     const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
-    int T, int C, int NH, int causal, float scale, float scale_log2, int paired) {
+    int T, int C, int NH, int causal, float scale, float scale_log2, int paired, Deal deal) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, deal, bh, ta, tb);
     bwd_dkdv_f32_tile<HS, STORE_DS>(ta, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
                                     scale, scale_log2);
     if (tb >= 0) {
@@ -759,10 +760,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_ds_f32_kernel(float* __restri
                                                                  const float* __restrict__ dsw,
                                                                  const float* __restrict__ qkv,
                                                                  int T, int C, int NH, int causal,
-                                                                 float scale) {
+                                                                 float scale, Deal deal) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
-    pair_of_block(gridDim.x / nt, nt, false, causal != 0, bh, ta, tb);
+    pair_of_block(gridDim.x / nt, nt, false, causal != 0, deal, bh, ta, tb);
     bwd_dq_ds_f32_tile<HS>(ta, bh, dqkv, dsw, qkv, T, C, NH, causal, scale);
 }
 
@@ -770,10 +771,10 @@ template <int HS>
 __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void bwd_dq_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ Dws, const float* __restrict__ dout,
     const float* __restrict__ qkv, const float* __restrict__ out, const float* __restrict__ lse,
-    int T, int C, int NH, int causal, float scale, float scale_log2, int paired) {
+    int T, int C, int NH, int causal, float scale, float scale_log2, int paired, Deal deal) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
-    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, bh, ta, tb);
+    pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, causal != 0, deal, bh, ta, tb);
     bwd_dq_f32_tile<HS>(ta, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
@@ -792,7 +793,8 @@ hipError_t fwd_f32_hs(float* out, float* lse, const float* qkv, const Shape& s, 
     const unsigned grid = (unsigned)(grid_tiles(nqt, paired) * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
     hipLaunchKernelGGL(fwd_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, out, lse, qkv, s.T,
-                       s.C, s.NH, s.causal, scale_log2, (int)paired);
+                       s.C, s.NH, s.causal, scale_log2, (int)paired,
+                       deal_for<fwd_f32_kernel<HS>>(kThreads));
     return hipGetLastError();
 }
 
@@ -821,11 +823,13 @@ hipError_t dkdv_f32_hs(float* dqkv, float* dsw, const float* dout, const float* 
     if (dsw)
         hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HS, true>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                            dsw, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
-                           scale * kLog2e, (int)paired);
+                           scale * kLog2e, (int)paired,
+                           deal_for<bwd_dkdv_f32_kernel<HS, true>>(kThreads));
     else
         hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HS, false>), dim3(grid), dim3(kThreads), 0, st,
                            dqkv, dsw, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
-                           scale * kLog2e, (int)paired);
+                           scale * kLog2e, (int)paired,
+                           deal_for<bwd_dkdv_f32_kernel<HS, false>>(kThreads));
     return hipGetLastError();
 }
 
@@ -837,7 +841,7 @@ hipError_t dq_ds_f32_hs(float* dqkv, const float* dsw, const float* qkv, const S
     const unsigned grid = (unsigned)((long long)nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dq_ds_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, dsw, qkv,
-                       s.T, s.C, s.NH, s.causal, scale);
+                       s.T, s.C, s.NH, s.causal, scale, deal_for<bwd_dq_ds_f32_kernel<HS>>(kThreads));
     return hipGetLastError();
 }
 
@@ -849,7 +853,8 @@ hipError_t dq_f32_hs(float* dqkv, float* D, const float* dout, const float* qkv,
     const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
     hipLaunchKernelGGL(bwd_dq_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, dqkv, D, dout, qkv,
-                       out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e, (int)paired);
+                       out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e, (int)paired,
+                       deal_for<bwd_dq_f32_kernel<HS>>(kThreads));
     return hipGetLastError();
 }
 

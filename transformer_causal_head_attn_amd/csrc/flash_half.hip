@@ -252,20 +252,9 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // equalises the work, measured no better on the GPT-2 layer and 2% slower
 // at long context.)  Consecutive workgroup ids walk the heads, so all tiles
 // of a head land on one XCD (one L2) whenever B*NH is a multiple of 8.
-struct Deal {
-    int ncu;      // compute units (a multiple of 8 for the snake)
-    int rounds;   // workgroups per CU resident at once
-};
 __device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal deal, int& bh,
                                           int& tile) {
-    int idx = blockIdx.x;
-    if ((deal.ncu & 7) == 0) {
-        const int r = idx / deal.ncu;
-        if ((r & 1) && r < deal.rounds && (r + 1) * deal.ncu <= (int)gridDim.x) {
-            const int c = idx - r * deal.ncu;
-            idx = r * deal.ncu + (deal.ncu - 8 - (c & ~7) + (c & 7));
-        }
-    }
+    const int idx = snake_block(deal);
     const int rank = idx / BH;
     bh = idx - rank * BH;
     tile = heavy_high ? nt - 1 - rank : rank;
@@ -827,28 +816,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
     bwd_dq_half_tile<E, HS, QB>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
 }
 
-// CUs and resident workgroups per CU for a kernel (one occupancy query per
-// kernel and device, cached; host threads may race to fill an entry, all
-// with the same value).  A failed query is cleared and treated as one round.
-template <auto Kernel>
-Deal deal_for() {
-    static std::atomic<int> cached[64];   // 0: not queried yet
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-        (void)hipGetLastError();
-        return Deal{device_cu_count(), 1};
-    }
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kThreads, 0) != hipSuccess || n < 1) {
-            (void)hipGetLastError();
-            n = 1;
-        }
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return Deal{device_cu_count(), n};
-}
-
 constexpr int kQB = 2;
 // dK/dV: 32 K/V rows per wave for hs <= 64, 16 for hs = 128 (fewer
 // registers, more resident waves; measured faster on the long-context shape)
@@ -861,7 +828,7 @@ hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Sha
     const int nqt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nqt * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
-    const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>();
+    const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>(kThreads);
     hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
                        qkv, s.T, s.C, s.NH, s.causal, scale_log2, deal);
     return hipGetLastError();
@@ -886,7 +853,7 @@ hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qk
     const int nt = (s.T + BN - 1) / BN;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB>>();
+    const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB>>(kThreads);
     hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
                        deal);
@@ -900,7 +867,7 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
     const int nt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB>>();
+    const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB>>(kThreads);
     hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
                        D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
                        deal);
