@@ -18,6 +18,15 @@ each kernel between HIP events recorded on the stream it runs on (torch's
 current stream, which the binding hands to libattn).  The same step captured
 once in a HIP graph (the stage calls allocate nothing) and replayed K times
 is reported beside it (graph_ms_per_step).
+
+Also reported: per-step median and minimum, forward and backward apart
+(step_stats), the same with a 512 MB buffer written before every step so
+that no input sits in the last-level cache (step_stats.flushed), the
+compulsory HBM bytes and their rate (hbm), the flop rate under the
+12 * hs * pairs count that leaves out the backward's score recompute,
+the peaks recomputed from rocminfo (device_peaks), a plain copy's HBM rate
+(hbm_copy), and the CPU oracle with its forward and backward timed apart,
+also on the two small workloads with one thread.
 """
 from __future__ import annotations
 
@@ -26,6 +35,8 @@ import hashlib
 import json
 import os
 import re
+import statistics
+import subprocess
 import sys
 import time
 
@@ -57,6 +68,9 @@ def parse_args():
                         "materialised mode, decode)")
     p.add_argument("--no-others", action="store_true",
                    help="skip the other workloads (keep only the chosen workload's shape)")
+    p.add_argument("--flush-mb", type=int, default=512,
+                   help="size of the buffer written between the steps of the cache-flushed "
+                        "timing (0: skip it); the MI355X last-level cache holds 256 MB")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes (3 times), "
                         "to calibrate the HBM byte counters of a profiler run")
@@ -73,6 +87,72 @@ def calibrate_copy(torch, mb):
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
                       "launches": 3}), flush=True)
+
+
+def device_peaks():
+    """Peaks recomputed from the device: compute units x maximum engine
+    clock (rocminfo) x matrix-core flops per clock per CU (four SIMDs; a
+    v_mfma_f32_16x16x4_f32 is 2048 flops in 32 cycles, a
+    v_mfma_f32_16x16x32_bf16 16384 flops in 16 cycles).  Called before the
+    process touches the GPU; None if rocminfo is not there."""
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for blk in txt.split("Agent "):
+        if "gfx950" not in blk:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", blk)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", blk)
+        if not (cu and mhz):
+            return None
+        cus, clk = int(cu.group(1)), int(mhz.group(1))
+        return {"cus": cus, "max_clock_mhz": clk,
+                "fp32_mfma_tflops": round(cus * clk * 1e6 * 4 * 64 / 1e12, 1),
+                "bf16_mfma_tflops": round(cus * clk * 1e6 * 4 * 1024 / 1e12, 1),
+                "source": "rocminfo: compute units x max engine clock x matrix-core flops "
+                          "per clock (fp32 256, bf16/fp16 4096 per CU)"}
+    return None
+
+
+def hbm_copy(torch, mb=1024, reps=10):
+    """Achievable HBM rate: a plain device-to-device copy of mb megabytes
+    (read once, written once), averaged over reps copies."""
+    n = mb * (1 << 20) // 4
+    src = torch.empty(n, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"bytes_moved_per_copy": 2 * n * 4, "gbs": round(gbs, 1),
+            "frac_of_8000_gbs": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def compulsory_bytes(w, dtype):
+    """Compulsory HBM bytes of one forward and one backward: the forward
+    reads qkv once and writes out and lse; the backward reads qkv, out, dout
+    and lse, writes and reads D, and writes dqkv."""
+    esz = 4 if dtype == "f32" else 2
+    io = w.B * w.T * w.C * esz
+    rows = 4 * w.B * w.NH * w.T
+    return 3 * io + io + rows, 3 * io + 2 * io + rows + 2 * rows + 3 * io
+
+
+def hbm_report(w, dtype, fwd_ms, bwd_ms):
+    fb, bb = compulsory_bytes(w, dtype)
+    return {"compulsory_bytes_fwd": fb, "compulsory_bytes_bwd": bb,
+            "gbs_fwd": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
+            "gbs_bwd": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak_step": round((fb + bb) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
+                                        / PEAK_HBM_GBS, 4)}
 
 
 def kernel_flops(w, dtype):
@@ -115,7 +195,7 @@ def measured_traffic(kernel, dtype, workload_key):
     return float(fetch.group(1)) + float(write.group(1))
 
 
-def run_gpu(la, torch, w, dtype, steps, warmup):
+def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0):
     from workloads import workload_inputs
     qkv_c, dout_c = workload_inputs(w, dtype)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
@@ -164,6 +244,40 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     for i, (name, _) in enumerate(stages):
         per_kernel[name] = sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps
     eager_ms = ev[0][0].elapsed_time(ev[-1][-1]) / steps
+    step_t = [ev[k][0].elapsed_time(ev[k][-1]) for k in range(steps)]
+    fwd_t = [ev[k][0].elapsed_time(ev[k][1]) for k in range(steps)]
+    bwd_t = [ev[k][1].elapsed_time(ev[k][-1]) for k in range(steps)]
+    stats = {"step_ms_median": round(statistics.median(step_t), 5),
+             "step_ms_min": round(min(step_t), 5),
+             "fwd_ms_median": round(statistics.median(fwd_t), 5),
+             "fwd_ms_min": round(min(fwd_t), 5),
+             "bwd_ms_median": round(statistics.median(bwd_t), 5),
+             "bwd_ms_min": round(min(bwd_t), 5)}
+
+    if flush_mb:
+        # Each step preceded by a write of flush_mb megabytes (a fill kernel
+        # on the same stream), so no input is left in the last-level cache
+        # (256 MB) when the step starts; only the step is between the events.
+        buf = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for k in range(steps):
+            buf.fill_(k & 0x7F)
+            fe[k][0].record()
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                if i == 0:
+                    fe[k][1].record()
+            fe[k][2].record()
+        torch.cuda.synchronize()
+        del buf
+        stats["flushed"] = {
+            "flush_mb": flush_mb,
+            "step_ms_median": round(statistics.median(
+                [fe[k][0].elapsed_time(fe[k][2]) for k in range(steps)]), 5),
+            "fwd_ms_median": round(statistics.median(
+                [fe[k][0].elapsed_time(fe[k][1]) for k in range(steps)]), 5),
+            "bwd_ms_median": round(statistics.median(
+                [fe[k][1].elapsed_time(fe[k][2]) for k in range(steps)]), 5)}
 
     # The same step captured once in a HIP graph (the stage calls allocate
     # nothing) and replayed K times: the kernels then follow each other
@@ -182,7 +296,7 @@ def run_gpu(la, torch, w, dtype, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / steps
-    return eager_ms, graph_ms, wall * 1e3 / steps, per_kernel
+    return eager_ms, graph_ms, wall * 1e3 / steps, per_kernel, stats
 
 
 def run_materialized(la, torch, w, steps, warmup):
@@ -269,12 +383,17 @@ def cpu_baseline(w, dtype, budget_s):
     qkv, dout = workload_inputs(w, dtype)
     heads = [(b, h) for b in range(w.B) for h in range(w.NH)]
     done = 0
+    tf = tb = 0.0
     t0 = time.perf_counter()
     for b, h in heads:
         qs = oracle.head_slice(qkv, b, h, w.NH, packed=True)
         ds = oracle.head_slice(dout, b, h, w.NH, packed=False)
+        t1 = time.perf_counter()
         oracle.forward(qs, 1, w.causal)
+        t2 = time.perf_counter()
         oracle.backward(qs, ds, 1, w.causal)
+        tf += t2 - t1
+        tb += time.perf_counter() - t2
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -283,7 +402,51 @@ def cpu_baseline(w, dtype, budget_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} heads (first in (b,h) order) of the same workload, "
-                      f"fp64 forward+backward, {dt:.1f} s"}
+                      f"fp64 forward+backward, {dt:.1f} s",
+            "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+            "host": host_description(),
+            "small_configs": oracle_small_configs()}
+
+
+def host_description():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_small_configs():
+    """The oracle on the whole of the two small workloads (tiny B1 T64 C64
+    NH4 and small B4 T256 C256 NH4, fp32 inputs), forward and backward timed
+    apart, with all threads and with one."""
+    import oracle
+    from workloads import WORKLOADS, workload_inputs
+    nmax = oracle.max_threads()
+    res = []
+    try:
+        for key in (1, 2):
+            wo = WORKLOADS[key]
+            qkv, dout = workload_inputs(wo, "f32")
+            for n in (nmax, 1):
+                oracle.set_threads(n)
+                t0 = time.perf_counter()
+                oracle.forward(qkv, wo.NH, wo.causal)
+                t1 = time.perf_counter()
+                oracle.backward(qkv, dout, wo.NH, wo.causal)
+                t2 = time.perf_counter()
+                res.append({"workload": f"{wo.name} {wo.label()}", "threads": n,
+                            "fwd_ms": round((t1 - t0) * 1e3, 3),
+                            "bwd_ms": round((t2 - t1) * 1e3, 3)})
+    finally:
+        oracle.set_threads(nmax)
+    return res
 
 
 def main():
@@ -292,6 +455,7 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
+    peaks = device_peaks() if not args.calibrate_copy else None
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
@@ -305,7 +469,8 @@ def main():
     la.load()
     w = WORKLOADS[args.workload]
     dtype = args.dtype or w.dtype
-    total_ms, graph_ms, wall_ms, per_kernel = run_gpu(la, torch, w, dtype, args.steps, args.warmup)
+    total_ms, graph_ms, wall_ms, per_kernel, stats = run_gpu(la, torch, w, dtype, args.steps,
+                                                             args.warmup, args.flush_mb)
     flops = w.flops_fwd + w.flops_bwd
     value = flops / (total_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
@@ -345,18 +510,26 @@ def main():
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3),
         "wall_ms_per_step": round(wall_ms, 5),
+        "step_stats": stats,
+        "tflops_no_recompute_count": round(12 * w.hs * w.pairs * w.B * w.NH
+                                           / (total_ms * 1e-3) / 1e12, 3),
+        "hbm": hbm_report(w, dtype, stats["fwd_ms_median"], stats["bwd_ms_median"]),
         "kernels": kernels,
         "roofline": roofline,
+        "device_peaks": peaks,
     }
 
     if not args.no_extra:
         for other in ("f32", "bf16", "f16"):
             if other == dtype:
                 continue
-            o_total, o_graph, _, o_kernels = run_gpu(la, torch, w, other, args.steps, args.warmup)
+            o_total, o_graph, _, o_kernels, o_stats = run_gpu(la, torch, w, other, args.steps,
+                                                              args.warmup)
             o_val = flops / (o_total * 1e-3) / 1e12
             line["same_workload_" + other] = {
                 "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
+                "step_stats": o_stats,
+                "hbm": hbm_report(w, other, o_stats["fwd_ms_median"], o_stats["bwd_ms_median"]),
                 "graph_ms_per_step": round(o_graph, 5),
                 "graph_tflops": round(flops / (o_graph * 1e-3) / 1e12, 3),
                 "frac_mfma_peak": round(o_val / PEAK_TFLOPS[other], 4),
@@ -370,8 +543,8 @@ def main():
             if key == args.workload:
                 continue
             wo = WORKLOADS[key]
-            o_total, o_graph, _, o_kernels = run_gpu(la, torch, wo, wo.dtype, args.steps,
-                                                     min(args.warmup, 150))
+            o_total, o_graph, _, o_kernels, o_stats = run_gpu(la, torch, wo, wo.dtype,
+                                                              args.steps, min(args.warmup, 150))
             o_flops = wo.flops_fwd + wo.flops_bwd
             o_val = o_flops / (o_total * 1e-3) / 1e12
             others.append({"workload": f"{wo.name} {wo.label()}", "dtype": wo.dtype,
@@ -379,11 +552,17 @@ def main():
                            "graph_ms_per_step": round(o_graph, 5),
                            "graph_tflops": round(o_flops / (o_graph * 1e-3) / 1e12, 3),
                            "frac_mfma_peak": round(o_val / PEAK_TFLOPS[wo.dtype], 4),
+                           "step_stats": o_stats,
+                           "hbm": hbm_report(wo, wo.dtype, o_stats["fwd_ms_median"],
+                                             o_stats["bwd_ms_median"]),
                            "kernels_ms": {k: round(v, 5) for k, v in o_kernels.items()}})
         line["other_workloads"] = others
 
     if not args.no_extra and dtype == "f32":
         line["materialized_f32"] = run_materialized(la, torch, w, min(args.steps, 10), 2)
+
+    if not args.no_extra:
+        line["hbm_copy"] = hbm_copy(torch)
 
     if not args.no_extra:
         line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),
