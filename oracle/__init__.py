@@ -59,6 +59,10 @@ def _load():
             lib.oracle_backward.restype = i
             lib.oracle_forward_block.argtypes = [dp, dp, dp] + [i] * 9
             lib.oracle_forward_block.restype = i
+            lib.oracle_layernorm_forward.argtypes = [dp] * 6 + [i, i]
+            lib.oracle_layernorm_forward.restype = i
+            lib.oracle_layernorm_backward.argtypes = [dp] * 6 + [i, i]
+            lib.oracle_layernorm_backward.restype = i
             lib.oracle_set_threads.argtypes = [i]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
@@ -168,3 +172,42 @@ def head_slice(x, b: int, h: int, NH: int, packed: bool):
     C = x.shape[2]
     hs = C // NH
     return np.ascontiguousarray(x[b:b + 1, :, h * hs:(h + 1) * hs])
+
+
+def layernorm_forward(inp, weight, bias):
+    """LayerNorm of each row of inp (N, C) (oracle.c, layernorm part):
+    return (out (N, C), mean (N,), rstd (N,)), float64, eps 1e-5."""
+    x = _as_f64(inp)
+    if x.ndim != 2:
+        raise ValueError(f"inp must be (N, C), got {x.shape}")
+    N, C = x.shape
+    w, b = _as_f64(weight), _as_f64(bias)
+    if w.shape != (C,) or b.shape != (C,):
+        raise ValueError(f"weight and bias must be ({C},)")
+    out = np.empty((N, C), np.float64)
+    mean = np.empty((N,), np.float64)
+    rstd = np.empty((N,), np.float64)
+    rc = _load().oracle_layernorm_forward(_ptr(out), _ptr(mean), _ptr(rstd), _ptr(x), _ptr(w),
+                                          _ptr(b), N, C)
+    if rc != 0:
+        raise RuntimeError(f"oracle_layernorm_forward failed with status {rc}")
+    return out, mean, rstd
+
+
+def layernorm_backward(dout, inp, weight):
+    """Gradients of the LayerNorm of inp (N, C) given dout (N, C): return
+    (dinp (N, C), dweight (C,), dbias (C,)), float64."""
+    x, dy, w = _as_f64(inp), _as_f64(dout), _as_f64(weight)
+    if x.ndim != 2 or dy.shape != x.shape:
+        raise ValueError(f"inp and dout must both be (N, C), got {x.shape} and {dy.shape}")
+    N, C = x.shape
+    if w.shape != (C,):
+        raise ValueError(f"weight must be ({C},)")
+    dx = np.empty((N, C), np.float64)
+    dw = np.empty((C,), np.float64)
+    db = np.empty((C,), np.float64)
+    rc = _load().oracle_layernorm_backward(_ptr(dx), _ptr(dw), _ptr(db), _ptr(dy), _ptr(x),
+                                           _ptr(w), N, C)
+    if rc != 0:
+        raise RuntimeError(f"oracle_layernorm_backward failed with status {rc}")
+    return dx, dw, db

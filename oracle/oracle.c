@@ -323,3 +323,94 @@ int oracle_backward(double* dqkv, double* dpreatt, double* datt,
     free(pv);
     return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/* ------------------------------------------------------------ LayerNorm
+ * Layer normalisation of each row of an (N, C) matrix, the neighbour of the
+ * attention block in a GPT-2 layer.  Sources:
+ *   [P1]  "llm.c 的中文注解-20240423", section 1.8 (layernorm_forward_kernel3):
+ *         per row the mean, then the mean of squared deviations from it,
+ *         rstd = 1/sqrt(var + 1e-5), out = (x - mean) * rstd * weight + bias;
+ *         mean and rstd are kept per row.
+ *   [P3]  "LLM Systems 10 & 11: Accelerating Transformer Training and
+ *         Inference", the LayerNorm part of the reduction section: the
+ *         backward in terms of xhat = (x - mean) / sigma and the upstream
+ *         gradient, with per-channel weight and bias.
+ * The forward is the definition written out, two passes over the row
+ * (mean, then variance about it).  The backward is the textbook gradient of
+ * that definition: with g = weight * dout and xhat = (x - mean) * rstd,
+ *     dinp   = rstd * (g - mean_c(g) - xhat * mean_c(g * xhat)),
+ *     dweight[c] = sum over rows of dout * xhat,   dbias[c] = sum of dout.
+ * mean and rstd are recomputed here from inp in double precision.  All
+ * outputs are written (=).
+ */
+#define ORACLE_LN_EPS 1e-5
+
+static void ln_row_stats(const double* x, int C, double* mean, double* rstd) {
+    double s = 0.0;
+    for (int c = 0; c < C; ++c) s += x[c];
+    const double m = s / C;
+    double v = 0.0;
+    for (int c = 0; c < C; ++c) v += (x[c] - m) * (x[c] - m);
+    v /= C;
+    *mean = m;
+    *rstd = 1.0 / sqrt(v + ORACLE_LN_EPS);
+}
+
+int oracle_layernorm_forward(double* out, double* mean, double* rstd, const double* inp,
+                             const double* weight, const double* bias, int N, int C) {
+    if (N < 1 || C < 1) return ORACLE_EINVAL;
+#pragma omp parallel for
+    for (int r = 0; r < N; ++r) {
+        const double* x = inp + (size_t)r * C;
+        double m, s;
+        ln_row_stats(x, C, &m, &s);
+        double* o = out + (size_t)r * C;
+        for (int c = 0; c < C; ++c) o[c] = (x[c] - m) * s * weight[c] + bias[c];
+        if (mean) mean[r] = m;
+        if (rstd) rstd[r] = s;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_layernorm_backward(double* dinp, double* dweight, double* dbias, const double* dout,
+                              const double* inp, const double* weight, int N, int C) {
+    if (N < 1 || C < 1) return ORACLE_EINVAL;
+    double* ms = (double*)malloc(sizeof(double) * 2 * (size_t)N);
+    if (!ms) return ORACLE_ENOMEM;
+#pragma omp parallel for
+    for (int r = 0; r < N; ++r) {
+        const double* x = inp + (size_t)r * C;
+        const double* dy = dout + (size_t)r * C;
+        double m, s;
+        ln_row_stats(x, C, &m, &s);
+        ms[2 * r] = m;
+        ms[2 * r + 1] = s;
+        double gmean = 0.0, gxmean = 0.0;
+        for (int c = 0; c < C; ++c) {
+            const double g = weight[c] * dy[c];
+            gmean += g;
+            gxmean += g * (x[c] - m) * s;
+        }
+        gmean /= C;
+        gxmean /= C;
+        double* dx = dinp + (size_t)r * C;
+        for (int c = 0; c < C; ++c) {
+            const double xhat = (x[c] - m) * s;
+            dx[c] = s * (weight[c] * dy[c] - gmean - xhat * gxmean);
+        }
+    }
+    /* column sums in row order (one thread per column) */
+#pragma omp parallel for
+    for (int c = 0; c < C; ++c) {
+        double dw = 0.0, db = 0.0;
+        for (int r = 0; r < N; ++r) {
+            const double dy = dout[(size_t)r * C + c];
+            dw += dy * (inp[(size_t)r * C + c] - ms[2 * r]) * ms[2 * r + 1];
+            db += dy;
+        }
+        dweight[c] = dw;
+        dbias[c] = db;
+    }
+    free(ms);
+    return ORACLE_OK;
+}
