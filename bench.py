@@ -25,7 +25,8 @@ that no input sits in the last-level cache (step_stats.flushed), the
 compulsory HBM bytes and their rate (hbm), the flop rate under the
 12 * hs * pairs count that leaves out the backward's score recompute,
 the peaks recomputed from rocminfo (device_peaks), a plain copy's HBM rate
-(hbm_copy), and the CPU oracle with its forward and backward timed apart,
+(hbm_copy), the LayerNorm over the workload's activation rows in GB/s
+(layernorm), and the CPU oracle with its forward and backward timed apart,
 also on the two small workloads with one thread.
 """
 from __future__ import annotations
@@ -375,6 +376,51 @@ def run_decode(la, torch, w, dtype, steps, warmup):
             "bytes_note": "compulsory bytes: K and V of every head once, q row and out"}
 
 
+def run_layernorm(la, torch, N, C, dtype, steps=50, warmup=100):
+    """Time the LayerNorm forward and backward over N rows of C (the GPT-2
+    layer's activations when N = B*T = 8192, C = 768).  Both are HBM-bound:
+    the compulsory bytes are the rows read and written once (forward: inp
+    in, out out; backward: dout and inp in, dinp out), plus the per-row
+    mean and rstd and the per-column weight, bias and their gradients."""
+    from workloads import randn
+    esz = 4 if dtype == "f32" else 2
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = randn((N, C), 31).to(tdt).cuda()
+    dy = randn((N, C), 32).to(tdt).cuda()
+    wt = (1.0 + 0.5 * randn((C,), 33)).cuda()
+    bs = randn((C,), 34).cuda()
+    out, mean, rstd = la.layernorm(x, wt, bs)
+    dx = torch.empty_like(x)
+    dw = torch.empty(C, device="cuda")
+    db = torch.empty(C, device="cuda")
+    ffn = la.layernorm_forward if dtype == "f32" else la.layernorm_forward_bf16
+    bfn = la.layernorm_backward if dtype == "f32" else la.layernorm_backward_bf16
+    fwd = lambda: ffn(out, mean, rstd, x, wt, bs, N, C)
+    bwd = lambda: bfn(dx, dw, db, dy, x, wt, mean, rstd, N, C)
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(steps):
+        fwd()
+    ev[1].record()
+    for _ in range(steps):
+        bwd()
+    ev[2].record()
+    torch.cuda.synchronize()
+    tf = ev[0].elapsed_time(ev[1]) / steps
+    tb = ev[1].elapsed_time(ev[2]) / steps
+    fb = 2 * N * C * esz + 2 * C * 4 + 8 * N
+    bb = 3 * N * C * esz + 3 * C * 4 + 8 * N
+    return {"workload": f"layernorm N{N} C{C}", "dtype": dtype,
+            "fwd_us": round(tf * 1e3, 2), "bwd_us": round(tb * 1e3, 2),
+            "fwd_gbs": round(fb / (tf * 1e-3) / 1e9, 1), "bwd_gbs": round(bb / (tb * 1e-3) / 1e9, 1),
+            "bytes_note": "compulsory bytes: rows read and written once, per-row mean and rstd, "
+                          "per-column weight, bias and gradients"}
+
+
 def cpu_baseline(w, dtype, budget_s):
     """The fp64 oracle, as it stands, on the first heads of the same
     workload in (b, h) order until the CPU budget is spent."""
@@ -563,6 +609,8 @@ def main():
 
     if not args.no_extra:
         line["hbm_copy"] = hbm_copy(torch)
+        line["layernorm"] = [run_layernorm(la, torch, w.B * w.T, w.C, "f32"),
+                             run_layernorm(la, torch, w.B * w.T, w.C, "bf16")]
 
     if not args.no_extra:
         line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),

@@ -266,6 +266,51 @@ int attn_merge_bf16(uint16_t* out, float* lse, const float* o_parts, const float
 int attn_merge_f16(uint16_t* out, float* lse, const float* o_parts, const float* lse_parts,
                    int nparts, int B, int T, int C, int NH);
 
+/*
+ * LayerNorm over the rows of inp (N, C), row-major: the normalisation of
+ * "llm.c 的中文注解-20240423", section 1.8, with the single-reduction
+ * forward and backward of "LLM Systems 10 & 11: Accelerating Transformer
+ * Training and Inference", section 1.2.1.  Per row r:
+ *     mean[r] = sum_c x[r,c] / C,   var = sum_c (x[r,c] - mean[r])^2 / C,
+ *     rstd[r] = 1 / sqrt(var + 1e-5),
+ *     out[r,c] = (x[r,c] - mean[r]) * rstd[r] * weight[c] + bias[c].
+ * out and inp are (N, C); mean and rstd are (N,) fp32 (kept for the
+ * backward); weight and bias are (C,) fp32.  Every pointer is a
+ * caller-owned device pointer, 16-byte aligned; outputs may not overlap
+ * each other or an input.  N, C >= 1 (any C; rows of C % 4 == 0 use vector
+ * loads).  No workspace.  Errors: ATTN_EINVAL for a NULL or misaligned
+ * pointer, N or C < 1, or overlapping buffers; ATTN_EHIP for a launch
+ * failure.
+ */
+int layernorm_forward(float* out, float* mean, float* rstd, const float* inp, const float* weight,
+                      const float* bias, int N, int C);
+
+/* LayerNorm with bfloat16 out and inp (round to nearest even); mean, rstd,
+ * weight, bias and all arithmetic fp32. */
+int layernorm_forward_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                           const float* weight, const float* bias, int N, int C);
+
+/*
+ * Gradients of layernorm_forward, written (=):
+ *     xhat = (x - mean) * rstd,  g = weight * dout,
+ *     dinp[r,c]  = rstd[r] * (g[r,c] - sum_c g[r,:] / C - xhat[r,c] * sum_c (g * xhat)[r,:] / C),
+ *     dweight[c] = sum_r dout[r,c] * xhat[r,c],   dbias[c] = sum_r dout[r,c],
+ * with mean and rstd as layernorm_forward wrote them for the same inp.
+ * dinp, dout and inp are (N, C); dweight, dbias and weight (C,); mean and
+ * rstd (N,).  Uses the library workspace (2 * C floats per chunk of 16
+ * rows) for partial column sums, which are added in a fixed order: results
+ * are bitwise deterministic.  Errors as layernorm_forward, plus ATTN_EHIP
+ * if the workspace cannot be allocated.
+ */
+int layernorm_backward(float* dinp, float* dweight, float* dbias, const float* dout,
+                       const float* inp, const float* weight, const float* mean, const float* rstd,
+                       int N, int C);
+
+/* The backward with bfloat16 dinp, dout and inp; the rest as above. */
+int layernorm_backward_bf16(uint16_t* dinp, float* dweight, float* dbias, const uint16_t* dout,
+                            const uint16_t* inp, const float* weight, const float* mean,
+                            const float* rstd, int N, int C);
+
 /* Set the HIP stream (a hipStream_t, or NULL for the null stream) used by
  * the calling thread's subsequent calls.  Always returns ATTN_OK. */
 int attn_set_stream(void* hip_stream);

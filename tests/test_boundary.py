@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "libattn.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:attn|layernorm)_\w+)\s*\(", src)))
 
 
 def test_header_declares_the_exports():
@@ -296,3 +296,53 @@ def test_error_state_is_per_thread():
     tb.join(timeout=30)
     assert "B, T and NH" in seen["a"]
     assert seen["b"] == ""
+
+
+LN = [("layernorm_forward", 6), ("layernorm_forward_bf16", 6), ("layernorm_backward", 8),
+      ("layernorm_backward_bf16", 8)]
+
+
+@pytest.mark.parametrize("name,nptr", LN)
+def test_layernorm_arguments(name, nptr):
+    lib = la.load()
+    fn = getattr(lib, name)
+    p = ptrs(nptr)
+    assert fn(*p, 0, 768) == la.ATTN_EINVAL                # N < 1
+    assert fn(*p, 8, 0) == la.ATTN_EINVAL                  # C < 1
+    assert "N and C" in lib.attn_last_error().decode()
+    for i in range(nptr):
+        q = ptrs(nptr)
+        q[i] = ctypes.c_void_p(0)
+        assert fn(*q, 8, 768) == la.ATTN_EINVAL
+        assert "NULL" in lib.attn_last_error().decode()
+        q = ptrs(nptr)
+        q[i] = ctypes.c_void_p(BASE + i * STEP + 4)
+        assert fn(*q, 8, 768) == la.ATTN_EINVAL
+        assert "aligned" in lib.attn_last_error().decode()
+    for o in range(3):                                     # each output inside each input
+        for j in range(3, nptr):
+            q = ptrs(nptr)
+            q[o] = ctypes.c_void_p(BASE + j * STEP + 16)
+            assert fn(*q, 8, 768) == la.ATTN_EINVAL
+            assert "overlaps" in lib.attn_last_error().decode()
+    q = ptrs(nptr)
+    q[1] = ctypes.c_void_p(BASE + 16)                      # second output inside the first
+    assert fn(*q, 8, 768) == la.ATTN_EINVAL
+
+
+def test_forced_workspace_failure_layernorm_backward():
+    """The LayerNorm backward keeps partial column sums in the workspace:
+    the forced allocation failure reaches it before any HIP call."""
+    code = (
+        "import ctypes, transformer_causal_head_attn_amd as la\n"
+        "lib = la.load()\n"
+        "p = [ctypes.c_void_p((1 << 40) + i * (1 << 36)) for i in range(8)]\n"
+        "rc = lib.layernorm_backward(*p, 8, 768)\n"
+        "print(rc, lib.attn_last_error().decode())\n"
+    )
+    env = dict(os.environ, ATTN_TEST_FAIL_ALLOC="1", PYTHONPATH=ROOT)
+    res = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env,
+                         cwd=ROOT, timeout=120)
+    assert res.returncode == 0, res.stderr
+    rc, msg = res.stdout.split(" ", 1)
+    assert int(rc) == la.ATTN_EHIP and "forced" in msg

@@ -17,4 +17,6 @@ from ._binding import (  # noqa: F401
     attn_forward, attn_forward_bf16, attn_forward_materialized, attn_last_error, attn_merge,
     attn_merge_bf16, attn_merge_f16, attn_release, attn_set_stream, backward, backward_materialized, decode,
     forward, forward_materialized, load, merge,
+    layernorm, layernorm_backward, layernorm_backward_bf16, layernorm_forward,
+    layernorm_forward_bf16, layernorm_grad,
 )

@@ -562,3 +562,102 @@ int attn_merge_f16(uint16_t* out, float* lse, const float* o_parts, const float*
 }
 
 }  // extern "C"
+
+// ---- LayerNorm ----
+namespace {
+int check_ln(int N, int C, const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i)
+        if (!outs[i].p) return fail(ATTN_EINVAL, "%s is NULL", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if (!ins[i].p) return fail(ATTN_EINVAL, "%s is NULL", ins[i].name);
+    if (N < 1 || C < 1) return fail(ATTN_EINVAL, "N and C must be >= 1 (got N=%d C=%d)", N, C);
+    for (int i = 0; i < nout; ++i)
+        if ((uintptr_t)outs[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if ((uintptr_t)ins[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", ins[i].name);
+    for (int i = 0; i < nout; ++i) {
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(ATTN_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(ATTN_EINVAL, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    }
+    return ATTN_OK;
+}
+
+template <typename T>
+int ln_forward_any(T* out, float* mean, float* rstd, const T* inp, const float* weight,
+                   const float* bias, int N, int C, const char* name,
+                   hipError_t (*launch)(T*, float*, float*, const T*, const float*, const float*,
+                                        int, int, hipStream_t)) {
+    const long long NC = (long long)N * C;
+    const Span outs[] = {{out, nbytes(NC, sizeof(T)), "out"},
+                         {mean, nbytes(N, 4), "mean"},
+                         {rstd, nbytes(N, 4), "rstd"}};
+    const Span ins[] = {{inp, nbytes(NC, sizeof(T)), "inp"},
+                        {weight, nbytes(C, 4), "weight"},
+                        {bias, nbytes(C, 4), "bias"}};
+    int rc = check_ln(N, C, outs, 3, ins, 3);
+    if (rc) return rc;
+    return launched(launch(out, mean, rstd, inp, weight, bias, N, C, g_stream), name);
+}
+
+template <typename T>
+int ln_backward_any(T* dinp, float* dweight, float* dbias, const T* dout, const T* inp,
+                    const float* weight, const float* mean, const float* rstd, int N, int C,
+                    const char* name,
+                    hipError_t (*launch)(T*, float*, float*, float*, const T*, const T*,
+                                         const float*, const float*, const float*, int, int,
+                                         hipStream_t)) {
+    const long long NC = (long long)N * C;
+    const Span outs[] = {{dinp, nbytes(NC, sizeof(T)), "dinp"},
+                         {dweight, nbytes(C, 4), "dweight"},
+                         {dbias, nbytes(C, 4), "dbias"}};
+    const Span ins[] = {{dout, nbytes(NC, sizeof(T)), "dout"},
+                        {inp, nbytes(NC, sizeof(T)), "inp"},
+                        {weight, nbytes(C, 4), "weight"},
+                        {mean, nbytes(N, 4), "mean"},
+                        {rstd, nbytes(N, 4), "rstd"}};
+    int rc = check_ln(N, C, outs, 3, ins, 5);
+    if (rc) return rc;
+    float* ws = nullptr;
+    rc = workspace(attn::layernorm_workspace_floats(N, C) * 4, &ws);
+    if (rc) return rc;
+    return launched(launch(dinp, dweight, dbias, ws, dout, inp, weight, mean, rstd, N, C,
+                           g_stream),
+                    name);
+}
+}  // namespace
+
+extern "C" {
+
+int layernorm_forward(float* out, float* mean, float* rstd, const float* inp, const float* weight,
+                      const float* bias, int N, int C) {
+    return ln_forward_any<float>(out, mean, rstd, inp, weight, bias, N, C,
+                                 "layernorm_forward launch", attn::launch_layernorm_fwd_f32);
+}
+
+int layernorm_forward_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                           const float* weight, const float* bias, int N, int C) {
+    return ln_forward_any<uint16_t>(out, mean, rstd, inp, weight, bias, N, C,
+                                    "layernorm_forward_bf16 launch",
+                                    attn::launch_layernorm_fwd_bf16);
+}
+
+int layernorm_backward(float* dinp, float* dweight, float* dbias, const float* dout,
+                       const float* inp, const float* weight, const float* mean, const float* rstd,
+                       int N, int C) {
+    return ln_backward_any<float>(dinp, dweight, dbias, dout, inp, weight, mean, rstd, N, C,
+                                  "layernorm_backward launch", attn::launch_layernorm_bwd_f32);
+}
+
+int layernorm_backward_bf16(uint16_t* dinp, float* dweight, float* dbias, const uint16_t* dout,
+                            const uint16_t* inp, const float* weight, const float* mean,
+                            const float* rstd, int N, int C) {
+    return ln_backward_any<uint16_t>(dinp, dweight, dbias, dout, inp, weight, mean, rstd, N, C,
+                                     "layernorm_backward_bf16 launch",
+                                     attn::launch_layernorm_bwd_bf16);
+}
+
+}  // extern "C"

@@ -216,4 +216,23 @@ hipError_t launch_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, flo
 hipError_t launch_merge_f16(uint16_t* out, float* lse, const float* o_parts,
                             const float* lse_parts, int P, const Shape& s, hipStream_t st);
 
+// LayerNorm over the rows of an (N, C) matrix (layernorm.hip); the backward
+// uses layernorm_workspace_floats(N, C) floats of workspace
+int layernorm_col_chunks(int N, int C, int* rows_per_chunk);
+size_t layernorm_workspace_floats(int N, int C);
+hipError_t launch_layernorm_fwd_f32(float* out, float* mean, float* rstd, const float* inp,
+                                    const float* weight, const float* bias, int N, int C,
+                                    hipStream_t st);
+hipError_t launch_layernorm_fwd_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                                     const float* weight, const float* bias, int N, int C,
+                                     hipStream_t st);
+hipError_t launch_layernorm_bwd_f32(float* dinp, float* dweight, float* dbias, float* ws,
+                                    const float* dout, const float* inp, const float* weight,
+                                    const float* mean, const float* rstd, int N, int C,
+                                    hipStream_t st);
+hipError_t launch_layernorm_bwd_bf16(uint16_t* dinp, float* dweight, float* dbias, float* ws,
+                                     const uint16_t* dout, const uint16_t* inp,
+                                     const float* weight, const float* mean, const float* rstd,
+                                     int N, int C, hipStream_t st);
+
 }  // namespace attn

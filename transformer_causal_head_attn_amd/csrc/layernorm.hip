@@ -1,0 +1,364 @@
+// layernorm.hip -- LayerNorm forward and backward over the rows of an
+// (N, C) matrix for gfx950: fp32 or bfloat16 rows, fp32 weight, bias, mean,
+// rstd and arithmetic.
+//
+// Method: "llm.c 的中文注解-20240423", section 1.8 (layernorm_forward_kernel3):
+// per row the mean and rstd = 1/sqrt(var + 1e-5) of the row, kept for the
+// backward, and out = (x - mean) * rstd * weight + bias.  "LLM Systems 10 &
+// 11: Accelerating Transformer Training and Inference" (section 1.2.1,
+// LayerNorm) rewrites both directions so that each needs a single
+// reduction per row: the forward sums x and x^2 in one pass (variance =
+// mean of squares minus squared mean), the backward sums the two terms it
+// needs in one pass, storage in 16 bits with fp32 accumulation.
+//
+// Here:
+//  * one wave per row; lanes stride the row 4 elements at a time (16-byte
+//    fp32 or 8-byte bf16 loads) when C % 4 == 0, one element otherwise;
+//  * forward: one pass of sums of d = x - x[0] and d^2 (shifted data, so
+//    that the difference of the two means does not cancel when |mean| is
+//    large against the spread; the shift changes neither mean nor
+//    variance), one wave reduction, then the row again (from cache) for
+//    the output;
+//  * backward, input gradient: with g = weight * dout and
+//    xhat = (x - mean) * rstd from the forward's mean and rstd, one pass
+//    sums g and g * xhat, one wave reduction, then
+//    dinp = rstd * (g - mean(g) - xhat * mean(g * xhat));
+//  * backward, weight and bias: a thread owns four columns (one when
+//    C % 4 != 0) of a chunk of 16 rows and sums dout * xhat and dout into a
+//    workspace of partial sums; a second kernel adds the chunks in a fixed
+//    order, so the result is bitwise deterministic (no atomics).  dweight
+//    and dbias are written (=).
+#include "common.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kLnThreads = 256;   // 4 waves, one row each
+constexpr int kLnRows = kLnThreads / 64;
+constexpr float kLnEps = 1e-5f;
+constexpr int kLnColThreads = 256;
+
+struct LnF32 {
+    typedef float T;
+    static __device__ __forceinline__ float get(float v) { return v; }
+    static __device__ __forceinline__ float put(float v) { return v; }
+    static __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        v[0] = x.x;
+        v[1] = x.y;
+        v[2] = x.z;
+        v[3] = x.w;
+    }
+    static __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+struct LnBF16 {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(uint16_t v) {
+        return __uint_as_float((uint32_t)v << 16);
+    }
+    static __device__ __forceinline__ uint16_t put(float v) {   // round to nearest even
+        const __bf16 h = (__bf16)v;
+        uint16_t u;
+        __builtin_memcpy(&u, &h, 2);
+        return u;
+    }
+    static __device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        v[0] = __uint_as_float(x.x << 16);
+        v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(x.y << 16);
+        v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+        const uint2 x = make_uint2((uint32_t)put(v[0]) | ((uint32_t)put(v[1]) << 16),
+                                   (uint32_t)put(v[2]) | ((uint32_t)put(v[3]) << 16));
+        *reinterpret_cast<uint2*>(p) = x;
+    }
+};
+
+// VEC consecutive elements starting at p (VEC = 4 needs p 4-element aligned)
+template <typename E, int VEC>
+__device__ __forceinline__ void load_row(const typename E::T* p, float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        E::load4(p, v);
+    } else {
+        v[0] = E::get(*p);
+    }
+}
+template <typename E, int VEC>
+__device__ __forceinline__ void store_row(typename E::T* p, const float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        E::store4(p, v);
+    } else {
+        *p = E::put(v[0]);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(typename E::T* __restrict__ out,
+                                                            float* __restrict__ mean,
+                                                            float* __restrict__ rstd,
+                                                            const typename E::T* __restrict__ inp,
+                                                            const float* __restrict__ weight,
+                                                            const float* __restrict__ bias, int N,
+                                                            int C) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kLnRows + (threadIdx.x >> 6);
+    if (row >= N) return;   // a whole wave; the kernel has no barrier
+    const typename E::T* x = inp + (size_t)row * C;
+    const float shift = E::get(x[0]);
+    float s1 = 0.f, s2 = 0.f;
+    for (int i = lane * VEC; i < C; i += 64 * VEC) {
+        float v[VEC];
+        load_row<E, VEC>(x + i, v);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float d = v[k] - shift;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+        }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const float md = s1 / (float)C;                       // mean - shift
+    const float var = fmaxf(s2 / (float)C - md * md, 0.f);
+    const float r = 1.0f / sqrtf(var + kLnEps);
+    if (lane == 0) {
+        mean[row] = shift + md;
+        rstd[row] = r;
+    }
+    typename E::T* o = out + (size_t)row * C;
+    for (int i = lane * VEC; i < C; i += 64 * VEC) {
+        float v[VEC], w[VEC], b[VEC], y[VEC];
+        load_row<E, VEC>(x + i, v);
+        load_row<LnF32, VEC>(weight + i, w);
+        load_row<LnF32, VEC>(bias + i, b);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) y[k] = fmaf(((v[k] - shift) - md) * r, w[k], b[k]);
+        store_row<E, VEC>(o + i, y);
+    }
+}
+
+template <typename E, int VEC>
+__global__ __launch_bounds__(kLnThreads) void ln_bwd_dx_kernel(
+    typename E::T* __restrict__ dinp, const typename E::T* __restrict__ dout,
+    const typename E::T* __restrict__ inp, const float* __restrict__ weight,
+    const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kLnRows + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const typename E::T* x = inp + (size_t)row * C;
+    const typename E::T* dy = dout + (size_t)row * C;
+    const float m = mean[row], r = rstd[row];
+    float sg = 0.f, sgx = 0.f;
+    for (int i = lane * VEC; i < C; i += 64 * VEC) {
+        float v[VEC], d[VEC], w[VEC];
+        load_row<E, VEC>(x + i, v);
+        load_row<E, VEC>(dy + i, d);
+        load_row<LnF32, VEC>(weight + i, w);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float g = w[k] * d[k];
+            sg += g;
+            sgx = fmaf(g, (v[k] - m) * r, sgx);
+        }
+    }
+    const float a = wave_sum(sg) / (float)C;
+    const float c = wave_sum(sgx) / (float)C;
+    typename E::T* dx = dinp + (size_t)row * C;
+    for (int i = lane * VEC; i < C; i += 64 * VEC) {
+        float v[VEC], d[VEC], w[VEC], o[VEC];
+        load_row<E, VEC>(x + i, v);
+        load_row<E, VEC>(dy + i, d);
+        load_row<LnF32, VEC>(weight + i, w);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float xhat = (v[k] - m) * r;
+            o[k] = r * (w[k] * d[k] - a - xhat * c);
+        }
+        store_row<E, VEC>(dx + i, o);
+    }
+}
+
+// Partial column sums over rows [chunk * rows, min(N, (chunk + 1) * rows)):
+// part[chunk][c] = sum of dout * xhat, part[chunk][C + c] = sum of dout.
+// A thread owns VEC consecutive columns; the rows of a chunk are unrolled so
+// that their loads are in flight together.
+template <typename E, int VEC>
+__global__ __launch_bounds__(kLnColThreads) void ln_bwd_cols_kernel(
+    float* __restrict__ part, const typename E::T* __restrict__ dout,
+    const typename E::T* __restrict__ inp, const float* __restrict__ mean,
+    const float* __restrict__ rstd, int N, int C, int rows) {
+    const int c = (blockIdx.x * kLnColThreads + threadIdx.x) * VEC;
+    if (c >= C) return;
+    const int r0 = blockIdx.y * rows;
+    const int r1 = min(N, r0 + rows);
+    float sw[VEC], sb[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) sw[k] = sb[k] = 0.f;
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
+        float d[8][VEC], x[8][VEC];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            load_row<E, VEC>(dout + (size_t)(r + u) * C + c, d[u]);
+            load_row<E, VEC>(inp + (size_t)(r + u) * C + c, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float m = mean[r + u], q = rstd[r + u];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                sw[k] = fmaf(d[u][k], (x[u][k] - m) * q, sw[k]);
+                sb[k] += d[u][k];
+            }
+        }
+    }
+    for (; r < r1; ++r) {
+        float d[VEC], x[VEC];
+        load_row<E, VEC>(dout + (size_t)r * C + c, d);
+        load_row<E, VEC>(inp + (size_t)r * C + c, x);
+        const float m = mean[r], q = rstd[r];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            sw[k] = fmaf(d[k], (x[k] - m) * q, sw[k]);
+            sb[k] += d[k];
+        }
+    }
+    float* p = part + (size_t)blockIdx.y * 2 * C;
+    store_row<LnF32, VEC>(p + c, sw);
+    store_row<LnF32, VEC>(p + C + c, sb);
+}
+
+// dweight and dbias from the chunk partials: a workgroup takes 64 of the 2C
+// partial columns; wave w adds chunks w, w + 16, w + 32, ... in order, and
+// wave 0 adds the 16 wave sums in order (a fixed order: deterministic).
+constexpr int kLnFinalWaves = 16;
+
+__global__ __launch_bounds__(64 * kLnFinalWaves) void ln_bwd_cols_final_kernel(
+    float* __restrict__ dweight, float* __restrict__ dbias, const float* __restrict__ part,
+    int nchunks, int C) {
+    __shared__ float acc[kLnFinalWaves][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + lane;   // of the 2C partial columns
+    float s = 0.f;
+    if (col < 2 * C) {
+        int k = w;
+        for (; k + 3 * kLnFinalWaves < nchunks; k += 4 * kLnFinalWaves) {
+            const float a = part[(size_t)k * 2 * C + col];
+            const float b = part[(size_t)(k + kLnFinalWaves) * 2 * C + col];
+            const float c = part[(size_t)(k + 2 * kLnFinalWaves) * 2 * C + col];
+            const float d = part[(size_t)(k + 3 * kLnFinalWaves) * 2 * C + col];
+            s = (((s + a) + b) + c) + d;
+        }
+        for (; k < nchunks; k += kLnFinalWaves) s += part[(size_t)k * 2 * C + col];
+    }
+    acc[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && col < 2 * C) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < kLnFinalWaves; ++i) t += acc[i][lane];
+        if (col < C)
+            dweight[col] = t;
+        else
+            dbias[col - C] = t;
+    }
+}
+
+template <typename E>
+hipError_t ln_fwd(typename E::T* out, float* mean, float* rstd, const typename E::T* inp,
+                  const float* weight, const float* bias, int N, int C, hipStream_t st) {
+    const unsigned grid = (unsigned)((N + kLnRows - 1) / kLnRows);
+    if (C % 4 == 0)
+        hipLaunchKernelGGL((ln_fwd_kernel<E, 4>), dim3(grid), dim3(kLnThreads), 0, st, out, mean,
+                           rstd, inp, weight, bias, N, C);
+    else
+        hipLaunchKernelGGL((ln_fwd_kernel<E, 1>), dim3(grid), dim3(kLnThreads), 0, st, out, mean,
+                           rstd, inp, weight, bias, N, C);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t ln_bwd(typename E::T* dinp, float* dweight, float* dbias, float* ws,
+                  const typename E::T* dout, const typename E::T* inp, const float* weight,
+                  const float* mean, const float* rstd, int N, int C, hipStream_t st) {
+    const unsigned grid = (unsigned)((N + kLnRows - 1) / kLnRows);
+    if (C % 4 == 0)
+        hipLaunchKernelGGL((ln_bwd_dx_kernel<E, 4>), dim3(grid), dim3(kLnThreads), 0, st, dinp,
+                           dout, inp, weight, mean, rstd, N, C);
+    else
+        hipLaunchKernelGGL((ln_bwd_dx_kernel<E, 1>), dim3(grid), dim3(kLnThreads), 0, st, dinp,
+                           dout, inp, weight, mean, rstd, N, C);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int rows = 0;
+    const int nchunks = layernorm_col_chunks(N, C, &rows);
+    if (C % 4 == 0) {
+        const unsigned gx = (unsigned)((C / 4 + kLnColThreads - 1) / kLnColThreads);
+        hipLaunchKernelGGL((ln_bwd_cols_kernel<E, 4>), dim3(gx, (unsigned)nchunks),
+                           dim3(kLnColThreads), 0, st, ws, dout, inp, mean, rstd, N, C, rows);
+    } else {
+        const unsigned gx = (unsigned)((C + kLnColThreads - 1) / kLnColThreads);
+        hipLaunchKernelGGL((ln_bwd_cols_kernel<E, 1>), dim3(gx, (unsigned)nchunks),
+                           dim3(kLnColThreads), 0, st, ws, dout, inp, mean, rstd, N, C, rows);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned gf = (unsigned)((2 * (long long)C + 63) / 64);
+    hipLaunchKernelGGL(ln_bwd_cols_final_kernel, dim3(gf), dim3(64 * kLnFinalWaves), 0, st,
+                       dweight, dbias, ws, nchunks, C);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Row chunks of the weight/bias gradient: 16 rows each (a thread keeps 16
+// rows' loads of its columns in flight), more when the chunk count would
+// pass 65535 (the grid's y limit).
+int layernorm_col_chunks(int N, int C, int* rows_per_chunk) {
+    (void)C;
+    long long rows = 16;
+    if ((N + rows - 1) / rows > 65535) rows = (N + 65534) / 65535;
+    *rows_per_chunk = (int)rows;
+    return (int)((N + rows - 1) / rows);
+}
+
+size_t layernorm_workspace_floats(int N, int C) {
+    int rows = 0;
+    return (size_t)layernorm_col_chunks(N, C, &rows) * 2 * (size_t)C;
+}
+
+hipError_t launch_layernorm_fwd_f32(float* out, float* mean, float* rstd, const float* inp,
+                                    const float* weight, const float* bias, int N, int C,
+                                    hipStream_t st) {
+    return ln_fwd<LnF32>(out, mean, rstd, inp, weight, bias, N, C, st);
+}
+hipError_t launch_layernorm_fwd_bf16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                                     const float* weight, const float* bias, int N, int C,
+                                     hipStream_t st) {
+    return ln_fwd<LnBF16>(out, mean, rstd, inp, weight, bias, N, C, st);
+}
+hipError_t launch_layernorm_bwd_f32(float* dinp, float* dweight, float* dbias, float* ws,
+                                    const float* dout, const float* inp, const float* weight,
+                                    const float* mean, const float* rstd, int N, int C,
+                                    hipStream_t st) {
+    return ln_bwd<LnF32>(dinp, dweight, dbias, ws, dout, inp, weight, mean, rstd, N, C, st);
+}
+hipError_t launch_layernorm_bwd_bf16(uint16_t* dinp, float* dweight, float* dbias, float* ws,
+                                     const uint16_t* dout, const uint16_t* inp,
+                                     const float* weight, const float* mean, const float* rstd,
+                                     int N, int C, hipStream_t st) {
+    return ln_bwd<LnBF16>(dinp, dweight, dbias, ws, dout, inp, weight, mean, rstd, N, C, st);
+}
+
+}  // namespace attn
