@@ -72,6 +72,9 @@ def parse_args():
     p.add_argument("--flush-mb", type=int, default=512,
                    help="size of the buffer written between the steps of the cache-flushed "
                         "timing (0: skip it); the MI355X last-level cache holds 256 MB")
+    p.add_argument("--layernorm-only", action="store_true",
+                   help="only time the LayerNorm forward and backward over the workload's "
+                        "activation rows (fp32 and bf16) and print them as one JSON line")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes (3 times), "
                         "to calibrate the HBM byte counters of a profiler run")
@@ -501,7 +504,7 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
-    peaks = device_peaks() if not args.calibrate_copy else None
+    peaks = device_peaks() if not (args.calibrate_copy or args.layernorm_only) else None
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
@@ -514,6 +517,11 @@ def main():
 
     la.load()
     w = WORKLOADS[args.workload]
+    if args.layernorm_only:
+        print(json.dumps({"layernorm": [run_layernorm(la, torch, w.B * w.T, w.C, "f32"),
+                                        run_layernorm(la, torch, w.B * w.T, w.C, "bf16")]}),
+              flush=True)
+        return
     dtype = args.dtype or w.dtype
     total_ms, graph_ms, wall_ms, per_kernel, stats = run_gpu(la, torch, w, dtype, args.steps,
                                                              args.warmup, args.flush_mb)
