@@ -1,7 +1,9 @@
 """LayerNorm forward and backward through the C ABI (layernorm_forward,
 layernorm_backward and their bf16 forms) against the fp64 oracle, element
 by element, on seeded inputs: the GPT-2 activation shape (8*1024 rows of
-768), ragged and tiny shapes, rows whose length is not a multiple of 4
+768), ragged and tiny shapes, rows kept in registers (C % 4 == 0 and
+C <= 2048: 1 to 8 float4 chunks per lane, the last one partly filled) and
+rows read twice (longer ones), rows whose length is not a multiple of 4
 (scalar loads), rows with a large mean against their spread, constant
 rows, and a repeat that must be bitwise equal.
 
@@ -27,7 +29,8 @@ from workloads import randn
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(8 * 1024, 768, 0.0), (1, 1, 0.0), (3, 5, 0.0), (17, 64, 0.0), (257, 1000, 3.0),
-          (100, 2050, 0.0), (5, 4097, -1.5), (33, 7, 0.0), (2, 8192, 0.0)]
+          (100, 2050, 0.0), (5, 4097, -1.5), (33, 7, 0.0), (2, 8192, 0.0), (64, 2048, 0.5),
+          (31, 1536, 0.0), (9, 256, 0.0), (7, 260, 0.0)]
 
 
 def _inputs(N, C, loc, dtype, seed):

@@ -14,6 +14,8 @@
 // Here:
 //  * one wave per row; lanes stride the row 4 elements at a time (16-byte
 //    fp32 or 8-byte bf16 loads) when C % 4 == 0, one element otherwise;
+//    rows of C <= 2048 (C % 4 == 0) stay in registers between the two
+//    sweeps, longer ones are read again (from cache);
 //  * forward: one pass of sums of d = x - x[0] and d^2 (shifted data, so
 //    that the difference of the two means does not cancel when |mean| is
 //    large against the spread; the shift changes neither mean nor
@@ -103,7 +105,10 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <typename E, int VEC>
+// NV > 0: the row (C <= 256 * NV, C % 4 == 0) stays in registers between
+// the two sweeps, NV float4 chunks per lane (lane l holds columns
+// 4l + 256k .. +3); NV = 0: the second sweep reads the row again.
+template <typename E, int VEC, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(typename E::T* __restrict__ out,
                                                             float* __restrict__ mean,
                                                             float* __restrict__ rstd,
@@ -111,81 +116,168 @@ __global__ __launch_bounds__(kLnThreads) void ln_fwd_kernel(typename E::T* __res
                                                             const float* __restrict__ weight,
                                                             const float* __restrict__ bias, int N,
                                                             int C) {
+    static_assert(NV == 0 || VEC == 4, "a cached row is read in 4-element chunks");
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kLnRows + (threadIdx.x >> 6);
     if (row >= N) return;   // a whole wave; the kernel has no barrier
     const typename E::T* x = inp + (size_t)row * C;
+    typename E::T* o = out + (size_t)row * C;
     const float shift = E::get(x[0]);
     float s1 = 0.f, s2 = 0.f;
-    for (int i = lane * VEC; i < C; i += 64 * VEC) {
-        float v[VEC];
-        load_row<E, VEC>(x + i, v);
+    if constexpr (NV > 0) {
+        float v[NV][4];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const float d = v[k] - shift;
-            s1 += d;
-            s2 = fmaf(d, d, s2);
+        for (int k = 0; k < NV; ++k) {
+            const int i = 4 * lane + 256 * k;
+            if (i < C) {
+                load_row<E, 4>(x + i, v[k]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[k][j] = shift;   // adds 0 to both sums
+            }
         }
-    }
-    s1 = wave_sum(s1);
-    s2 = wave_sum(s2);
-    const float md = s1 / (float)C;                       // mean - shift
-    const float var = fmaxf(s2 / (float)C - md * md, 0.f);
-    const float r = 1.0f / sqrtf(var + kLnEps);
-    if (lane == 0) {
-        mean[row] = shift + md;
-        rstd[row] = r;
-    }
-    typename E::T* o = out + (size_t)row * C;
-    for (int i = lane * VEC; i < C; i += 64 * VEC) {
-        float v[VEC], w[VEC], b[VEC], y[VEC];
-        load_row<E, VEC>(x + i, v);
-        load_row<LnF32, VEC>(weight + i, w);
-        load_row<LnF32, VEC>(bias + i, b);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) y[k] = fmaf(((v[k] - shift) - md) * r, w[k], b[k]);
-        store_row<E, VEC>(o + i, y);
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float d = v[k][j] - shift;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        const float md = s1 / (float)C;
+        const float var = fmaxf(s2 / (float)C - md * md, 0.f);
+        const float r = 1.0f / sqrtf(var + kLnEps);
+        if (lane == 0) {
+            mean[row] = shift + md;
+            rstd[row] = r;
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int i = 4 * lane + 256 * k;
+            if (i < C) {
+                float w[4], b[4], y[4];
+                load_row<LnF32, 4>(weight + i, w);
+                load_row<LnF32, 4>(bias + i, b);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = fmaf(((v[k][j] - shift) - md) * r, w[j], b[j]);
+                store_row<E, 4>(o + i, y);
+            }
+        }
+    } else {
+        for (int i = lane * VEC; i < C; i += 64 * VEC) {
+            float v[VEC];
+            load_row<E, VEC>(x + i, v);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float d = v[k] - shift;
+                s1 += d;
+                s2 = fmaf(d, d, s2);
+            }
+        }
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        const float md = s1 / (float)C;                       // mean - shift
+        const float var = fmaxf(s2 / (float)C - md * md, 0.f);
+        const float r = 1.0f / sqrtf(var + kLnEps);
+        if (lane == 0) {
+            mean[row] = shift + md;
+            rstd[row] = r;
+        }
+        for (int i = lane * VEC; i < C; i += 64 * VEC) {
+            float v[VEC], w[VEC], b[VEC], y[VEC];
+            load_row<E, VEC>(x + i, v);
+            load_row<LnF32, VEC>(weight + i, w);
+            load_row<LnF32, VEC>(bias + i, b);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) y[k] = fmaf(((v[k] - shift) - md) * r, w[k], b[k]);
+            store_row<E, VEC>(o + i, y);
+        }
     }
 }
 
-template <typename E, int VEC>
+// Input gradient; NV as in ln_fwd_kernel (dout and inp rows both cached).
+template <typename E, int VEC, int NV>
 __global__ __launch_bounds__(kLnThreads) void ln_bwd_dx_kernel(
     typename E::T* __restrict__ dinp, const typename E::T* __restrict__ dout,
     const typename E::T* __restrict__ inp, const float* __restrict__ weight,
     const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C) {
+    static_assert(NV == 0 || VEC == 4, "a cached row is read in 4-element chunks");
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kLnRows + (threadIdx.x >> 6);
     if (row >= N) return;
     const typename E::T* x = inp + (size_t)row * C;
     const typename E::T* dy = dout + (size_t)row * C;
+    typename E::T* dx = dinp + (size_t)row * C;
     const float m = mean[row], r = rstd[row];
     float sg = 0.f, sgx = 0.f;
-    for (int i = lane * VEC; i < C; i += 64 * VEC) {
-        float v[VEC], d[VEC], w[VEC];
-        load_row<E, VEC>(x + i, v);
-        load_row<E, VEC>(dy + i, d);
-        load_row<LnF32, VEC>(weight + i, w);
+    if constexpr (NV > 0) {
+        float v[NV][4], g[NV][4];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const float g = w[k] * d[k];
-            sg += g;
-            sgx = fmaf(g, (v[k] - m) * r, sgx);
-        }
-    }
-    const float a = wave_sum(sg) / (float)C;
-    const float c = wave_sum(sgx) / (float)C;
-    typename E::T* dx = dinp + (size_t)row * C;
-    for (int i = lane * VEC; i < C; i += 64 * VEC) {
-        float v[VEC], d[VEC], w[VEC], o[VEC];
-        load_row<E, VEC>(x + i, v);
-        load_row<E, VEC>(dy + i, d);
-        load_row<LnF32, VEC>(weight + i, w);
+        for (int k = 0; k < NV; ++k) {
+            const int i = 4 * lane + 256 * k;
+            if (i < C) {
+                float d[4], w[4];
+                load_row<E, 4>(x + i, v[k]);
+                load_row<E, 4>(dy + i, d);
+                load_row<LnF32, 4>(weight + i, w);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const float xhat = (v[k] - m) * r;
-            o[k] = r * (w[k] * d[k] - a - xhat * c);
+                for (int j = 0; j < 4; ++j) {
+                    g[k][j] = w[j] * d[j];
+                    v[k][j] = (v[k][j] - m) * r;   // xhat
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[k][j] = v[k][j] = 0.f;
+            }
         }
-        store_row<E, VEC>(dx + i, o);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sg += g[k][j];
+                sgx = fmaf(g[k][j], v[k][j], sgx);
+            }
+        const float a = wave_sum(sg) / (float)C;
+        const float c = wave_sum(sgx) / (float)C;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int i = 4 * lane + 256 * k;
+            if (i < C) {
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = r * (g[k][j] - a - v[k][j] * c);
+                store_row<E, 4>(dx + i, o);
+            }
+        }
+    } else {
+        for (int i = lane * VEC; i < C; i += 64 * VEC) {
+            float v[VEC], d[VEC], w[VEC];
+            load_row<E, VEC>(x + i, v);
+            load_row<E, VEC>(dy + i, d);
+            load_row<LnF32, VEC>(weight + i, w);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float g = w[k] * d[k];
+                sg += g;
+                sgx = fmaf(g, (v[k] - m) * r, sgx);
+            }
+        }
+        const float a = wave_sum(sg) / (float)C;
+        const float c = wave_sum(sgx) / (float)C;
+        for (int i = lane * VEC; i < C; i += 64 * VEC) {
+            float v[VEC], d[VEC], w[VEC], o[VEC];
+            load_row<E, VEC>(x + i, v);
+            load_row<E, VEC>(dy + i, d);
+            load_row<LnF32, VEC>(weight + i, w);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float xhat = (v[k] - m) * r;
+                o[k] = r * (w[k] * d[k] - a - xhat * c);
+            }
+            store_row<E, VEC>(dx + i, o);
+        }
     }
 }
 
@@ -275,16 +367,33 @@ __global__ __launch_bounds__(64 * kLnFinalWaves) void ln_bwd_cols_final_kernel(
     }
 }
 
+// Rows of C % 4 == 0 and C <= 2048 stay in registers between the sweeps
+// (NV = ceil(C / 256) float4 chunks per lane); others are read twice.
+#define LN_ROW_DISPATCH(KERNEL, E, GRID, ...)                                                     \
+    do {                                                                                           \
+        const int nv = (C % 4 == 0 && C <= 2048) ? (C + 255) / 256 : 0;                           \
+        switch (nv) {                                                                              \
+            case 1: hipLaunchKernelGGL((KERNEL<E, 4, 1>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 2: hipLaunchKernelGGL((KERNEL<E, 4, 2>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 3: hipLaunchKernelGGL((KERNEL<E, 4, 3>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 4: hipLaunchKernelGGL((KERNEL<E, 4, 4>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 5: hipLaunchKernelGGL((KERNEL<E, 4, 5>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 6: hipLaunchKernelGGL((KERNEL<E, 4, 6>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 7: hipLaunchKernelGGL((KERNEL<E, 4, 7>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            case 8: hipLaunchKernelGGL((KERNEL<E, 4, 8>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); break; \
+            default:                                                                               \
+                if (C % 4 == 0)                                                                    \
+                    hipLaunchKernelGGL((KERNEL<E, 4, 0>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); \
+                else                                                                               \
+                    hipLaunchKernelGGL((KERNEL<E, 1, 0>), GRID, dim3(kLnThreads), 0, st, __VA_ARGS__); \
+        }                                                                                          \
+    } while (0)
+
 template <typename E>
 hipError_t ln_fwd(typename E::T* out, float* mean, float* rstd, const typename E::T* inp,
                   const float* weight, const float* bias, int N, int C, hipStream_t st) {
-    const unsigned grid = (unsigned)((N + kLnRows - 1) / kLnRows);
-    if (C % 4 == 0)
-        hipLaunchKernelGGL((ln_fwd_kernel<E, 4>), dim3(grid), dim3(kLnThreads), 0, st, out, mean,
-                           rstd, inp, weight, bias, N, C);
-    else
-        hipLaunchKernelGGL((ln_fwd_kernel<E, 1>), dim3(grid), dim3(kLnThreads), 0, st, out, mean,
-                           rstd, inp, weight, bias, N, C);
+    const dim3 grid((unsigned)((N + kLnRows - 1) / kLnRows));
+    LN_ROW_DISPATCH(ln_fwd_kernel, E, grid, out, mean, rstd, inp, weight, bias, N, C);
     return hipGetLastError();
 }
 
@@ -292,13 +401,8 @@ template <typename E>
 hipError_t ln_bwd(typename E::T* dinp, float* dweight, float* dbias, float* ws,
                   const typename E::T* dout, const typename E::T* inp, const float* weight,
                   const float* mean, const float* rstd, int N, int C, hipStream_t st) {
-    const unsigned grid = (unsigned)((N + kLnRows - 1) / kLnRows);
-    if (C % 4 == 0)
-        hipLaunchKernelGGL((ln_bwd_dx_kernel<E, 4>), dim3(grid), dim3(kLnThreads), 0, st, dinp,
-                           dout, inp, weight, mean, rstd, N, C);
-    else
-        hipLaunchKernelGGL((ln_bwd_dx_kernel<E, 1>), dim3(grid), dim3(kLnThreads), 0, st, dinp,
-                           dout, inp, weight, mean, rstd, N, C);
+    const dim3 grid((unsigned)((N + kLnRows - 1) / kLnRows));
+    LN_ROW_DISPATCH(ln_bwd_dx_kernel, E, grid, dinp, dout, inp, weight, mean, rstd, N, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int rows = 0;
