@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(8 * 1024, 768, 0.0), (1, 1, 0.0), (3, 5, 0.0), (17, 64, 0.0), (257, 1000, 3.0),
           (100, 2050, 0.0), (5, 4097, -1.5), (33, 7, 0.0), (2, 8192, 0.0), (64, 2048, 0.5),
-          (31, 1536, 0.0), (9, 256, 0.0), (7, 260, 0.0)]
+          (31, 1536, 0.0), (9, 256, 0.0), (7, 260, 0.0), (12, 1100, 0.0), (10, 1700, 0.0)]
 
 
 def _inputs(N, C, loc, dtype, seed):
