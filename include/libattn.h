@@ -311,6 +311,19 @@ int layernorm_backward_bf16(uint16_t* dinp, float* dweight, float* dbias, const 
                             const uint16_t* inp, const float* weight, const float* mean,
                             const float* rstd, int N, int C);
 
+/* LayerNorm with IEEE-half out and inp (round to nearest even), the 16-bit
+ * storage with fp32 accumulation that "LLM Systems 10 & 11: Accelerating
+ * Transformer Training and Inference" (section 1.2.1) names; the rest as
+ * layernorm_forward.  Outputs must stay below 65504 in magnitude. */
+int layernorm_forward_f16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                          const float* weight, const float* bias, int N, int C);
+
+/* The backward with IEEE-half dinp, dout and inp; the rest as
+ * layernorm_backward. */
+int layernorm_backward_f16(uint16_t* dinp, float* dweight, float* dbias, const uint16_t* dout,
+                           const uint16_t* inp, const float* weight, const float* mean,
+                           const float* rstd, int N, int C);
+
 /* Set the HIP stream (a hipStream_t, or NULL for the null stream) used by
  * the calling thread's subsequent calls.  Always returns ATTN_OK. */
 int attn_set_stream(void* hip_stream);

@@ -298,8 +298,8 @@ def test_error_state_is_per_thread():
     assert seen["b"] == ""
 
 
-LN = [("layernorm_forward", 6), ("layernorm_forward_bf16", 6), ("layernorm_backward", 8),
-      ("layernorm_backward_bf16", 8)]
+LN = [("layernorm_forward", 6), ("layernorm_forward_bf16", 6), ("layernorm_forward_f16", 6),
+      ("layernorm_backward", 8), ("layernorm_backward_bf16", 8), ("layernorm_backward_f16", 8)]
 
 
 @pytest.mark.parametrize("name,nptr", LN)

@@ -18,5 +18,5 @@ from ._binding import (  # noqa: F401
     attn_merge_bf16, attn_merge_f16, attn_release, attn_set_stream, backward, backward_materialized, decode,
     forward, forward_materialized, load, merge,
     layernorm, layernorm_backward, layernorm_backward_bf16, layernorm_forward,
-    layernorm_forward_bf16, layernorm_grad,
+    layernorm_forward_bf16, layernorm_grad, layernorm_forward_f16, layernorm_backward_f16,
 )

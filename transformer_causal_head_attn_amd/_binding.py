@@ -35,6 +35,7 @@ EXPORTS = (
     "attn_decode", "attn_decode_bf16", "attn_decode_f16",
     "attn_merge", "attn_merge_bf16", "attn_merge_f16",
     "layernorm_forward", "layernorm_forward_bf16", "layernorm_backward", "layernorm_backward_bf16",
+    "layernorm_forward_f16", "layernorm_backward_f16",
     "attn_set_stream", "attn_last_error", "attn_release",
 )
 
@@ -88,11 +89,11 @@ def load(path: str | None = None):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 4 + [i] * 5
             fn.restype = i
-        for name in ("layernorm_forward", "layernorm_forward_bf16"):
+        for name in ("layernorm_forward", "layernorm_forward_bf16", "layernorm_forward_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 6 + [i] * 2
             fn.restype = i
-        for name in ("layernorm_backward", "layernorm_backward_bf16"):
+        for name in ("layernorm_backward", "layernorm_backward_bf16", "layernorm_backward_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 8 + [i] * 2
             fn.restype = i
@@ -420,15 +421,32 @@ def layernorm_backward_bf16(dinp, dweight, dbias, dout, inp, weight, mean, rstd,
           int(N), int(C))
 
 
+def layernorm_forward_f16(out, mean, rstd, inp, weight, bias, N, C) -> None:
+    h, f = torch.float16, torch.float32
+    _call("layernorm_forward_f16", _check(out, "out", h, N * C), _check(mean, "mean", f, N),
+          _check(rstd, "rstd", f, N), _check(inp, "inp", h, N * C),
+          _check(weight, "weight", f, C), _check(bias, "bias", f, C), int(N), int(C))
+
+
+def layernorm_backward_f16(dinp, dweight, dbias, dout, inp, weight, mean, rstd, N, C) -> None:
+    h, f = torch.float16, torch.float32
+    _call("layernorm_backward_f16", _check(dinp, "dinp", h, N * C),
+          _check(dweight, "dweight", f, C), _check(dbias, "dbias", f, C),
+          _check(dout, "dout", h, N * C), _check(inp, "inp", h, N * C),
+          _check(weight, "weight", f, C), _check(mean, "mean", f, N), _check(rstd, "rstd", f, N),
+          int(N), int(C))
+
+
 def layernorm(inp: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor):
     """Allocate and return (out, mean, rstd) for the LayerNorm of the rows
-    of inp (..., C), fp32 or bf16 by inp's dtype."""
+    of inp (..., C), fp32, bf16 or fp16 by inp's dtype."""
     C = inp.shape[-1]
     N = inp.numel() // C
     out = torch.empty_like(inp)
     mean = torch.empty(N, dtype=torch.float32, device=inp.device)
     rstd = torch.empty(N, dtype=torch.float32, device=inp.device)
-    fn = layernorm_forward_bf16 if inp.dtype == torch.bfloat16 else layernorm_forward
+    fn = {torch.bfloat16: layernorm_forward_bf16,
+          torch.float16: layernorm_forward_f16}.get(inp.dtype, layernorm_forward)
     fn(out, mean, rstd, inp, weight, bias, N, C)
     return out, mean, rstd
 
@@ -440,7 +458,8 @@ def layernorm_grad(dout, inp, weight, mean, rstd):
     dinp = torch.empty_like(inp)
     dw = torch.empty(C, dtype=torch.float32, device=inp.device)
     db = torch.empty(C, dtype=torch.float32, device=inp.device)
-    fn = layernorm_backward_bf16 if inp.dtype == torch.bfloat16 else layernorm_backward
+    fn = {torch.bfloat16: layernorm_backward_bf16,
+          torch.float16: layernorm_backward_f16}.get(inp.dtype, layernorm_backward)
     fn(dinp, dw, db, dout, inp, weight, mean, rstd, N, C)
     return dinp, dw, db
 

@@ -645,6 +645,21 @@ int layernorm_forward_bf16(uint16_t* out, float* mean, float* rstd, const uint16
                                     attn::launch_layernorm_fwd_bf16);
 }
 
+int layernorm_forward_f16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                          const float* weight, const float* bias, int N, int C) {
+    return ln_forward_any<uint16_t>(out, mean, rstd, inp, weight, bias, N, C,
+                                    "layernorm_forward_f16 launch",
+                                    attn::launch_layernorm_fwd_f16);
+}
+
+int layernorm_backward_f16(uint16_t* dinp, float* dweight, float* dbias, const uint16_t* dout,
+                           const uint16_t* inp, const float* weight, const float* mean,
+                           const float* rstd, int N, int C) {
+    return ln_backward_any<uint16_t>(dinp, dweight, dbias, dout, inp, weight, mean, rstd, N, C,
+                                     "layernorm_backward_f16 launch",
+                                     attn::launch_layernorm_bwd_f16);
+}
+
 int layernorm_backward(float* dinp, float* dweight, float* dbias, const float* dout,
                        const float* inp, const float* weight, const float* mean, const float* rstd,
                        int N, int C) {

@@ -230,6 +230,13 @@ hipError_t launch_layernorm_bwd_f32(float* dinp, float* dweight, float* dbias, f
                                     const float* dout, const float* inp, const float* weight,
                                     const float* mean, const float* rstd, int N, int C,
                                     hipStream_t st);
+hipError_t launch_layernorm_fwd_f16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                                    const float* weight, const float* bias, int N, int C,
+                                    hipStream_t st);
+hipError_t launch_layernorm_bwd_f16(uint16_t* dinp, float* dweight, float* dbias, float* ws,
+                                    const uint16_t* dout, const uint16_t* inp, const float* weight,
+                                    const float* mean, const float* rstd, int N, int C,
+                                    hipStream_t st);
 hipError_t launch_layernorm_bwd_bf16(uint16_t* dinp, float* dweight, float* dbias, float* ws,
                                      const uint16_t* dout, const uint16_t* inp,
                                      const float* weight, const float* mean, const float* rstd,

@@ -1,5 +1,5 @@
 // layernorm.hip -- LayerNorm forward and backward over the rows of an
-// (N, C) matrix for gfx950: fp32 or bfloat16 rows, fp32 weight, bias, mean,
+// (N, C) matrix for gfx950: fp32, bfloat16 or IEEE-half rows, fp32 weight, bias, mean,
 // rstd and arithmetic.
 //
 // Method: "llm.c 的中文注解-20240423", section 1.8 (layernorm_forward_kernel3):
@@ -77,6 +77,33 @@ struct LnBF16 {
         v[1] = __uint_as_float(x.x & 0xFFFF0000u);
         v[2] = __uint_as_float(x.y << 16);
         v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+        const uint2 x = make_uint2((uint32_t)put(v[0]) | ((uint32_t)put(v[1]) << 16),
+                                   (uint32_t)put(v[2]) | ((uint32_t)put(v[3]) << 16));
+        *reinterpret_cast<uint2*>(p) = x;
+    }
+};
+
+struct LnF16 {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(uint16_t v) {
+        _Float16 h;
+        __builtin_memcpy(&h, &v, 2);
+        return (float)h;
+    }
+    static __device__ __forceinline__ uint16_t put(float v) {   // round to nearest even
+        const _Float16 h = (_Float16)v;
+        uint16_t u;
+        __builtin_memcpy(&u, &h, 2);
+        return u;
+    }
+    static __device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        v[0] = get((uint16_t)(x.x & 0xFFFFu));
+        v[1] = get((uint16_t)(x.x >> 16));
+        v[2] = get((uint16_t)(x.y & 0xFFFFu));
+        v[3] = get((uint16_t)(x.y >> 16));
     }
     static __device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
         const uint2 x = make_uint2((uint32_t)put(v[0]) | ((uint32_t)put(v[1]) << 16),
@@ -588,4 +615,18 @@ hipError_t launch_layernorm_bwd_bf16(uint16_t* dinp, float* dweight, float* dbia
     return ln_bwd<LnBF16>(dinp, dweight, dbias, ws, dout, inp, weight, mean, rstd, N, C, st);
 }
 
+}  // namespace attn
+
+namespace attn {
+hipError_t launch_layernorm_fwd_f16(uint16_t* out, float* mean, float* rstd, const uint16_t* inp,
+                                    const float* weight, const float* bias, int N, int C,
+                                    hipStream_t st) {
+    return ln_fwd<LnF16>(out, mean, rstd, inp, weight, bias, N, C, st);
+}
+hipError_t launch_layernorm_bwd_f16(uint16_t* dinp, float* dweight, float* dbias, float* ws,
+                                    const uint16_t* dout, const uint16_t* inp, const float* weight,
+                                    const float* mean, const float* rstd, int N, int C,
+                                    hipStream_t st) {
+    return ln_bwd<LnF16>(dinp, dweight, dbias, ws, dout, inp, weight, mean, rstd, N, C, st);
+}
 }  // namespace attn
