@@ -118,3 +118,59 @@ def test_layernorm_backward_is_deterministic():
     torch.cuda.synchronize()
     for a, c in zip(r1, r2):
         assert torch.equal(a, c)
+
+
+def test_layernorm_on_torch_stream():
+    """The calls are enqueued on torch's current stream, behind the copy
+    that fills their input on that stream."""
+    N, C = 4096, 768
+    x, dy, w, b = _inputs(N, C, 0.5, "f32", 77)
+    ref_out, _, _ = oracle.layernorm_forward(x.double().numpy(), w.numpy(), b.numpy())
+    ref_dx, _, _ = oracle.layernorm_backward(dy.double().numpy(), x.double().numpy(), w.numpy())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xg = torch.empty((N, C), device="cuda")
+        dyg = torch.empty((N, C), device="cuda")
+        xg.copy_(x.pin_memory(), non_blocking=True)
+        dyg.copy_(dy.pin_memory(), non_blocking=True)
+        out, mean, rstd = la.layernorm(xg, w.cuda(), b.cuda())
+        dx, _, _ = la.layernorm_grad(dyg, xg, w.cuda(), mean, rstd)
+    s.synchronize()
+    _close(out, ref_out, 2e-5, 1e-4, "out")
+    _close(dx, ref_dx, 2e-5, 1e-4, "dinp")
+
+
+def test_layernorm_graph_replays():
+    """Forward and backward captured in a HIP graph (the backward's
+    workspace already grown by an eager call) give the eager bits on every
+    replay, with eager work in between."""
+    N, C = 2048, 768
+    x, dy, w, b = _inputs(N, C, 0.0, "f32", 78)
+    xg, dyg, wg, bg = x.cuda(), dy.cuda(), w.cuda(), b.cuda()
+    out, mean, rstd = torch.empty_like(xg), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+    dx, dw, db = torch.empty_like(xg), torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+
+    def step():
+        la.layernorm_forward(out, mean, rstd, xg, wg, bg, N, C)
+        la.layernorm_backward(dx, dw, db, dyg, xg, wg, mean, rstd, N, C)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, mean, rstd, dx, dw, db)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in (out, mean, rstd, dx, dw, db):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, e in zip((out, mean, rstd, dx, dw, db), eager):
+            assert torch.equal(a, e)
