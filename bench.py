@@ -2,11 +2,13 @@
 """Benchmark of the fused attention path on one MI355X.
 
 One step = one forward (attn_forward) plus one backward over the workload's
-synthetic batch, inputs resident in device memory.  The fp32 backward is the
-one attn_backward runs: the D = rowsum(dO*O) pre-pass, the dK/dV kernel that
-also stores dS, and the dQ kernel that reads it.  The 16-bit backward is the
-dQ kernel (which also forms D, recomputing S and dP) then the dK/dV kernel.
-Prints one JSON line.
+synthetic batch, inputs resident in device memory.  The backward is the one
+attn_backward runs, in every dtype: the dQ kernel (which recomputes S and dP
+from lse and also forms D = rowsum(dO*O)), then the dK/dV kernel (which
+recomputes P from lse and reads D); its only scratch is D, B*NH*T floats.
+The fp32 dS block store order (the D pre-pass, a dK/dV kernel that also
+stores dS, a dQ kernel that reads it; O(T^2) caller-owned memory) is timed
+beside it as fp32_ds_store_order.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16]
 
@@ -48,17 +50,20 @@ METRIC = "attention fwd+bwd causal TFLOP/s and % MFMA peak, B8 T1024 C768 NH12"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_causal_head_attn_amd", "csrc")
-KERNEL_SOURCE = {"f32": "flash_f32.hip", "bf16": "flash_half.hip", "f16": "flash_half.hip"}
+KERNEL_SOURCE = {"f32": "flash_f32.hip", "f32_ds": "flash_f32.hip", "bf16": "flash_half.hip", "f16": "flash_half.hip"}
 
 
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=600,
-                   help="untimed steps per dtype; the bf16 kernels reach their steady speed "
-                        "only after ~70 ms of work (600 bf16 steps of the GPT-2 layer), the "
-                        "fp32 ones after ~30 ms")
+    p.add_argument("--warmup", type=int, default=5,
+                   help="untimed steps per dtype (at least; see --warmup-ms)")
+    p.add_argument("--warmup-ms", type=float, default=150.0,
+                   help="after the --warmup steps, keep running untimed steps until this much "
+                        "time has passed since the first one: the kernels reach their steady "
+                        "speed only after ~30 ms (fp32) to ~70 ms (bf16) of work, whatever "
+                        "the step count")
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--dtype", choices=["f32", "bf16", "f16"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,7 +149,7 @@ def compulsory_bytes(w, dtype):
     """Compulsory HBM bytes of one forward and one backward: the forward
     reads qkv once and writes out and lse; the backward reads qkv, out, dout
     and lse, writes and reads D, and writes dqkv."""
-    esz = 4 if dtype == "f32" else 2
+    esz = 4 if dtype in ("f32", "f32_ds") else 2
     io = w.B * w.T * w.C * esz
     rows = 4 * w.B * w.NH * w.T
     return 3 * io + io + rows, 3 * io + 2 * io + rows + 2 * rows + 3 * io
@@ -163,20 +168,14 @@ def kernel_flops(w, dtype):
     """Algorithmic flops of each kernel for one launch: 2*hs per unmasked
     (query, key) pair per contraction it performs."""
     u = 2 * w.hs * w.pairs * w.B * w.NH
-    if dtype == "f32":
+    if dtype == "f32_ds":           # the fp32 dS block store order
         return {"fwd": 2 * u,       # S = Q K^T, O = P V
                 "prepass": 0,       # D = dO.O per row (HBM-bound)
                 "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q (+ dS stored)
                 "dq": u}            # dQ = dS K from the stored dS
     return {"fwd": 2 * u,
-            "dkdv": 4 * u,
+            "dkdv": 4 * u,          # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
             "dq": 3 * u}            # S, dP, dQ = dS K (plus the D = dO.O row sums)
-
-
-def ds_path(la, w):
-    """Whether attn_backward (fp32) takes the dS block store order for this
-    shape (the store fits under the library's 4 GiB cap)."""
-    return 0 < la.attn_backward_ds_bytes(w.B, w.T, w.C, w.NH, int(w.causal)) <= 4 << 30
 
 
 def source_sha(dtype):
@@ -199,9 +198,26 @@ def measured_traffic(kernel, dtype, workload_key):
     return float(fetch.group(1)) + float(write.group(1))
 
 
-def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0):
+def warm_up(torch, stages, warmup, warmup_ms):
+    """`warmup` untimed steps, then more until `warmup_ms` have passed since
+    the first (the clocks and caches settle after tens of milliseconds of
+    work, not after a fixed step count).  Returns (steps run, ms)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(max(1, warmup) if n == 0 else 10):
+            for _, fn in stages:
+                fn()
+            n += 1
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        if n >= warmup and ms >= warmup_ms:
+            return n, ms
+
+
+def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0, warmup_ms=150.0):
     from workloads import workload_inputs
-    qkv_c, dout_c = workload_inputs(w, dtype)
+    qkv_c, dout_c = workload_inputs(w, "f32" if dtype == "f32_ds" else dtype)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
     B, T, C, NH = w.B, w.T, w.C, w.NH
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
@@ -209,15 +225,13 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0):
     lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
     dqkv = torch.empty_like(qkv)
     D = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
-    sfx = "" if dtype == "f32" else "_" + dtype
+    sfx = "" if dtype in ("f32", "f32_ds") else "_" + dtype
     fwd = getattr(la, "attn_forward" + sfx)
     dkdv = getattr(la, "attn_backward_dkdv" + sfx)
     dq = getattr(la, "attn_backward_dq" + sfx)
     c = int(w.causal)
-    if dtype == "f32":
-        if not ds_path(la, w):
-            raise SystemExit("bench.py: this shape's dS block store exceeds the fused "
-                             "backward's cap; the bench times the dS order only")
+    if dtype == "f32_ds":
+        # caller-owned dS block store (O(T^2) floats)
         dS = torch.empty((la.attn_backward_ds_bytes(B, T, C, NH, c) // 4,), device="cuda")
         stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
                   ("prepass", lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH)),
@@ -229,10 +243,7 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0):
                   ("dq", lambda: dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c)),
                   ("dkdv", lambda: dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c))]
 
-    for _ in range(warmup):
-        for _, fn in stages:
-            fn()
-    torch.cuda.synchronize()
+    warm_steps, warm_ms = warm_up(torch, stages, warmup, warmup_ms)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(steps)]
@@ -300,6 +311,8 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0):
     e1.record()
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / steps
+    stats["warmup_steps_run"] = warm_steps
+    stats["warmup_ms"] = round(warm_ms, 1)
     return eager_ms, graph_ms, wall * 1e3 / steps, per_kernel, stats
 
 
@@ -426,17 +439,22 @@ def run_layernorm(la, torch, N, C, dtype, steps=50, warmup=100):
 
 def cpu_baseline(w, dtype, budget_s):
     """The fp64 oracle, as it stands, on the first heads of the same
-    workload in (b, h) order until the CPU budget is spent."""
+    workload in (b, h) order until the CPU budget is spent.  The inputs are
+    widened to float64 and the heads cut out before the clock starts; value
+    is the useful flop count of the heads done over the oracle's own
+    forward + backward time."""
+    import numpy as np
     import oracle
     from workloads import workload_inputs
     qkv, dout = workload_inputs(w, dtype)
+    q64 = np.ascontiguousarray(qkv.double().numpy())
+    d64 = np.ascontiguousarray(dout.double().numpy())
     heads = [(b, h) for b in range(w.B) for h in range(w.NH)]
     done = 0
     tf = tb = 0.0
-    t0 = time.perf_counter()
     for b, h in heads:
-        qs = oracle.head_slice(qkv, b, h, w.NH, packed=True)
-        ds = oracle.head_slice(dout, b, h, w.NH, packed=False)
+        qs = oracle.head_slice(q64, b, h, w.NH, packed=True)
+        ds = oracle.head_slice(d64, b, h, w.NH, packed=False)
         t1 = time.perf_counter()
         oracle.forward(qs, 1, w.causal)
         t2 = time.perf_counter()
@@ -444,14 +462,13 @@ def cpu_baseline(w, dtype, budget_s):
         tf += t2 - t1
         tb += time.perf_counter() - t2
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if tf + tb >= budget_s:
             break
-    dt = time.perf_counter() - t0
     flops = 14 * w.hs * w.pairs * done
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+    return {"value": flops / (tf + tb) / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} heads (first in (b,h) order) of the same workload, "
-                      f"fp64 forward+backward, {dt:.1f} s",
+                      f"fp64 forward+backward, {tf + tb:.2f} s of oracle time",
             "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
             "host": host_description(),
             "small_configs": oracle_small_configs()}
@@ -524,7 +541,8 @@ def main():
         return
     dtype = args.dtype or w.dtype
     total_ms, graph_ms, wall_ms, per_kernel, stats = run_gpu(la, torch, w, dtype, args.steps,
-                                                             args.warmup, args.flush_mb)
+                                                             args.warmup, args.flush_mb,
+                                                             args.warmup_ms)
     flops = w.flops_fwd + w.flops_bwd
     value = flops / (total_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
@@ -552,7 +570,10 @@ def main():
         f"attention fwd+bwd TFLOP/s and % MFMA peak, {w.label()}"
     line = {
         "metric": metric, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 5),
+        "steps": args.steps, "warmup": args.warmup,
+        "warmup_note": f"{stats['warmup_steps_run']} untimed steps were run: the --warmup "
+                       f"count, then more until {args.warmup_ms:g} ms had passed",
+        "ms_per_step": round(total_ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded N(0,1) qkv and dout, no dataset)",
         "config": {"workload": f"{w.name} {w.label()}", "B": w.B, "T": w.T, "C": w.C,
@@ -561,6 +582,8 @@ def main():
         "timing": "ms_per_step and kernels: the C-ABI calls launched one by one, each kernel "
                   "between HIP events; graph_ms_per_step: K replays of the step captured in "
                   "one HIP graph",
+        "backward": "attn_backward's order: dQ (recomputes S and dP from lse, forms D), "
+                    "then dK/dV (recomputes P, reads D); scratch B*NH*T floats",
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3),
         "wall_ms_per_step": round(wall_ms, 5),
@@ -573,12 +596,31 @@ def main():
         "device_peaks": peaks,
     }
 
+    if not args.no_extra and dtype == "f32":
+        # the fp32 dS block store order through the stage calls, with a
+        # caller-owned store of O(T^2) floats (beside the headline, which
+        # runs attn_backward's recompute order)
+        d_total, d_graph, _, d_kernels, d_stats = run_gpu(la, torch, w, "f32_ds", args.steps,
+                                                          args.warmup, 0, args.warmup_ms)
+        d_val = flops / (d_total * 1e-3) / 1e12
+        dkf = kernel_flops(w, "f32_ds")
+        line["fp32_ds_store_order"] = {
+            "order": "pre-pass D, dK/dV also storing dS, dQ = scale dS K from the store",
+            "ds_store_bytes": la.attn_backward_ds_bytes(w.B, w.T, w.C, w.NH, int(w.causal)),
+            "ms_per_step": round(d_total, 5), "tflops": round(d_val, 3),
+            "frac_mfma_peak": round(d_val / PEAK_TFLOPS["f32"], 4),
+            "graph_ms_per_step": round(d_graph, 5), "step_stats": d_stats,
+            "kernels": {k: ({"ms": round(v, 5),
+                             "frac_peak": round(dkf[k] / (v * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4)}
+                            if dkf[k] else {"ms": round(v, 5)})
+                        for k, v in d_kernels.items()}}
+
     if not args.no_extra:
         for other in ("f32", "bf16", "f16"):
             if other == dtype:
                 continue
             o_total, o_graph, _, o_kernels, o_stats = run_gpu(la, torch, w, other, args.steps,
-                                                              args.warmup)
+                                                              args.warmup, 0, args.warmup_ms)
             o_val = flops / (o_total * 1e-3) / 1e12
             line["same_workload_" + other] = {
                 "ms_per_step": round(o_total, 5), "tflops": round(o_val, 3),
@@ -598,7 +640,8 @@ def main():
                 continue
             wo = WORKLOADS[key]
             o_total, o_graph, _, o_kernels, o_stats = run_gpu(la, torch, wo, wo.dtype,
-                                                              args.steps, min(args.warmup, 150))
+                                                              args.steps, args.warmup, 0,
+                                                              args.warmup_ms)
             o_flops = wo.flops_fwd + wo.flops_bwd
             o_val = o_flops / (o_total * 1e-3) / 1e12
             others.append({"workload": f"{wo.name} {wo.label()}", "dtype": wo.dtype,

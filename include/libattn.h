@@ -45,13 +45,21 @@
  * (attn_set_stream; default: the null stream) and return without waiting.
  * Results are deterministic: no atomics, fixed reduction order.
  *
- * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need B*NH*T floats of
- * scratch for D, attn_backward (fp32) also the dS block store of up to 4 GiB
- * (attn_backward_ds_bytes), attn_decode and attn_decode_bf16 room for their
- * partial results; libattn keeps one grow-only buffer per device, allocated with
- * hipMalloc on first need, and frees it in attn_release().  Calls that use
- * it share it, so such calls on one device must not overlap in time (calls
- * on one stream never do).  With the environment variable
+ * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need
+ * B*NH*T floats of scratch for D, attn_decode* room for their partial
+ * results (4*B*NH*(hs+1)*ceil(T/128) bytes at most), layernorm_backward*
+ * room for column partial sums.  libattn keeps one grow-only buffer per
+ * device, allocated with hipMalloc on first need.  A call that needs more
+ * allocates a larger buffer and retires the old one without freeing it, so
+ * growing never synchronises the device and never frees memory that queued
+ * work or a captured HIP graph still uses; attn_release() frees the current
+ * and every retired buffer.  Calls that use the workspace share it, so such
+ * calls on one device must not overlap in time (calls on one stream never
+ * do).  HIP graphs: a captured call keeps the workspace address it saw, and
+ * a call that grows the workspace allocates, which stream capture may
+ * forbid; capture only after an eager call of the same or a larger shape
+ * has sized the workspace, or capture the stage calls, which take
+ * caller-owned buffers and allocate nothing.  With the environment variable
  * ATTN_TEST_FAIL_ALLOC=1 that allocation fails (ATTN_EHIP) before any HIP
  * call, so callers can test their error handling on any host.
  *
@@ -89,16 +97,14 @@ int attn_forward(float* out, float* lse, const float* qkv,
 
 /*
  * Fused backward, fp32.  Reads dout (B,T,C), qkv, and the forward's out and
- * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  When the dS block store of the
- * shape (attn_backward_ds_bytes) is at most 4 GiB it runs the D pre-pass, a
- * dK/dV kernel that recomputes the probabilities from lse and also writes dS,
- * and a dQ kernel that forms dq = scale * dS K from the stored blocks (the
- * three stages attn_backward_preprocess, attn_backward_dkdv_ds and
- * attn_backward_dq_ds below, with the dS blocks in the library workspace).
- * Otherwise it runs a dQ kernel that recomputes S and dP itself (and also
- * forms D = rowsum(dout*out)) and then the dK/dV kernel
- * (attn_backward_dq, attn_backward_dkdv).  Both orders give the same result
- * up to the rounding of fp32 sums.
+ * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  It runs a dQ kernel that
+ * recomputes the probabilities from lse and the products dP = dout V^T
+ * itself and also forms D = rowsum(dout*out), then a dK/dV kernel that
+ * recomputes the probabilities again and reads D (the stages
+ * attn_backward_dq and attn_backward_dkdv below).  Memory is O(B*NH*T): the
+ * only scratch is D in the library workspace.  (The dS block store stages
+ * further below trade O(T^2) caller-owned memory for two of the dQ
+ * kernel's three contractions.)
  */
 int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   const float* out, const float* lse,
@@ -111,8 +117,7 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
  *       (D[t] = sum_j att[t,j] datt[t,j], the row term of the closed-form
  *       softmax gradient) and the dq third of dqkv;
  *   attn_backward_dkdv: reads that D, writes the dk and dv thirds of dqkv.
- * attn_backward runs dq then dkdv on the same stream for shapes whose dS
- * block store would exceed 4 GiB (below: the dS store stages).
+ * attn_backward runs dq then dkdv on the same stream.
  * attn_backward_preprocess computes D alone (the same value attn_backward_dq
  * writes, up to summation order), for callers that run dkdv first or need D
  * by itself.

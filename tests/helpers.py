@@ -31,6 +31,74 @@ def assert_close(gpu, ref, dtype: str, what: str):
     return float(err.max())
 
 
+# Row-scaled checks of the 16-bit paths, beside the stated bound: per row
+# of each head and q/k/v part, elementwise |gpu - oracle| <= ROW_TOL[0] *
+# (RMS_row + 0.01 RMS_head) + rtol |oracle|, and in the 2-norm
+# ||gpu - oracle||_row <= ROW_TOL[1] * (||oracle||_row + 0.01 RMS_head sqrt(hs)).
+# A zeroed (or wholly wrong) row fails both whatever its magnitude.  The
+# constants leave 2.5-4x over the worst errors of a model of the bf16
+# rounding (P and dS rounded as matrix-core operands, the normaliser over
+# the rounded P, D from the rounded out) on heads of the GPT-2, ViT and
+# long-context workloads: 0.064 elementwise and 0.020 row-wise
+# (tests/test_parity_power.py).  fp16 rounds 8x finer; its constants are 4x
+# smaller.  Exempt, and held to the stated bound only: the dq rows of causal
+# queries with fewer than FEW_KEYS keys.  There sum_j dS[t,j] = 0 (exactly,
+# in exact arithmetic) cancels over a few terms, and the rounding of the
+# normaliser and of out (through D = dout . out) leaves the row with a large
+# relative error: up to 0.27 of its norm in the rounding model, at t = 1
+# (2 keys), and never past t = 2 on the GPT-2 layer's 96 heads.
+ROW_TOL = {"bf16": (0.25, 0.05), "f16": (0.0625, 0.0125)}
+FEW_KEYS = 16
+
+
+def _row_view(r, NH: int, kind: str):
+    """(B, T, parts, NH, hs) view of a packed (B,T,3C) or (B,T,C) array."""
+    B, T, W = r.shape
+    parts = 3 if kind == "packed" else 1
+    return r.reshape(B, T, parts, NH, W // (parts * NH))
+
+
+def row_scaled_violations(g, r, dtype: str, NH: int, kind: str, causal: bool = True):
+    """(elementwise violations, row-norm violations, worst elementwise
+    index) of the row-scaled checks above."""
+    eatol, nrel = ROW_TOL[dtype]
+    rtol = TOL[dtype][1]
+    gv, rv = _row_view(g, NH, kind), _row_view(r, NH, kind)
+    hs = rv.shape[-1]
+    rms_head = np.sqrt(np.mean(rv * rv, axis=(1, 4), keepdims=True))
+    rms_row = np.sqrt(np.mean(rv * rv, axis=4, keepdims=True))
+    err = np.abs(gv - rv)
+    bound = eatol * (rms_row + 0.01 * rms_head) + rtol * np.abs(rv)
+    ebad = err > bound
+    enorm = np.sqrt(np.sum(err * err, axis=4))
+    rnorm = np.sqrt(np.sum(rv * rv, axis=4))
+    nbad = enorm > nrel * (rnorm + 0.01 * rms_head[..., 0] * np.sqrt(hs))
+    T = rv.shape[1]
+    if kind == "packed" and (causal or T < FEW_KEYS):
+        few = FEW_KEYS - 1 if causal else T   # causal row t has t + 1 keys
+        ebad[:, :few, 0] = False
+        nbad[:, :few, 0] = False
+    worst = np.unravel_index(int(np.argmax(np.where(ebad.reshape(r.shape), (err - bound).reshape(r.shape), -np.inf))), r.shape) if ebad.any() else None
+    return int(ebad.sum()), int(nbad.sum()), worst
+
+
+def assert_close_scaled(gpu, ref, dtype: str, what: str, NH: int, kind: str,
+                        causal: bool = True):
+    """The stated elementwise bound, then the row-scaled checks (ROW_TOL)
+    on `kind` "packed" (B,T,3C) or "rows" (B,T,C) arrays.  With dout ~
+    N(0, 0.1) most gradient entries lie below the stated absolute term, so
+    the stated bound alone would accept a zeroed row; these do not."""
+    assert_close(gpu, ref, dtype, what)
+    g = gpu.detach().to("cpu").double().numpy() if hasattr(gpu, "detach") else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    ne, nn, worst = row_scaled_violations(g, r, dtype, NH, kind, causal)
+    if ne or nn:
+        at = f"; worst element {worst}: gpu={g[worst]!r} ref={r[worst]!r}" if worst else ""
+        raise AssertionError(f"{what}: {ne} elements and {nn} rows outside the row-scaled "
+                             f"bounds {ROW_TOL[dtype]}{at}")
+    return float(np.abs(g - r).max())
+
+
 def gpu_fwd_bwd(la, qkv_cpu: torch.Tensor, dout_cpu: torch.Tensor, NH: int, causal: bool):
     """Run the fused forward and backward on cuda:0; return CPU tensors
     (out, lse, dqkv)."""
@@ -54,3 +122,42 @@ def head_view(x, b: int, h: int, NH: int, packed: bool):
     C = x.shape[2]
     hs = C // NH
     return x[b:b + 1, :, h * hs:(h + 1) * hs]
+
+
+def check_workload(la, oracle_mod, w, dtype: str, heads=None, case=None):
+    """Run workload `w`'s seeded inputs in `dtype` through the fused forward
+    and backward on the GPU, in the launch configuration the benchmark
+    times, and compare against the oracle: every head when `heads` is None
+    (one oracle call on the whole batch), else the listed (b, h) heads (the
+    oracle on each head cut out of the packed tensors; heads are
+    independent).  out and dqkv get the stated bound and the RMS-scaled one
+    (assert_close_scaled), lse the stated bound."""
+    from workloads import workload_inputs
+    qkv, dout = workload_inputs(w, dtype)
+    if case:
+        print(f"\n[case] {case}", flush=True)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
+    if heads is None:
+        ro, rl = oracle_mod.forward(qkv, w.NH, w.causal)
+        rd = oracle_mod.backward(qkv, dout, w.NH, w.causal)
+        assert_close_scaled(out, ro, dtype, "out", w.NH, "rows", w.causal)
+        assert_close(lse, rl, dtype, "lse")
+        assert_close_scaled(dqkv, rd, dtype, "dqkv", w.NH, "packed", w.causal)
+        return
+    q64 = qkv.double().numpy()
+    d64 = dout.double().numpy()
+    for b, h in heads:
+        qs = oracle_mod.head_slice(q64, b, h, w.NH, packed=True)
+        ds = oracle_mod.head_slice(d64, b, h, w.NH, packed=False)
+        ro, rl = oracle_mod.forward(qs, 1, w.causal)
+        rd = oracle_mod.backward(qs, ds, 1, w.causal)
+        assert_close_scaled(head_view(out, b, h, w.NH, False), ro, dtype, f"out head {(b, h)}",
+                            1, "rows", w.causal)
+        assert_close(lse[b:b + 1, h:h + 1].numpy(), rl, dtype, f"lse head {(b, h)}")
+        assert_close_scaled(head_view(dqkv, b, h, w.NH, True), rd, dtype, f"dqkv head {(b, h)}",
+                            1, "packed", w.causal)
+
+
+# 8 of the 16 heads of the long-context workload (B = 1), spread over the
+# head index range
+LONG_CONTEXT_HEADS = [(0, h) for h in (0, 2, 5, 7, 8, 10, 13, 15)]

@@ -1,7 +1,8 @@
 """bench.py's accounting on the CPU: the per-kernel flop counts add up to
-the useful 14 * hs * pairs * B * NH of a step for fp32 (whose dQ kernel
-reads the stored dS) and to 18 * hs * pairs * B * NH for the 16-bit step
-(whose dQ kernel recomputes S and dP: 4 + 8 + 6), and the compulsory HBM bytes
+18 * hs * pairs * B * NH for the step attn_backward runs in every dtype
+(whose dQ kernel recomputes S and dP: 4 + 8 + 6) and to the useful
+14 * hs * pairs * B * NH for the fp32 dS block store order (whose dQ kernel
+reads the stored dS: 4 + 8 + 2), and the compulsory HBM bytes
 match the figures worked out by hand for the five workloads (forward: qkv
 read, out and lse written; backward: qkv, out, dout, lse read, D written and
 read, dqkv written)."""
@@ -12,13 +13,13 @@ from workloads import WORKLOADS
 
 
 @pytest.mark.parametrize("key", sorted(WORKLOADS))
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16"])
 def test_kernel_flops_add_up_to_the_step(key, dtype):
     w = WORKLOADS[key]
     kf = bench.kernel_flops(w, dtype)
     unit = w.hs * w.pairs * w.B * w.NH
     assert w.flops_fwd + w.flops_bwd == 14 * unit
-    assert sum(kf.values()) == (14 if dtype == "f32" else 18) * unit
+    assert sum(kf.values()) == (14 if dtype == "f32_ds" else 18) * unit
     assert kf["fwd"] == w.flops_fwd
 
 

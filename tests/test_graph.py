@@ -24,6 +24,10 @@ def la():
 def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
     if dtype == "f32":
         return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
+                lambda: la.attn_backward_dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c),
+                lambda: la.attn_backward_dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
+    if dtype == "f32_ds":
+        return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
                 lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH),
                 lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D, B, T, C, NH, c),
                 lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c)]
@@ -32,14 +36,14 @@ def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
             lambda: la.attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16"])
 def test_graph_replays_equal_eager(la, dtype):
     B, T, C, NH, c = 2, 150, 256, 4, 1
     print(f"\n[case] graph replay {dtype} B{B} T{T} C{C} NH{NH}", flush=True)
     sys.stdout.flush()
-    qkv_c, dout_c = make_inputs(B, T, C, dtype, seed=71)
+    qkv_c, dout_c = make_inputs(B, T, C, "bf16" if dtype == "bf16" else "f32", seed=71)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     out = torch.empty((B, T, C), dtype=tdt, device="cuda")
     lse = torch.empty((B, NH, T), device="cuda")
     D = torch.empty((B, NH, T), device="cuda")
@@ -69,3 +73,41 @@ def test_graph_replays_equal_eager(la, dtype):
         o2, l2 = la.forward(other, NH, True)
         la.backward(dout, other, o2, l2, NH, True)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_captured_fused_backward_survives_workspace_growth(la, dtype):
+    """A captured fused backward keeps the workspace address it saw; a later
+    eager call at a larger shape grows the workspace, which must retire the
+    old buffer without freeing it, so the graph's replays still give the
+    eager bits."""
+    B, T, C, NH, c = 2, 150, 256, 4, 1
+    print(f"\n[case] workspace growth under a captured {dtype} attn_backward", flush=True)
+    torch.cuda.synchronize()
+    la.attn_release()           # start from no workspace: the first call sizes it
+    sfx = "" if dtype == "f32" else "_bf16"
+    bwd = getattr(la, "attn_backward" + sfx)
+    qkv_c, dout_c = make_inputs(B, T, C, dtype, seed=72)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    out, lse = la.forward(qkv, NH, True)
+    dqkv = torch.empty_like(qkv)
+    bwd(dqkv, dout, qkv, out, lse, B, T, C, NH, c)     # eager: sizes the workspace
+    torch.cuda.synchronize()
+    ref = dqkv.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bwd(dqkv, dout, qkv, out, lse, B, T, C, NH, c)
+    # a shape with 16x the D rows: the workspace must grow
+    Bb, Tb = 4, 1200
+    qb_c, db_c = make_inputs(Bb, Tb, C, dtype, seed=73)
+    qb, db = qb_c.cuda(), db_c.cuda()
+    ob, lb = la.forward(qb, NH, True)
+    gb = torch.empty_like(qb)
+    for r in range(3):
+        bwd(gb, db, qb, ob, lb, Bb, Tb, C, NH, c)
+        torch.cuda.synchronize()
+        dqkv.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dqkv, ref), f"replay {r} after growth differs from the eager result"

@@ -1,11 +1,10 @@
 """bf16 fused path (bf16 tensors, fp32 accumulation) against the fp64 oracle
 run on the same bf16-rounded inputs, element by element
 (|gpu - oracle| <= 2e-2 + 2e-2 |oracle|)."""
-import numpy as np
 import pytest
 import torch
 
-from helpers import assert_close, gpu_fwd_bwd, head_view
+from helpers import LONG_CONTEXT_HEADS, assert_close, check_workload, gpu_fwd_bwd
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -62,29 +61,15 @@ def test_small_workloads_in_bf16(la, oracle_mod, key):
     assert_close(dqkv, rd, "bf16", "dqkv")
 
 
-def _sampled_heads(la, oracle_mod, w, heads, dtype="bf16"):
-    qkv, dout = workload_inputs(w, dtype)
-    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
-    for b, h in heads:
-        qs = oracle_mod.head_slice(qkv, b, h, w.NH, packed=True)
-        ds = oracle_mod.head_slice(dout, b, h, w.NH, packed=False)
-        ro, rl = oracle_mod.forward(qs, 1, w.causal)
-        rd = oracle_mod.backward(qs, ds, 1, w.causal)
-        assert_close(head_view(out, b, h, w.NH, False), ro, dtype, f"out head {(b, h)}")
-        assert_close(lse[b:b + 1, h:h + 1].numpy(), rl, dtype, f"lse head {(b, h)}")
-        assert_close(head_view(dqkv, b, h, w.NH, True), rd, dtype, f"dqkv head {(b, h)}")
-
-
-def test_gpt2_layer_bf16_sampled_heads(la, oracle_mod):
+def test_gpt2_layer_bf16_all_heads(la, oracle_mod):
     w = WORKLOADS[3]
-    _case(f"bf16 run of workload 3, sampled heads: {w.label()}")
-    _sampled_heads(la, oracle_mod, w, [(0, 0), (4, 6), (7, 11)])
+    check_workload(la, oracle_mod, w, "bf16", None,
+                   f"bf16 run of workload 3, every head: {w.label()}")
 
 
-def test_vit_workload_sampled_heads(la, oracle_mod):
+def test_vit_workload_all_heads(la, oracle_mod):
     w = WORKLOADS[4]
-    _case(f"bf16 workload 4, sampled heads: {w.label()}")
-    _sampled_heads(la, oracle_mod, w, [(0, 0), (17, 3), (64, 11), (127, 5), (127, 11)])
+    check_workload(la, oracle_mod, w, "bf16", None, f"bf16 workload 4, every head: {w.label()}")
 
 
 def test_partial_deal_round(la, oracle_mod):
@@ -102,10 +87,10 @@ def test_partial_deal_round(la, oracle_mod):
     assert_close(dqkv, rd, "bf16", "dqkv")
 
 
-def test_long_context_sampled_heads(la, oracle_mod):
+def test_long_context_eight_heads(la, oracle_mod):
     w = WORKLOADS[5]
-    _case(f"bf16 workload 5, sampled heads: {w.label()}")
-    _sampled_heads(la, oracle_mod, w, [(0, 0), (0, 13)])
+    check_workload(la, oracle_mod, w, "bf16", LONG_CONTEXT_HEADS,
+                   f"bf16 workload 5, 8 of 16 heads: {w.label()}")
 
 
 def test_deterministic_and_causal(la):

@@ -4,7 +4,7 @@ oracle run on the same fp16-rounded inputs, element by element
 import pytest
 import torch
 
-from helpers import assert_close, gpu_fwd_bwd, head_view
+from helpers import LONG_CONTEXT_HEADS, assert_close, check_workload, gpu_fwd_bwd
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -59,29 +59,22 @@ def test_small_workloads_in_f16(la, oracle_mod, key):
     assert_close(dqkv, rd, "f16", "dqkv")
 
 
-def _sampled_heads(la, oracle_mod, w, heads):
-    qkv, dout = workload_inputs(w, "f16")
-    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
-    for b, h in heads:
-        qs = oracle_mod.head_slice(qkv, b, h, w.NH, packed=True)
-        ds = oracle_mod.head_slice(dout, b, h, w.NH, packed=False)
-        ro, rl = oracle_mod.forward(qs, 1, w.causal)
-        rd = oracle_mod.backward(qs, ds, 1, w.causal)
-        assert_close(head_view(out, b, h, w.NH, False), ro, "f16", f"out head {(b, h)}")
-        assert_close(lse[b:b + 1, h:h + 1].numpy(), rl, "f16", f"lse head {(b, h)}")
-        assert_close(head_view(dqkv, b, h, w.NH, True), rd, "f16", f"dqkv head {(b, h)}")
-
-
-def test_gpt2_layer_f16_sampled_heads(la, oracle_mod):
+def test_gpt2_layer_f16_all_heads(la, oracle_mod):
     w = WORKLOADS[3]
-    _case(f"f16 run of workload 3, sampled heads: {w.label()}")
-    _sampled_heads(la, oracle_mod, w, [(0, 0), (4, 6), (7, 11)])
+    check_workload(la, oracle_mod, w, "f16", None,
+                   f"f16 run of workload 3, every head: {w.label()}")
 
 
-def test_long_context_f16_sampled_heads(la, oracle_mod):
+def test_vit_f16_all_heads(la, oracle_mod):
+    w = WORKLOADS[4]
+    check_workload(la, oracle_mod, w, "f16", None,
+                   f"f16 run of workload 4, every head: {w.label()}")
+
+
+def test_long_context_f16_eight_heads(la, oracle_mod):
     w = WORKLOADS[5]
-    _case(f"f16 run of workload 5, sampled heads: {w.label()}")
-    _sampled_heads(la, oracle_mod, w, [(0, 0), (0, 13)])
+    check_workload(la, oracle_mod, w, "f16", LONG_CONTEXT_HEADS,
+                   f"f16 run of workload 5, 8 of 16 heads: {w.label()}")
 
 
 def test_deterministic_and_causal(la):

@@ -2,11 +2,10 @@
 (|gpu - oracle| <= 1e-5 + 1e-4 |oracle|), plus GPU-only invariants."""
 import sys
 
-import numpy as np
 import pytest
 import torch
 
-from helpers import assert_close, gpu_fwd_bwd, head_view
+from helpers import assert_close, gpu_fwd_bwd
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -66,22 +65,19 @@ def test_ragged_shapes(la, oracle_mod, shape, causal):
     assert_close(dqkv, rd, "f32", "dqkv")
 
 
-def test_gpt2_layer_sampled_heads(la, oracle_mod):
+def test_gpt2_layer_all_heads(la, oracle_mod):
     """The benchmark's workload (B8 T1024 C768 NH12, causal, fp32) in the
-    benchmark's launch configuration; the oracle runs on 4 sampled heads and
-    every element of those heads is compared."""
+    benchmark's launch configuration; every element of every head is
+    compared with the oracle."""
     w = WORKLOADS[3]
-    _case(f"f32 workload 3 sampled heads: {w.label()}")
+    _case(f"f32 workload 3, every head: {w.label()}")
     qkv, dout = workload_inputs(w)
     out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, w.NH, w.causal)
-    for b, h in [(0, 0), (3, 7), (5, 11), (7, 4)]:
-        qs = oracle_mod.head_slice(qkv, b, h, w.NH, packed=True)
-        ds = oracle_mod.head_slice(dout, b, h, w.NH, packed=False)
-        ro, rl = oracle_mod.forward(qs, 1, True)
-        rd = oracle_mod.backward(qs, ds, 1, True)
-        assert_close(head_view(out, b, h, w.NH, False), ro, "f32", f"out head {(b, h)}")
-        assert_close(lse[b:b + 1, h:h + 1].numpy(), rl, "f32", f"lse head {(b, h)}")
-        assert_close(head_view(dqkv, b, h, w.NH, True), rd, "f32", f"dqkv head {(b, h)}")
+    ro, rl = oracle_mod.forward(qkv, w.NH, True)
+    rd = oracle_mod.backward(qkv, dout, w.NH, True)
+    assert_close(out, ro, "f32", "out")
+    assert_close(lse, rl, "f32", "lse")
+    assert_close(dqkv, rd, "f32", "dqkv")
 
 
 def test_deterministic(la):
@@ -152,11 +148,11 @@ def test_respects_torch_stream(la, oracle_mod):
 
 
 def test_stages_equal_fused_backward(la):
-    """attn_backward (fp32) is the pre-pass, dK/dV with the dS block store
-    and dQ from it: the three stage calls give the same bits.  The other
-    order (dQ recomputing S and dP, writing D, then dK/dV) agrees up to fp32
-    summation order, and dK/dV from the pre-pass D gives the same dk and dv
-    bits with or without the dS store."""
+    """attn_backward (fp32) is the dQ kernel that recomputes S and dP and
+    writes D, then dK/dV: the two stage calls give the same bits.  The dS
+    block store order (pre-pass D, dK/dV writing dS, dQ from dS) agrees up
+    to fp32 summation order, and its dK/dV gives the same dk and dv bits as
+    the plain dK/dV kernel run from the same D."""
     B, T, C, NH = 2, 190, 256, 4
     _case(f"f32 stages B{B} T{T} C{C} NH{NH}")
     qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=33)
@@ -164,23 +160,23 @@ def test_stages_equal_fused_backward(la):
     out, lse = la.forward(qkv, NH, True)
     ref = la.backward(dout, qkv, out, lse, NH, True)
     nan = float("nan")
+    D2 = torch.full((B, NH, T), nan, device="cuda")
+    g2 = torch.full_like(qkv, nan)
+    la.attn_backward_dq(g2, D2, dout, qkv, out, lse, B, T, C, NH, 1)
+    la.attn_backward_dkdv(g2, dout, qkv, lse, D2, B, T, C, NH, 1)
     D = torch.full((B, NH, T), nan, device="cuda")
     dS = torch.full((la.attn_backward_ds_bytes(B, T, C, NH, 1) // 4,), nan, device="cuda")
     g = torch.full_like(qkv, nan)
     la.attn_backward_preprocess(D, dout, out, B, T, C, NH)
     la.attn_backward_dkdv_ds(g, dS, dout, qkv, lse, D, B, T, C, NH, 1)
     la.attn_backward_dq_ds(g, dS, qkv, B, T, C, NH, 1)
-    D2 = torch.full((B, NH, T), nan, device="cuda")
-    g2 = torch.full_like(qkv, nan)
-    la.attn_backward_dq(g2, D2, dout, qkv, out, lse, B, T, C, NH, 1)
-    la.attn_backward_dkdv(g2, dout, qkv, lse, D2, B, T, C, NH, 1)
     g3 = torch.full_like(qkv, nan)
     la.attn_backward_dkdv(g3, dout, qkv, lse, D, B, T, C, NH, 1)
     torch.cuda.synchronize()
-    assert torch.equal(g, ref)
+    assert torch.equal(g2, ref)
     torch.testing.assert_close(D2, D, rtol=1e-5, atol=1e-5)
-    torch.testing.assert_close(g2, ref, rtol=1e-5, atol=1e-5)
-    assert torch.equal(g3[:, :, C:], ref[:, :, C:])
+    torch.testing.assert_close(g, ref, rtol=1e-5, atol=1e-5)
+    assert torch.equal(g3[:, :, C:], g[:, :, C:])
 
 
 RECOMPUTE_SHAPES = [(1, 1, 64, 4), (2, 65, 128, 2), (1, 100, 96, 3), (1, 129, 512, 4),
@@ -190,9 +186,8 @@ RECOMPUTE_SHAPES = [(1, 1, 64, 4), (2, 65, 128, 2), (1, 100, 96, 3), (1, 129, 51
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", RECOMPUTE_SHAPES)
 def test_recompute_stages_ragged(la, oracle_mod, shape, causal):
-    """The dQ kernel that recomputes S and dP (the fused backward's path for
-    shapes whose dS block store would exceed its cap), then dK/dV, against
-    the oracle."""
+    """The two stage calls the fused fp32 backward runs (the dQ kernel that
+    recomputes S and dP and writes D, then dK/dV), against the oracle."""
     B, T, C, NH = shape
     _case(f"f32 recompute stages B{B} T{T} C{C} NH{NH} causal={causal}")
     qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=200 + T)

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/libattn.h"
 #include "common.hpp"
@@ -101,11 +102,18 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
-// ---- per-device grow-only workspace (D for the backward) ----
+// ---- per-device grow-only workspace (D for the backward, decode partials,
+// LayerNorm column partials) ----
+// A call that needs more than the current buffer allocates a larger one and
+// keeps the old one on a retired list instead of freeing it: work queued
+// earlier on any stream, or a HIP graph captured earlier, may still read or
+// write the old buffer.  Only attn_release frees buffers.  Growing therefore
+// never synchronises the device.
 constexpr int kMaxDevices = 64;
 std::mutex g_ws_mutex;
 void* g_ws_ptr[kMaxDevices] = {};
 size_t g_ws_bytes[kMaxDevices] = {};
+std::vector<void*> g_ws_retired[kMaxDevices];
 
 int workspace(size_t bytes, float** out) {
     // ATTN_TEST_FAIL_ALLOC=1 makes the allocation fail before any HIP call,
@@ -118,29 +126,24 @@ int workspace(size_t bytes, float** out) {
     if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EHIP, "device id %d out of range", dev);
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     if (g_ws_bytes[dev] < bytes) {
-        if (g_ws_ptr[dev]) {
-            // the old buffer may still be read by queued work on any stream
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return fail(ATTN_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
-            (void)hipFree(g_ws_ptr[dev]);
-            g_ws_ptr[dev] = nullptr;
-            g_ws_bytes[dev] = 0;
-        }
+        // grow by at least half, so a slowly rising shape retires few buffers
+        const size_t want = bytes > g_ws_bytes[dev] + g_ws_bytes[dev] / 2
+                                ? bytes : g_ws_bytes[dev] + g_ws_bytes[dev] / 2;
         void* p = nullptr;
-        e = hipMalloc(&p, bytes);
-        if (e != hipSuccess) return fail(ATTN_EHIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+        e = hipMalloc(&p, want);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();   // a failed allocation must not surface at the next launch
+            return fail(ATTN_EHIP, "hipMalloc(%zu): %s", want, hipGetErrorString(e));
+        }
+        if (g_ws_ptr[dev]) g_ws_retired[dev].push_back(g_ws_ptr[dev]);
         g_ws_ptr[dev] = p;
-        g_ws_bytes[dev] = bytes;
+        g_ws_bytes[dev] = want;
     }
     *out = (float*)g_ws_ptr[dev];
     return ATTN_OK;
 }
 
 size_t nbytes(long long elems, size_t elem) { return (size_t)elems * elem; }
-
-// Largest dS block store the fused fp32 backward keeps in the workspace;
-// larger shapes run the dQ kernel that recomputes S and dP instead.
-constexpr size_t kMaxDsStoreBytes = (size_t)4 << 30;
 
 }  // namespace
 
@@ -158,10 +161,14 @@ void attn_release(void) {
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) cur = -1;
     for (int d = 0; d < kMaxDevices; ++d) {
-        if (!g_ws_ptr[d]) continue;
-        if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_ws_ptr[d]);
+        if (!g_ws_ptr[d] && g_ws_retired[d].empty()) continue;
+        if (hipSetDevice(d) == hipSuccess) {
+            if (g_ws_ptr[d]) (void)hipFree(g_ws_ptr[d]);
+            for (void* p : g_ws_retired[d]) (void)hipFree(p);
+        }
         g_ws_ptr[d] = nullptr;
         g_ws_bytes[d] = 0;
+        g_ws_retired[d].clear();
     }
     if (cur >= 0) (void)hipSetDevice(cur);
 }
@@ -187,25 +194,12 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
                         {lse, nbytes(BT * NH, 4), "lse"}};
     int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
     if (rc) return rc;
-    const attn::Shape s = shape_of(B, T, C, NH, causal);
-    const size_t dbytes = (nbytes(BT * NH, 4) + 255) & ~(size_t)255;
-    const size_t dsbytes = attn::ds_store_floats(s) * 4;
+    // the recompute order: dQ (recomputes S and dP, forms D = dO . O per
+    // row), then dK/dV (reads D); the only workspace is D, B*NH*T floats
     float* D = nullptr;
-    if (dsbytes <= kMaxDsStoreBytes) {
-        // D pre-pass, dK/dV writing dS, dQ from dS; if the store cannot be
-        // allocated, the recompute order below needs only D
-        rc = workspace(dbytes + dsbytes, &D);
-        if (rc == ATTN_OK) {
-            float* dS = D + dbytes / 4;
-            hipError_t e = attn::launch_prepass_f32(D, dout, out, s, g_stream);
-            if (e == hipSuccess) e = attn::launch_dkdv_ds_f32(dqkv, dS, dout, qkv, lse, D, s, g_stream);
-            if (e == hipSuccess) e = attn::launch_dq_ds_f32(dqkv, dS, qkv, s, g_stream);
-            return launched(e, "attn_backward launch");
-        }
-        (void)hipGetLastError();   // a failed hipMalloc must not surface at the next launch
-    }
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
     hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward launch");

@@ -34,11 +34,13 @@
 //  * the forward raises a row's running maximum only when a tile's maximum
 //    exceeds it by more than 2^kLazyMax (log2 domain), as the 16-bit forward
 //    does, and folds the scale into the exponent's FMA;
-//  * the fused backward runs dK/dV first and lets it store dS, so that the
-//    dQ kernel (bwd_dq_ds_f32_tile) performs one contraction instead of
-//    three: on the fp32 matrix cores recomputing S and dP costs more than
-//    writing dS once and reading it back.  bwd_dq_f32_tile (recompute, D
-//    fused) serves shapes whose dS store would be too large.
+//  * the fused backward (attn_backward) runs the dQ kernel that recomputes
+//    S and dP and also forms D = dO . O (bwd_dq_f32_tile), then dK/dV,
+//    keeping memory O(B*NH*T).  A second order, for callers that own an
+//    O(T^2) buffer, lets dK/dV store dS (bwd_dkdv_f32_tile<HS, true>) so
+//    that the dQ kernel (bwd_dq_ds_f32_tile) performs one contraction
+//    instead of three: on the fp32 matrix cores recomputing S and dP costs
+//    more than writing dS once and reading it back.
 #include "common.hpp"
 
 namespace attn {

@@ -22,6 +22,7 @@
 // wholly above the diagonal and treat entries above the diagonal as 0, so
 // only the lower triangle of an att argument is ever read.
 #include "common.hpp"
+#include "tiles.hpp"
 
 namespace attn {
 namespace {
@@ -39,9 +40,10 @@ __device__ __forceinline__ P* wave_uniform(P* p) {
     return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 // apply_kernel: 16-row output blocks per wave, and output rows per workgroup
-// (the launchers size the grid with the same constant)
-constexpr int kApplyRB = 1;
-constexpr int kApplyRows = 4 * 16 * kApplyRB;
+// (tiles.hpp: the launchers size the grid and the kernel decodes its tile
+// with the same functions)
+using tiles::kApplyRB;
+using tiles::kApplyRows;
 
 struct Lane {
     int tid, w, l, r16, g;
@@ -201,7 +203,7 @@ template <int HS, bool TRANS>
 __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
                                                          const float* __restrict__ A,
                                                          const float* __restrict__ Bm, int T,
-                                                         int NH, int causal, size_t ldb,
+                                                         int NH, int BH, int causal, size_t ldb,
                                                          size_t ldc, size_t batch_b,
                                                          size_t batch_c) {
     constexpr int RB = kApplyRB;                 // 16-row output blocks per wave
@@ -219,16 +221,15 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ Cm,
     __shared__ float As[AROWS * LDA];
     __shared__ float Bs[kTile * LDB];
     const Lane L;
-    const int nrt = (T + BR - 1) / BR;
     const int nkt = (T + kTile - 1) / kTile;
     // causal: heaviest row tiles first (op(A) = A: row tile rt sees rt + 1
     // blocks; A^T: nkt - rt), heads fastest, so that the last workgroups to
     // start are the lightest (forward 410 -> 380 us, backward 693 -> 595 us on
     // the GPT-2 layer against row tiles in order)
-    const int nbh = gridDim.x / nrt;
-    const int rank = blockIdx.x / nbh;
-    const int bh = blockIdx.x - rank * nbh;
-    const int rt = (causal && !TRANS) ? nrt - 1 - rank : rank;
+    const tiles::TileId tid = tiles::apply_tile(blockIdx.x, BH, T, causal && !TRANS);
+    if (!tid.valid) return;   // whole workgroup: no barrier is reached
+    const int bh = tid.bh;
+    const int rt = tid.rt;
     const int b = bh / NH, h = bh - (bh / NH) * NH;
     const float* Ah = A + (size_t)bh * T * T;
     const float* bb = Bm + (size_t)b * batch_b + (size_t)h * HS;
@@ -594,9 +595,10 @@ hipError_t fwd_hs(float* out, float* preatt, float* att, const float* qkv, const
     const float scale = (float)(1.0 / sqrt((double)HS));
     e = launch_softmax_rows(att, preatt, s.T, rows, s.causal, scale * kLog2e, st);
     if (e != hipSuccess) return e;
-    const unsigned ga = (unsigned)(BH * ((s.T + kApplyRows - 1) / kApplyRows));
-    hipLaunchKernelGGL((apply_kernel<HS, false>), dim3(ga), dim3(kThreads), 0, st, out, att,
-                       qkv + 2 * s.C, s.T, s.NH, s.causal, C3, (size_t)s.C, bstride,
+    const long long ga = tiles::apply_grid(BH, s.T);
+    if (ga < 1 || ga > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((apply_kernel<HS, false>), dim3((unsigned)ga), dim3(kThreads), 0, st, out, att,
+                       qkv + 2 * s.C, s.T, s.NH, (int)BH, s.causal, C3, (size_t)s.C, bstride,
                        (size_t)s.T * s.C);
     return hipGetLastError();
 }
@@ -622,18 +624,20 @@ hipError_t bwd_hs(float* dqkv, float* dpreatt, float* datt, const float* dout, c
     const float scale = (float)(1.0 / sqrt((double)HS));
     e = launch_softmax_bwd_rows(dpreatt, att, datt, s.T, rows, s.causal, scale, st);
     if (e != hipSuccess) return e;
-    const unsigned g = (unsigned)(BH * ((s.T + kApplyRows - 1) / kApplyRows));
+    const long long gl = tiles::apply_grid(BH, s.T);
+    if (gl < 1 || gl > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const unsigned g = (unsigned)gl;
     // dv = att^T dO
     hipLaunchKernelGGL((apply_kernel<HS, true>), dim3(g), dim3(kThreads), 0, st, dqkv + 2 * C, att,
-                       dout, s.T, s.NH, s.causal, C, C3, bo, bq);
+                       dout, s.T, s.NH, (int)BH, s.causal, C, C3, bo, bq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dq = dpreatt K
     hipLaunchKernelGGL((apply_kernel<HS, false>), dim3(g), dim3(kThreads), 0, st, dqkv, dpreatt,
-                       qkv + C, s.T, s.NH, s.causal, C3, C3, bq, bq);
+                       qkv + C, s.T, s.NH, (int)BH, s.causal, C3, C3, bq, bq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dk = dpreatt^T Q
     hipLaunchKernelGGL((apply_kernel<HS, true>), dim3(g), dim3(kThreads), 0, st, dqkv + C, dpreatt,
-                       qkv, s.T, s.NH, s.causal, C3, C3, bq, bq);
+                       qkv, s.T, s.NH, (int)BH, s.causal, C3, C3, bq, bq);
     return hipGetLastError();
 }
 
