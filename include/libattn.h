@@ -111,6 +111,24 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   int B, int T, int C, int NH, int causal);
 
 /*
+ * attn_backward without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments, kernels and result (bit for bit)
+ * as attn_backward; its D scratch (B*NH*T floats) lives in a fixed device
+ * array of 4194304 floats (16 MiB) that each GPU the library runs on holds
+ * from library load until the process ends.  Shapes with B*NH*T above
+ * that return ATTN_EINVAL before any HIP call.  The first call on a device
+ * looks up the array's address there (hipGetSymbolAddress); make that first
+ * call outside graph capture.  Every call on one GPU shares its array, so
+ * calls that overlap in time on one GPU (different streams or threads)
+ * race: serialise them, e.g. on one stream.  The array holds no state a
+ * call depends on: D is written in full before it is read.
+ */
+int attn_backward_noalloc(float* dqkv, const float* dout, const float* qkv,
+                          const float* out, const float* lse,
+                          int B, int T, int C, int NH, int causal);
+
+/*
  * The stages of attn_backward, for callers that want to time, order or
  * overlap them, or to own the D buffer (these calls allocate nothing):
  *   attn_backward_dq: writes D (B,NH,T) fp32 = dout . out per row and head

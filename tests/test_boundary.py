@@ -63,7 +63,8 @@ def call(name, nptr, B, T, C, NH, causal, override=None):
     return rc, lib.attn_last_error().decode()
 
 
-ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_forward_bf16", 3),
+ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_backward_noalloc", 5),
+         ("attn_forward_bf16", 3),
          ("attn_backward_bf16", 5), ("attn_forward_materialized", 4),
          ("attn_backward_materialized", 6),
          ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
@@ -346,3 +347,12 @@ def test_forced_workspace_failure_layernorm_backward():
     assert res.returncode == 0, res.stderr
     rc, msg = res.stdout.split(" ", 1)
     assert int(rc) == la.ATTN_EHIP and "forced" in msg
+
+
+def test_noalloc_rejects_shapes_past_its_fixed_scratch():
+    """attn_backward_noalloc holds D (B*NH*T floats) in a fixed array of
+    4194304 floats: a larger shape is refused before any HIP call."""
+    rc, msg = call("attn_backward_noalloc", 5, 1100, 1024, 768, 12, 1)
+    assert rc == la.ATTN_EINVAL and "fixed scratch" in msg
+    rc, msg = call("attn_backward_noalloc", 5, 342, 1024, 768, 12, 1)   # 4202496 rows
+    assert rc == la.ATTN_EINVAL and "fixed scratch" in msg

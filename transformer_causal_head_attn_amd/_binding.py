@@ -24,7 +24,7 @@ ATTN_EUNSUPPORTED = -2
 ATTN_EHIP = -3
 
 EXPORTS = (
-    "attn_forward", "attn_backward",
+    "attn_forward", "attn_backward", "attn_backward_noalloc",
     "attn_backward_preprocess", "attn_backward_dkdv", "attn_backward_dq",
     "attn_backward_ds_bytes", "attn_backward_dkdv_ds", "attn_backward_dq_ds",
     "attn_forward_bf16", "attn_backward_bf16",
@@ -64,6 +64,7 @@ def load(path: str | None = None):
         vp, i = ctypes.c_void_p, ctypes.c_int
         for name, nptr in (("attn_forward", 3), ("attn_forward_bf16", 3),
                            ("attn_backward", 5), ("attn_backward_bf16", 5),
+                           ("attn_backward_noalloc", 5),
                            ("attn_forward_materialized", 4),
                            ("attn_backward_materialized", 6),
                            ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
@@ -144,6 +145,14 @@ def attn_forward(out, lse, qkv, B, T, C, NH, causal) -> None:
 def attn_backward(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
     f = torch.float32
     _call("attn_backward", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_noalloc(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_backward_noalloc", _check(dqkv, "dqkv", f, B * T * 3 * C),
           _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
           _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
           *_dims(B, T, C, NH, causal))

@@ -145,6 +145,37 @@ int workspace(size_t bytes, float** out) {
 
 size_t nbytes(long long elems, size_t elem) { return (size_t)elems * elem; }
 
+// ---- fixed scratch for attn_backward_noalloc ----
+// A file-scope device array of kNoAllocScratchFloats floats: every GPU the
+// library runs on holds its own copy from module load until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory, so kernels are only ever handed the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchFloats = (size_t)4 << 20;   // 16 MiB: B*NH*T <= 4194304
+__device__ __align__(256) float scratch[kNoAllocScratchFloats];
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_device(float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EHIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(ATTN_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = (float*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +234,31 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
     hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward launch");
+}
+
+int attn_backward_noalloc(float* dqkv, const float* dout, const float* qkv, const float* out,
+                          const float* lse, int B, int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {out, nbytes(BT * C, 4), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    if ((unsigned long long)BT * NH > kNoAllocScratchFloats)
+        return fail(ATTN_EINVAL,
+                    "attn_backward_noalloc: B*NH*T = %lld exceeds the fixed scratch of %zu floats",
+                    BT * NH, kNoAllocScratchFloats);
+    // D lives in the fixed scratch: written in full by the dQ kernel before
+    // the dK/dV kernel reads it, so nothing needs clearing
+    float* D = nullptr;
+    rc = scratch_for_device(&D);
+    if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
+    return launched(e, "attn_backward_noalloc launch");
 }
 
 uint64_t attn_backward_ds_bytes(int B, int T, int C, int NH, int causal) {
