@@ -392,6 +392,75 @@ def run_decode(la, torch, w, dtype, steps, warmup):
             "bytes_note": "compulsory bytes: K and V of every head once, q row and out"}
 
 
+def _time_call(torch, fn, steps, warmup_ms):
+    """Average ms of `fn` over `steps` calls between HIP events on the current
+    stream, after untimed calls for `warmup_ms`."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_splitkv(la, torch, steps=20, warmup_ms=100.0):
+    """The split-KV forward and the split backward against the plain ones
+    (bf16) on one GPU's share of the long-context workload under an 8-way
+    head split (2 heads of T = 8192, hs = 128: 128 query tiles for the plain
+    forward grid) and on the whole workload (16 heads).  Useful flops: 4 (fwd)
+    and 10 (bwd) * hs * pairs * B * NH."""
+    from workloads import WORKLOADS, workload_inputs
+    w = WORKLOADS[5]
+    qkv_full, dout_full = workload_inputs(w, "bf16")
+    res = []
+    for nh in (2, w.NH):
+        C = nh * w.hs
+        qkv = torch.cat([qkv_full[:, :, p * w.C:p * w.C + C] for p in range(3)], dim=2).contiguous().cuda()
+        dout = dout_full[:, :, :C].contiguous().cuda()
+        out = torch.empty((w.B, w.T, C), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, nh, w.T), device="cuda")
+        dqkv = torch.empty_like(qkv)
+        ffl = 4 * w.hs * w.pairs * w.B * nh
+        bfl = 10 * w.hs * w.pairs * w.B * nh
+        auto = la.attn_forward_splitkv_chunk(w.B, w.T, C, nh, 1)
+        rec = {"workload": f"long-context B{w.B} T{w.T} NH{nh} hs{w.hs} causal bf16",
+               "auto_chunk": auto}
+
+        def put(name, f_ms, b_ms):
+            rec[name] = {"fwd_us": round(f_ms * 1e3, 2), "bwd_us": round(b_ms * 1e3, 2),
+                         "fwd_frac_mfma_peak": round(ffl / (f_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                         "bwd_frac_mfma_peak": round(bfl / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                         "step_tflops": round((ffl + bfl) / ((f_ms + b_ms) * 1e-3) / 1e12, 1)}
+
+        la.attn_forward_bf16(out, lse, qkv, w.B, w.T, C, nh, 1)
+        f_ms = _time_call(torch, lambda: la.attn_forward_bf16(out, lse, qkv, w.B, w.T, C, nh, 1),
+                          steps, warmup_ms)
+        b_ms = _time_call(torch, lambda: la.attn_backward_bf16(dqkv, dout, qkv, out, lse, w.B, w.T,
+                                                                C, nh, 1), steps, warmup_ms)
+        put("plain", f_ms, b_ms)
+        for chunk in sorted({auto, 1024, 2048, 4096}):
+            if chunk >= w.T:
+                continue
+            nf = la.attn_forward_splitkv_bytes(w.B, w.T, C, nh, 1, chunk) // 4
+            nb = la.attn_backward_splitkv_bytes(w.B, w.T, C, nh, 1, chunk) // 4
+            wf = torch.empty((max(nf, 4),), device="cuda")
+            wb = torch.empty((max(nb, 4),), device="cuda")
+            f_ms = _time_call(torch, lambda: la.attn_forward_splitkv_bf16(
+                out, lse, qkv, wf, w.B, w.T, C, nh, 1, chunk), steps, warmup_ms)
+            b_ms = _time_call(torch, lambda: la.attn_backward_splitkv_bf16(
+                dqkv, dout, qkv, out, lse, wb, w.B, w.T, C, nh, 1, chunk), steps, warmup_ms)
+            put(f"chunk{chunk}", f_ms, b_ms)
+            del wf, wb
+        res.append(rec)
+    return res
+
+
 def run_layernorm(la, torch, N, C, dtype, steps=50, warmup=100):
     """Time the LayerNorm forward and backward over N rows of C (the GPT-2
     layer's activations when N = B*T = 8192, C = 768).  Both are HBM-bound:
@@ -662,6 +731,9 @@ def main():
         line["hbm_copy"] = hbm_copy(torch)
         line["layernorm"] = [run_layernorm(la, torch, w.B * w.T, w.C, "f32"),
                              run_layernorm(la, torch, w.B * w.T, w.C, "bf16")]
+
+    if not args.no_extra:
+        line["splitkv_forward"] = run_splitkv(la, torch)
 
     if not args.no_extra:
         line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),

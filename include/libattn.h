@@ -201,6 +201,66 @@ int attn_backward_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t
                             int B, int T, int C, int NH, int causal);
 
 /*
+ * Split-KV forward (16-bit path), for shapes whose plain forward grid leaves
+ * the chip under-filled (few heads per GPU at long T: e.g. 2 heads of
+ * T = 8192 give 128 query tiles for 256 compute units).  The keys each
+ * query tile sees are split into chunks of kv_chunk keys, one workgroup per
+ * (query tile, chunk); each writes its output normalised over its own keys
+ * and that range's log-sum-exp, and a merge forms, per row,
+ * L = log sum_p exp(lse_p), out = sum_p exp(lse_p - L) o_p: the rescale the
+ * running softmax applies from one key block to the next ("Umakini wa
+ * kujitegemea, kerneli za CUDA na FlashAttention", the FlashAttention part),
+ * applied across workgroups.  Same out and lse as attn_forward_bf16 / _f16
+ * up to rounding (the partial outputs stay fp32; out is rounded once).
+ *   kv_chunk: keys per chunk, a positive multiple of 64, or 0 for the
+ *       library's choice (attn_forward_splitkv_chunk: the longest
+ *       power-of-two number of 64-key tiles that keeps a workgroup per
+ *       compute unit; T rounded up to 64, i.e. no split, when the unsplit
+ *       grid already does).  Returns the chunk in keys or a negative status.
+ *   work: caller-owned device memory of attn_forward_splitkv_bytes bytes
+ *       (fp32 partial outputs and log-sum-exps of every chunk, layout
+ *       internal); 0 bytes when the chunk covers all keys, in which case
+ *       the plain forward runs and work is not touched (it must still be a
+ *       valid, aligned, non-null pointer).  attn_forward_splitkv_bytes
+ *       returns 0 also for arguments the other calls would reject.
+ * Nothing is allocated.  Errors as for attn_forward_bf16, plus ATTN_EINVAL
+ * for a kv_chunk that is negative or not a multiple of 64.
+ */
+int attn_forward_splitkv_chunk(int B, int T, int C, int NH, int causal);
+uint64_t attn_forward_splitkv_bytes(int B, int T, int C, int NH, int causal, int kv_chunk);
+int attn_forward_splitkv_bf16(uint16_t* out, float* lse, const uint16_t* qkv, float* work,
+                              int B, int T, int C, int NH, int causal, int kv_chunk);
+int attn_forward_splitkv_f16(uint16_t* out, float* lse, const uint16_t* qkv, float* work,
+                             int B, int T, int C, int NH, int causal, int kv_chunk);
+
+/*
+ * Split backward (16-bit path), the counterpart of the split-KV forward for
+ * under-filled grids.  The dQ kernel's keys and the dK/dV kernel's queries
+ * are split into chunks of kv_chunk (keys, resp. query rows), one workgroup
+ * per (tile, chunk); each writes its fp32 partial sum of dq, resp. dk and
+ * dv (the sums over key or query ranges of the analytic backward of
+ * attention_backward_cpu in llm.c dev/cuda/attention_backward.cu, with the
+ * softmax step of its kernel 7), and a last kernel adds the partials of
+ * every row in a fixed order and rounds once to the 16-bit type, so the
+ * result is deterministic.  Same dqkv as attn_backward_bf16 / _f16 up to
+ * rounding.
+ *   kv_chunk: as for attn_forward_splitkv_bf16 (0: the library's choice).
+ *   work: caller-owned device memory of attn_backward_splitkv_bytes bytes:
+ *       D (B*NH*T floats, rounded up to 64) and, when the chunk splits the
+ *       keys, fp32 partial sums (3*ceil(T/kv_chunk)*B*T*C floats).  Without
+ *       a split the call runs attn_backward_dq_bf16 / _f16 and
+ *       attn_backward_dkdv_bf16 / _f16 with D in work.
+ * Nothing is allocated.  Errors as for attn_forward_splitkv_bf16.
+ */
+uint64_t attn_backward_splitkv_bytes(int B, int T, int C, int NH, int causal, int kv_chunk);
+int attn_backward_splitkv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                               const uint16_t* out, const float* lse, float* work,
+                               int B, int T, int C, int NH, int causal, int kv_chunk);
+int attn_backward_splitkv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                              const uint16_t* out, const float* lse, float* work,
+                              int B, int T, int C, int NH, int causal, int kv_chunk);
+
+/*
  * The same fused forward, backward and backward stages with IEEE half
  * (fp16) tensors, passed as uint16_t bit patterns: the section names FP16
  * beside BF16 for mixed-precision training.  Same kernels, fp16 matrix-core

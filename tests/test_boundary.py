@@ -356,3 +356,59 @@ def test_noalloc_rejects_shapes_past_its_fixed_scratch():
     assert rc == la.ATTN_EINVAL and "fixed scratch" in msg
     rc, msg = call("attn_backward_noalloc", 5, 342, 1024, 768, 12, 1)   # 4202496 rows
     assert rc == la.ATTN_EINVAL and "fixed scratch" in msg
+
+
+def _splitkv(name, B, T, C, NH, causal, kv_chunk, override=None):
+    lib = la.load()
+    p = ptrs(4)
+    if override:
+        for i, v in override.items():
+            p[i] = ctypes.c_void_p(v)
+    rc = getattr(lib, name)(*p, B, T, C, NH, causal, kv_chunk)
+    return rc, lib.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("name", ["attn_forward_splitkv_bf16", "attn_forward_splitkv_f16"])
+def test_splitkv_argument_errors(name):
+    for chunk in (-64, 100, 32):
+        rc, msg = _splitkv(name, 1, 8192, 256, 2, 1, chunk)
+        assert rc == la.ATTN_EINVAL and "kv_chunk" in msg
+    for i in range(4):
+        rc, msg = _splitkv(name, 1, 8192, 256, 2, 1, 2048, override={i: 0})
+        assert rc == la.ATTN_EINVAL and "NULL" in msg
+    rc, msg = _splitkv(name, 1, 8192, 96, 4, 1, 2048)
+    assert rc == la.ATTN_EUNSUPPORTED
+
+
+def test_splitkv_work_bytes():
+    lib = la.load()
+    # two heads of the long-context shape, 2048-key chunks: 4 parts of
+    # (B*T*C + B*NH*T) floats
+    B, T, C, NH = 1, 8192, 256, 2
+    assert lib.attn_forward_splitkv_bytes(B, T, C, NH, 1, 2048) == 4 * 4 * (B * T * C + B * NH * T)
+    # a ragged T: ceil(ceil(1000/64)/3) = 6 parts of 192 keys
+    assert lib.attn_forward_splitkv_bytes(2, 1000, 128, 2, 0, 192) == 6 * 4 * (2 * 1000 * 128 + 2 * 2 * 1000)
+    # a chunk covering every key: no split, no work
+    assert lib.attn_forward_splitkv_bytes(B, T, C, NH, 1, 8192) == 0
+    assert lib.attn_forward_splitkv_bytes(B, T, C, NH, 1, 1 << 20) == 0
+    # rejected arguments: 0
+    assert lib.attn_forward_splitkv_bytes(B, T, C, NH, 1, 100) == 0
+    assert lib.attn_forward_splitkv_bytes(B, T, 96, 4, 1, 2048) == 0
+
+
+def test_backward_splitkv_work_bytes_and_errors():
+    lib = la.load()
+    B, T, C, NH = 1, 8192, 256, 2
+    d = B * NH * T   # a multiple of 64 already
+    assert lib.attn_backward_splitkv_bytes(B, T, C, NH, 1, 2048) == 4 * (d + 3 * 4 * B * T * C)
+    # no split: D only (rounded up to 64 floats)
+    assert lib.attn_backward_splitkv_bytes(2, 100, 64, 4, 1, 128) == 4 * 832
+    assert lib.attn_backward_splitkv_bytes(B, T, C, NH, 1, 100) == 0
+    p = ptrs(6)
+    for name in ("attn_backward_splitkv_bf16", "attn_backward_splitkv_f16"):
+        rc = getattr(lib, name)(*p, B, T, C, NH, 1, 96)
+        assert rc == la.ATTN_EINVAL and b"kv_chunk" in lib.attn_last_error()
+        q = list(p)
+        q[5] = ctypes.c_void_p(0)
+        rc = getattr(lib, name)(*q, B, T, C, NH, 1, 2048)
+        assert rc == la.ATTN_EINVAL and b"NULL" in lib.attn_last_error()

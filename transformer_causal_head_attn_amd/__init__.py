@@ -9,7 +9,10 @@ if it cannot.
 from ._binding import (  # noqa: F401
     ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_OK, EXPORTS, LIB_PATH, AttnError,
     attn_backward, attn_backward_bf16, attn_backward_dkdv, attn_backward_dkdv_bf16,
-    attn_backward_noalloc,
+    attn_backward_noalloc, attn_forward_splitkv_chunk, attn_forward_splitkv_bytes,
+    attn_forward_splitkv_bf16, attn_forward_splitkv_f16, forward_splitkv,
+    attn_backward_splitkv_bytes, attn_backward_splitkv_bf16, attn_backward_splitkv_f16,
+    backward_splitkv,
     attn_backward_dq, attn_backward_dq_bf16, attn_backward_materialized,
     attn_backward_ds_bytes, attn_backward_dkdv_ds, attn_backward_dq_ds,
     attn_backward_preprocess, attn_backward_preprocess_bf16, attn_decode, attn_decode_bf16, attn_decode_f16,

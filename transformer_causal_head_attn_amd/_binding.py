@@ -30,6 +30,9 @@ EXPORTS = (
     "attn_forward_bf16", "attn_backward_bf16",
     "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
     "attn_forward_f16", "attn_backward_f16",
+    "attn_forward_splitkv_chunk", "attn_forward_splitkv_bytes",
+    "attn_forward_splitkv_bf16", "attn_forward_splitkv_f16",
+    "attn_backward_splitkv_bytes", "attn_backward_splitkv_bf16", "attn_backward_splitkv_f16",
     "attn_backward_preprocess_f16", "attn_backward_dkdv_f16", "attn_backward_dq_f16",
     "attn_forward_materialized", "attn_backward_materialized",
     "attn_decode", "attn_decode_bf16", "attn_decode_f16",
@@ -79,6 +82,20 @@ def load(path: str | None = None):
                      "attn_decode", "attn_decode_bf16", "attn_decode_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
+            fn.restype = i
+        lib.attn_forward_splitkv_chunk.argtypes = [i] * 5
+        lib.attn_forward_splitkv_chunk.restype = i
+        lib.attn_forward_splitkv_bytes.argtypes = [i] * 6
+        lib.attn_forward_splitkv_bytes.restype = ctypes.c_uint64
+        for name in ("attn_forward_splitkv_bf16", "attn_forward_splitkv_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 4 + [i] * 6
+            fn.restype = i
+        lib.attn_backward_splitkv_bytes.argtypes = [i] * 6
+        lib.attn_backward_splitkv_bytes.restype = ctypes.c_uint64
+        for name in ("attn_backward_splitkv_bf16", "attn_backward_splitkv_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 6 + [i] * 6
             fn.restype = i
         lib.attn_backward_ds_bytes.argtypes = [i] * 5
         lib.attn_backward_ds_bytes.restype = ctypes.c_uint64
@@ -179,6 +196,70 @@ def attn_backward_dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, causal) -> None:
           _check(D, "D", f, B * NH * T), _check(dout, "dout", f, B * T * C),
           _check(qkv, "qkv", f, B * T * 3 * C), _check(out, "out", f, B * T * C),
           _check(lse, "lse", f, B * NH * T), *_dims(B, T, C, NH, causal))
+
+
+def attn_forward_splitkv_chunk(B, T, C, NH, causal) -> int:
+    """Keys per chunk the split-KV forward picks for this shape (raises on
+    invalid arguments)."""
+    lib = load()
+    rc = lib.attn_forward_splitkv_chunk(*_dims(B, T, C, NH, causal))
+    if rc < 0:
+        raise AttnError("attn_forward_splitkv_chunk", rc, lib.attn_last_error().decode())
+    return int(rc)
+
+
+def attn_forward_splitkv_bytes(B, T, C, NH, causal, kv_chunk) -> int:
+    """Bytes of the split-KV forward's work buffer (0: no split, or invalid
+    arguments)."""
+    return int(load().attn_forward_splitkv_bytes(*_dims(B, T, C, NH, causal), int(kv_chunk)))
+
+
+def _splitkv(name, dtype, out, lse, qkv, work, B, T, C, NH, causal, kv_chunk):
+    nw = attn_forward_splitkv_bytes(B, T, C, NH, causal, kv_chunk) // 4
+    if work.numel() < nw:
+        raise ValueError(f"work has {work.numel()} floats, the split needs {nw}")
+    _call(name, _check(out, "out", dtype, B * T * C), _check(lse, "lse", torch.float32, B * NH * T),
+          _check(qkv, "qkv", dtype, B * T * 3 * C),
+          _check(work, "work", torch.float32, work.numel()),
+          *_dims(B, T, C, NH, causal), int(kv_chunk))
+
+
+def attn_forward_splitkv_bf16(out, lse, qkv, work, B, T, C, NH, causal, kv_chunk) -> None:
+    _splitkv("attn_forward_splitkv_bf16", torch.bfloat16, out, lse, qkv, work, B, T, C, NH, causal,
+             kv_chunk)
+
+
+def attn_forward_splitkv_f16(out, lse, qkv, work, B, T, C, NH, causal, kv_chunk) -> None:
+    _splitkv("attn_forward_splitkv_f16", torch.float16, out, lse, qkv, work, B, T, C, NH, causal,
+             kv_chunk)
+
+
+def attn_backward_splitkv_bytes(B, T, C, NH, causal, kv_chunk) -> int:
+    """Bytes of the split backward's work buffer (0 for invalid arguments)."""
+    return int(load().attn_backward_splitkv_bytes(*_dims(B, T, C, NH, causal), int(kv_chunk)))
+
+
+def _bwd_splitkv(name, dtype, dqkv, dout, qkv, out, lse, work, B, T, C, NH, causal, kv_chunk):
+    nw = attn_backward_splitkv_bytes(B, T, C, NH, causal, kv_chunk) // 4
+    if work.numel() < nw:
+        raise ValueError(f"work has {work.numel()} floats, the split needs {nw}")
+    _call(name, _check(dqkv, "dqkv", dtype, B * T * 3 * C), _check(dout, "dout", dtype, B * T * C),
+          _check(qkv, "qkv", dtype, B * T * 3 * C), _check(out, "out", dtype, B * T * C),
+          _check(lse, "lse", torch.float32, B * NH * T),
+          _check(work, "work", torch.float32, work.numel()),
+          *_dims(B, T, C, NH, causal), int(kv_chunk))
+
+
+def attn_backward_splitkv_bf16(dqkv, dout, qkv, out, lse, work, B, T, C, NH, causal,
+                               kv_chunk) -> None:
+    _bwd_splitkv("attn_backward_splitkv_bf16", torch.bfloat16, dqkv, dout, qkv, out, lse, work,
+                 B, T, C, NH, causal, kv_chunk)
+
+
+def attn_backward_splitkv_f16(dqkv, dout, qkv, out, lse, work, B, T, C, NH, causal,
+                              kv_chunk) -> None:
+    _bwd_splitkv("attn_backward_splitkv_f16", torch.float16, dqkv, dout, qkv, out, lse, work,
+                 B, T, C, NH, causal, kv_chunk)
 
 
 def attn_backward_ds_bytes(B, T, C, NH, causal) -> int:
@@ -370,6 +451,31 @@ def forward(qkv: torch.Tensor, NH: int, causal: bool = True):
     fn = {torch.bfloat16: attn_forward_bf16, torch.float16: attn_forward_f16}.get(qkv.dtype, attn_forward)
     fn(out, lse, qkv, B, T, C, NH, int(causal))
     return out, lse
+
+
+def forward_splitkv(qkv: torch.Tensor, NH: int, causal: bool = True, kv_chunk: int = 0):
+    """Allocate (out, lse) and the work buffer with torch and run the split-KV
+    forward (bf16 or fp16 by qkv's dtype)."""
+    B, T, C = _shape(qkv, NH)
+    out = torch.empty((B, T, C), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
+    nw = attn_forward_splitkv_bytes(B, T, C, NH, int(causal), kv_chunk) // 4
+    work = torch.empty((max(nw, 4),), dtype=torch.float32, device=qkv.device)
+    fn = {torch.bfloat16: attn_forward_splitkv_bf16, torch.float16: attn_forward_splitkv_f16}[qkv.dtype]
+    fn(out, lse, qkv, work, B, T, C, NH, int(causal), kv_chunk)
+    return out, lse
+
+
+def backward_splitkv(dout, qkv, out, lse, NH: int, causal: bool = True, kv_chunk: int = 0):
+    """Allocate dqkv and the work buffer with torch and run the split
+    backward (bf16 or fp16 by qkv's dtype)."""
+    B, T, C = _shape(qkv, NH)
+    dqkv = torch.empty_like(qkv)
+    nw = attn_backward_splitkv_bytes(B, T, C, NH, int(causal), kv_chunk) // 4
+    work = torch.empty((max(nw, 4),), dtype=torch.float32, device=qkv.device)
+    fn = {torch.bfloat16: attn_backward_splitkv_bf16, torch.float16: attn_backward_splitkv_f16}[qkv.dtype]
+    fn(dqkv, dout, qkv, out, lse, work, B, T, C, NH, int(causal), kv_chunk)
+    return dqkv
 
 
 def backward(dout, qkv, out, lse, NH: int, causal: bool = True):

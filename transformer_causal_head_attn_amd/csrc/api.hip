@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -376,6 +377,184 @@ int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv
     hipError_t e = attn::launch_dq_bf16(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward_bf16 launch");
+}
+
+}  // extern "C"
+
+namespace {
+// Split-KV forward geometry: key chunks of `chunk` keys (a multiple of 64)
+// over Q tiles of attn::kFwdHalfRows rows.
+long long splitkv_items(const attn::Shape& s, int chunk_tiles) {
+    const int BM = attn::kFwdHalfRows;
+    const int nqt = (s.T + BM - 1) / BM, nkt = (s.T + 63) / 64;
+    long long per_head = 0;
+    for (int i = 0; i < nqt; ++i) {
+        const int kt = s.causal ? std::min(nkt, ((i + 1) * BM + 63) / 64) : nkt;
+        per_head += (kt + chunk_tiles - 1) / chunk_tiles;
+    }
+    return per_head * s.B * s.NH;
+}
+
+// The chunk the library picks: the longest power-of-two number of 64-key
+// tiles (at least 2) that still gives a workgroup per CU; the whole key
+// range (no split) when the unsplit grid already does.  (Two long-context
+// heads, T = 8192: 2048-key chunks, 320 workgroups, measured faster than
+// 1024-key ones, 576 workgroups, whose partial results cost the merge more.)
+int splitkv_auto_chunk(const attn::Shape& s) {
+    const long long want = (long long)attn::device_cu_count();
+    const int nkt = (s.T + 63) / 64;
+    int best = 2;
+    for (int ct = 2; ct < 2 * nkt; ct *= 2)
+        if (splitkv_items(s, ct) >= want) best = ct;
+    if (splitkv_items(s, nkt) >= want) best = nkt;
+    return std::min(best, nkt) * 64;
+}
+
+size_t splitkv_parts(const attn::Shape& s, int chunk) {
+    return (size_t)(((s.T + 63) / 64 + chunk / 64 - 1) / (chunk / 64));
+}
+
+size_t splitkv_floats(const attn::Shape& s, int chunk) {
+    const size_t P = splitkv_parts(s, chunk);
+    return P * ((size_t)s.B * s.T * s.C + (size_t)s.B * s.NH * s.T);
+}
+
+// Split backward work: D (B*NH*T floats, rounded up to 64), then the dq
+// slabs (P of B*T*C floats) and the dk/dv slabs (P of B*T*2C floats).
+size_t bwd_split_floats(const attn::Shape& s, int chunk) {
+    const size_t P = splitkv_parts(s, chunk);
+    const size_t d = ((size_t)s.B * s.NH * s.T + 63) & ~(size_t)63;
+    return P <= 1 ? d : d + 3 * P * (size_t)s.B * s.T * s.C;
+}
+
+int check_chunk(int kv_chunk) {
+    if (kv_chunk < 0 || kv_chunk % 64 != 0)
+        return fail(ATTN_EINVAL, "kv_chunk must be 0 or a positive multiple of 64 (got %d)",
+                    kv_chunk);
+    return ATTN_OK;
+}
+
+int forward_splitkv_any(uint16_t* out, float* lse, const uint16_t* qkv, float* work, int B,
+                        int T, int C, int NH, int causal, int kv_chunk, bool f16) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, 2), "out"}, {lse, nbytes(BT * NH, 4), "lse"},
+                         {work, 0, "work"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 2), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 3, ins, 1, false);
+    if (rc) return rc;
+    if ((rc = check_chunk(kv_chunk))) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const int chunk = kv_chunk ? std::min(kv_chunk, (T + 63) / 64 * 64) : splitkv_auto_chunk(s);
+    const size_t P = splitkv_parts(s, chunk);
+    if (P <= 1)   // no split: the plain forward, the work buffer untouched
+        return launched(f16 ? attn::launch_fwd_f16(out, lse, qkv, s, g_stream)
+                            : attn::launch_fwd_bf16(out, lse, qkv, s, g_stream),
+                        "attn_forward_splitkv launch");
+    const Span ws = {work, splitkv_floats(s, chunk) * 4, "work"};
+    if (overlaps(ws, outs[0]) || overlaps(ws, outs[1]) || overlaps(ws, ins[0]))
+        return fail(ATTN_EINVAL, "work overlaps another tensor argument");
+    if ((unsigned long long)P * BT * C >= (1ULL << 62)) return fail(ATTN_EINVAL, "work too large");
+    float* o_parts = work;
+    float* l_parts = work + P * (size_t)BT * C;
+    hipError_t e = f16 ? attn::launch_fwd_part_f16(o_parts, l_parts, qkv, chunk / 64, s, g_stream)
+                       : attn::launch_fwd_part_bf16(o_parts, l_parts, qkv, chunk / 64, s, g_stream);
+    if (e == hipSuccess)
+        e = f16 ? attn::launch_merge_split_f16(out, lse, o_parts, l_parts, (int)P,
+                                               attn::kFwdHalfRows, chunk, s, g_stream)
+                : attn::launch_merge_split_bf16(out, lse, o_parts, l_parts, (int)P,
+                                                attn::kFwdHalfRows, chunk, s, g_stream);
+    return launched(e, "attn_forward_splitkv launch");
+}
+
+int backward_splitkv_any(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                         const uint16_t* out, const float* lse, float* work, int B, int T, int C,
+                         int NH, int causal, int kv_chunk, bool f16) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 2), "dqkv"}, {work, 0, "work"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 2), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 2), "qkv"},
+                        {out, nbytes(BT * C, 2), "out"},
+                        {lse, nbytes(BT * NH, 4), "lse"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 4, false);
+    if (rc) return rc;
+    if ((rc = check_chunk(kv_chunk))) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const int chunk = kv_chunk ? std::min(kv_chunk, (T + 63) / 64 * 64) : splitkv_auto_chunk(s);
+    const Span ws = {work, bwd_split_floats(s, chunk) * 4, "work"};
+    if (overlaps(ws, outs[0])) return fail(ATTN_EINVAL, "work overlaps dqkv");
+    for (const Span& in : ins)
+        if (overlaps(ws, in)) return fail(ATTN_EINVAL, "work overlaps input %s", in.name);
+    hipError_t e;
+    if (splitkv_parts(s, chunk) <= 1) {   // no split: the two stages, D in work
+        e = f16 ? attn::launch_dq_f16(dqkv, work, dout, qkv, out, lse, s, g_stream)
+                : attn::launch_dq_bf16(dqkv, work, dout, qkv, out, lse, s, g_stream);
+        if (e == hipSuccess)
+            e = f16 ? attn::launch_dkdv_f16(dqkv, dout, qkv, lse, work, s, g_stream)
+                    : attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, work, s, g_stream);
+    } else {
+        e = f16 ? attn::launch_bwd_split_f16(dqkv, work, dout, qkv, out, lse, chunk / 64, s, g_stream)
+                : attn::launch_bwd_split_bf16(dqkv, work, dout, qkv, out, lse, chunk / 64, s, g_stream);
+    }
+    return launched(e, "attn_backward_splitkv launch");
+}
+}  // namespace
+
+extern "C" {
+
+uint64_t attn_backward_splitkv_bytes(int B, int T, int C, int NH, int causal, int kv_chunk) {
+    static const float dummy[4] __attribute__((aligned(16))) = {};
+    const Span none[] = {{dummy, 0, "none"}};
+    if (check_args(B, T, C, NH, causal, none, 0, none, 0, false) != ATTN_OK) return 0;
+    if (check_chunk(kv_chunk) != ATTN_OK) return 0;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const int chunk = kv_chunk ? std::min(kv_chunk, (T + 63) / 64 * 64) : splitkv_auto_chunk(s);
+    ok();
+    return (uint64_t)bwd_split_floats(s, chunk) * 4;
+}
+
+int attn_backward_splitkv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                               const uint16_t* out, const float* lse, float* work, int B, int T,
+                               int C, int NH, int causal, int kv_chunk) {
+    return backward_splitkv_any(dqkv, dout, qkv, out, lse, work, B, T, C, NH, causal, kv_chunk,
+                                false);
+}
+
+int attn_backward_splitkv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                              const uint16_t* out, const float* lse, float* work, int B, int T,
+                              int C, int NH, int causal, int kv_chunk) {
+    return backward_splitkv_any(dqkv, dout, qkv, out, lse, work, B, T, C, NH, causal, kv_chunk,
+                                true);
+}
+
+int attn_forward_splitkv_chunk(int B, int T, int C, int NH, int causal) {
+    static const float dummy[4] __attribute__((aligned(16))) = {};
+    const Span none[] = {{dummy, 0, "none"}};
+    int rc = check_args(B, T, C, NH, causal, none, 0, none, 0, false);
+    if (rc) return rc;
+    ok();
+    return splitkv_auto_chunk(shape_of(B, T, C, NH, causal));
+}
+
+uint64_t attn_forward_splitkv_bytes(int B, int T, int C, int NH, int causal, int kv_chunk) {
+    static const float dummy[4] __attribute__((aligned(16))) = {};
+    const Span none[] = {{dummy, 0, "none"}};
+    if (check_args(B, T, C, NH, causal, none, 0, none, 0, false) != ATTN_OK) return 0;
+    if (check_chunk(kv_chunk) != ATTN_OK) return 0;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    const int chunk = kv_chunk ? std::min(kv_chunk, (T + 63) / 64 * 64) : splitkv_auto_chunk(s);
+    ok();
+    if (splitkv_parts(s, chunk) <= 1) return 0;
+    return (uint64_t)splitkv_floats(s, chunk) * 4;
+}
+
+int attn_forward_splitkv_bf16(uint16_t* out, float* lse, const uint16_t* qkv, float* work, int B,
+                              int T, int C, int NH, int causal, int kv_chunk) {
+    return forward_splitkv_any(out, lse, qkv, work, B, T, C, NH, causal, kv_chunk, false);
+}
+
+int attn_forward_splitkv_f16(uint16_t* out, float* lse, const uint16_t* qkv, float* work, int B,
+                             int T, int C, int NH, int causal, int kv_chunk) {
+    return forward_splitkv_any(out, lse, qkv, work, B, T, C, NH, causal, kv_chunk, true);
 }
 
 int attn_backward_preprocess_bf16(float* D, const uint16_t* dout, const uint16_t* out, int B,

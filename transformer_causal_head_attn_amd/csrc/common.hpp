@@ -183,6 +183,26 @@ hipError_t launch_dkdv_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t
                             const float* lse, const float* D, const Shape& s, hipStream_t st);
 hipError_t launch_dq_bf16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                           const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
+// split-KV forward of the 16-bit path: partial (O, lse) per (Q tile, key
+// chunk of chunk_tiles 64-key tiles), then the merge per row
+constexpr int kFwdHalfRows = 128;   // rows per Q tile of the 16-bit forward
+hipError_t launch_fwd_part_bf16(float* o_parts, float* lse_parts, const uint16_t* qkv,
+                                int chunk_tiles, const Shape& s, hipStream_t st);
+hipError_t launch_fwd_part_f16(float* o_parts, float* lse_parts, const uint16_t* qkv,
+                               int chunk_tiles, const Shape& s, hipStream_t st);
+hipError_t launch_merge_split_bf16(uint16_t* out, float* lse, const float* o_parts,
+                                   const float* lse_parts, int P, int part_rows, int part_keys,
+                                   const Shape& s, hipStream_t st);
+hipError_t launch_merge_split_f16(uint16_t* out, float* lse, const float* o_parts,
+                                  const float* lse_parts, int P, int part_rows, int part_keys,
+                                  const Shape& s, hipStream_t st);
+// split backward of the 16-bit path (work: D, dq slabs, dk/dv slabs)
+hipError_t launch_bwd_split_bf16(uint16_t* dqkv, float* work, const uint16_t* dout,
+                                 const uint16_t* qkv, const uint16_t* out, const float* lse,
+                                 int chunk_tiles, const Shape& s, hipStream_t st);
+hipError_t launch_bwd_split_f16(uint16_t* dqkv, float* work, const uint16_t* dout,
+                                const uint16_t* qkv, const uint16_t* out, const float* lse,
+                                int chunk_tiles, const Shape& s, hipStream_t st);
 // fp16 fused path (IEEE half tensors as raw 16-bit patterns)
 hipError_t launch_fwd_f16(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                           hipStream_t st);

@@ -229,13 +229,20 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(typename OUT::T* __rest
                                                          const float* __restrict__ o_parts,
                                                          const float* __restrict__ lse_parts,
                                                          int P, int B, int T, int C, int NH,
-                                                         long long n4) {
+                                                         long long n4, int part_rows,
+                                                         int part_keys) {
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= n4) return;
     const int C4 = C / 4;
     const long long row = gid / C4;               // b*T + t
     const int c = (int)(gid - row * C4) * 4;
     const int b = (int)(row / T), t = (int)(row - (long long)b * T);
+    // causal split of the keys of part_rows-row query tiles into part_keys
+    // chunks: only the chunks up to the tile's last key were written
+    if (part_rows > 0) {
+        const int kend = min(T, (t / part_rows + 1) * part_rows);
+        P = min(P, (kend + part_keys - 1) / part_keys);
+    }
     const int hs = C / NH;
     const int h = c / hs;
     const size_t BT = (size_t)B * T;
@@ -290,11 +297,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(typename OUT::T* __rest
 
 template <typename OUT>
 hipError_t merge_launch(typename OUT::T* out, float* lse, const float* o_parts, const float* lse_parts, int P,
-                        const Shape& s, hipStream_t st) {
+                        const Shape& s, hipStream_t st, int part_rows = 0, int part_keys = 1) {
     const long long n4 = (long long)s.B * s.T * (s.C / 4);
     const unsigned grid = (unsigned)((n4 + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(merge_kernel<OUT>, dim3(grid), dim3(kThreads), 0, st, out, lse, o_parts,
-                       lse_parts, P, s.B, s.T, s.C, s.NH, n4);
+                       lse_parts, P, s.B, s.T, s.C, s.NH, n4, part_rows, part_keys);
     return hipGetLastError();
 }
 
@@ -376,6 +383,21 @@ hipError_t launch_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, flo
 hipError_t launch_merge_f16(uint16_t* out, float* lse, const float* o_parts,
                             const float* lse_parts, int P, const Shape& s, hipStream_t st) {
     return merge_launch<EF16>(out, lse, o_parts, lse_parts, P, s, st);
+}
+
+// merge of a causal split-KV forward: rows of part_rows-row query tiles, key
+// chunks of part_keys keys (non-causal: every row has all P parts)
+hipError_t launch_merge_split_bf16(uint16_t* out, float* lse, const float* o_parts,
+                                   const float* lse_parts, int P, int part_rows, int part_keys,
+                                   const Shape& s, hipStream_t st) {
+    return merge_launch<EBF16>(out, lse, o_parts, lse_parts, P, s, st, s.causal ? part_rows : 0,
+                               part_keys);
+}
+hipError_t launch_merge_split_f16(uint16_t* out, float* lse, const float* o_parts,
+                                  const float* lse_parts, int P, int part_rows, int part_keys,
+                                  const Shape& s, hipStream_t st) {
+    return merge_launch<EF16>(out, lse, o_parts, lse_parts, P, s, st, s.causal ? part_rows : 0,
+                              part_keys);
 }
 
 }  // namespace attn

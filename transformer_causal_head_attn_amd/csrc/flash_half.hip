@@ -264,11 +264,20 @@ __device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal 
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
 // stream through LDS 64 at a time (one buffer; the next tile's registers
 // are loaded while the current tile is used).
-template <typename E, int HS, int QB>
+// Key range of one forward workgroup and, for a split of the keys over
+// workgroups, where its partial result goes.
+struct KeyPart {
+    int kt_lo, kt_hi;      // 64-key tiles [kt_lo, kt_hi) (kt_hi clipped to what the tile sees)
+    float* o;              // PART: output normalised over the range, fp32 (B, T, C) slab
+    float* l;              // PART: log-sum-exp over the range, (B, NH, T) slab
+};
+
+template <typename E, int HS, int QB, bool PART>
 __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __restrict__ out,
                                               float* __restrict__ lse,
                                               const uint16_t* __restrict__ qkv, int T, int C,
-                                              int NH, int causal, float scale_log2) {
+                                              int NH, int causal, float scale_log2,
+                                              KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
     constexpr int BM = 4 * R;
@@ -308,7 +317,9 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
     }
 
     const int nkt_all = (T + kStream - 1) / kStream;
-    const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    const int nkt_tile = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    const int kt_lo = PART ? part.kt_lo : 0;
+    const int nkt = PART ? min(part.kt_hi, nkt_tile) : nkt_tile;
     // last key tile with a key <= some row of this wave; none when the
     // wave has no row below T (its stores are skipped anyway)
     int last = causal ? min(nkt - 1, (r0 + R - 1) / kStream) : nkt - 1;
@@ -398,10 +409,10 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
     TileRegs<HS> rk, rv;
     {
         f32x4 sc[QB][4];
-        rk.fetch(kbase, C3, 0, T, L.tid);
-        rv.fetch(vbase, C3, 0, T, L.tid);
+        rk.fetch(kbase, C3, kt_lo * kStream, T, L.tid);
+        rv.fetch(vbase, C3, kt_lo * kStream, T, L.tid);
         wait_global_loads();
-        for (int j = 0; j < nkt; ++j) {
+        for (int j = kt_lo; j < nkt; ++j) {
             __syncthreads();
             rk.store(Ks, L.tid);
             rv.store(Vs, L.tid);
@@ -427,11 +438,26 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
         const int row = r0 + 16 * qb + L.r16;
         const float ltot = lsum[qb][0];
         if (row < T) {
-            const float inv = 1.0f / ltot;
-            uint16_t* orow = out + ((size_t)b * T + row) * C + (size_t)h * HS;
+            if constexpr (PART) {
+                // a row with no key in the range (its keys all lie past it):
+                // out 0, lse -inf, which the merge weighs by exp(-inf) = 0
+                const bool any = ltot > 0.f;
+                const float inv = any ? 1.0f / ltot : 0.f;
+                float* orow = part.o + ((size_t)b * T + row) * C + (size_t)h * HS;
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb) store4<E>(orow + 16 * mb + 4 * L.g, o[qb][mb] * inv);
-            if (L.g == 0) lse[(size_t)bh * T + row] = (m[qb] + __log2f(ltot)) * kLn2;
+                for (int mb = 0; mb < G::MB; ++mb) {
+                    const f32x4 v = o[qb][mb] * inv;
+                    *reinterpret_cast<float4*>(orow + 16 * mb + 4 * L.g) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+                if (L.g == 0)
+                    part.l[(size_t)bh * T + row] = any ? (m[qb] + __log2f(ltot)) * kLn2 : -INFINITY;
+            } else {
+                const float inv = 1.0f / ltot;
+                uint16_t* orow = out + ((size_t)b * T + row) * C + (size_t)h * HS;
+#pragma unroll
+                for (int mb = 0; mb < G::MB; ++mb) store4<E>(orow + 16 * mb + 4 * L.g, o[qb][mb] * inv);
+                if (L.g == 0) lse[(size_t)bh * T + row] = (m[qb] + __log2f(ltot)) * kLn2;
+            }
         }
     }
 }
@@ -472,12 +498,15 @@ __global__ __launch_bounds__(kThreads) void prepass_half_kernel(float* __restric
 // ----------------------------------------------------- backward dK / dV
 // Workgroup: a 4*R-row K/V tile of one head (R = 16*KB rows per wave, kept
 // in registers); Q and dO stream through LDS 64 rows at a time.
-template <typename E, int HS, int KB>
+// PART: the workgroup takes the query tiles [part.kt_lo, part.kt_hi) only
+// (64-row tiles) and writes its fp32 dk (scaled) and dv sums to the partial
+// slab part.o, rows of 2C: [dk | dv] (a later kernel adds the slabs).
+template <typename E, int HS, int KB, bool PART>
 __device__ __forceinline__ void bwd_dkdv_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
-    float scale_log2) {
+    float scale_log2, KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * KB;
     constexpr int BN = 4 * R;
@@ -517,8 +546,9 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
             dv[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    const int nqt = (T + kStream - 1) / kStream;
-    const int qt0 = causal ? (kvt * BN) / kStream : 0;
+    const int nqt_all = (T + kStream - 1) / kStream;
+    const int nqt = PART ? min(nqt_all, part.kt_hi) : nqt_all;
+    const int qt0 = max(causal ? (kvt * BN) / kStream : 0, PART ? part.kt_lo : 0);
     TileRegs<HS> rq, rd;
     float rl = 0.f, rD = 0.f;
     // lse and D of the tile's rows are loaded raw and only transformed when
@@ -622,12 +652,23 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
     for (int kb = 0; kb < KB; ++kb) {
         const int kv = c0 + 16 * kb + L.r16;
         if (kv < T) {
-            uint16_t* dkrow = dqkv + ((size_t)b * T + kv) * C3 + C + (size_t)h * HS;
-            uint16_t* dvrow = dkrow + C;
+            if constexpr (PART) {
+                float* prow = part.o + ((size_t)b * T + kv) * 2 * C + (size_t)h * HS;
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb) {
-                store4<E>(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
-                store4<E>(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
+                for (int mb = 0; mb < G::MB; ++mb) {
+                    const f32x4 a = dk[kb][mb] * scale;
+                    const f32x4 v = dv[kb][mb];
+                    *reinterpret_cast<float4*>(prow + 16 * mb + 4 * L.g) = make_float4(a[0], a[1], a[2], a[3]);
+                    *reinterpret_cast<float4*>(prow + C + 16 * mb + 4 * L.g) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                uint16_t* dkrow = dqkv + ((size_t)b * T + kv) * C3 + C + (size_t)h * HS;
+                uint16_t* dvrow = dkrow + C;
+#pragma unroll
+                for (int mb = 0; mb < G::MB; ++mb) {
+                    store4<E>(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
+                    store4<E>(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
+                }
             }
         }
     }
@@ -638,12 +679,15 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
 // registers); K and V stream through LDS 64 rows at a time.  It first forms
 // D = dO . O for its rows and writes it out for the dK/dV kernel, which runs
 // after it.
-template <typename E, int HS, int QB>
+// PART: the workgroup takes the key tiles [part.kt_lo, part.kt_hi) only and
+// writes its fp32 dq sum (scaled) to the partial slab part.o (B, T, C); the
+// workgroup of the first key range also writes D.
+template <typename E, int HS, int QB, bool PART>
 __device__ __forceinline__ void bwd_dq_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, float* __restrict__ Dws,
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ qkv,
     const uint16_t* __restrict__ out, const float* __restrict__ lse, int T, int C, int NH,
-    int causal, float scale, float scale_log2) {
+    int causal, float scale, float scale_log2, KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
     constexpr int BM = 4 * R;
@@ -682,7 +726,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
             for (int e = 0; e < 8; ++e) acc = fmaf((float)doreg[qb][s][e], (float)oc[e], acc);
         }
         Dq[qb] = group4_sum(acc);
-        if (v && L.g == 0) Dws[(size_t)bh * T + q] = Dq[qb];
+        if (v && L.g == 0 && (!PART || part.kt_lo == 0)) Dws[(size_t)bh * T + q] = Dq[qb];
     }
     f32x4 dq[QB][G::MB], dneg[QB];
 #pragma unroll
@@ -693,12 +737,14 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     }
 
     const int nkt_all = (T + kStream - 1) / kStream;
-    const int nkt = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    const int nkt_tile = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
+    const int kt_lo = PART ? part.kt_lo : 0;
+    const int nkt = PART ? min(nkt_tile, part.kt_hi) : nkt_tile;
     TileRegs<HS> rk, rv;
-    rk.fetch(kbase, C3, 0, T, L.tid);
-    rv.fetch(vbase, C3, 0, T, L.tid);
+    rk.fetch(kbase, C3, kt_lo * kStream, T, L.tid);
+    rv.fetch(vbase, C3, kt_lo * kStream, T, L.tid);
     wait_global_loads();
-    for (int kt = 0; kt < nkt; ++kt) {
+    for (int kt = kt_lo; kt < nkt; ++kt) {
         __syncthreads();
         rk.store(Ks, L.tid);
         rv.store(Vs, L.tid);
@@ -769,9 +815,18 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     for (int qb = 0; qb < QB; ++qb) {
         const int q = r0 + 16 * qb + L.r16;
         if (q < T) {
-            uint16_t* dqrow = dqkv + ((size_t)b * T + q) * C3 + (size_t)h * HS;
+            if constexpr (PART) {
+                float* prow = part.o + ((size_t)b * T + q) * C + (size_t)h * HS;
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb) store4<E>(dqrow + 16 * mb + 4 * L.g, dq[qb][mb] * scale);
+                for (int mb = 0; mb < G::MB; ++mb) {
+                    const f32x4 v = dq[qb][mb] * scale;
+                    *reinterpret_cast<float4*>(prow + 16 * mb + 4 * L.g) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                uint16_t* dqrow = dqkv + ((size_t)b * T + q) * C3 + (size_t)h * HS;
+#pragma unroll
+                for (int mb = 0; mb < G::MB; ++mb) store4<E>(dqrow + 16 * mb + 4 * L.g, dq[qb][mb] * scale);
+            }
         }
     }
 }
@@ -789,7 +844,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
-    fwd_half_tile<E, HS, QB>(t, bh, out, lse, qkv, T, C, NH, causal, scale_log2);
+    fwd_half_tile<E, HS, QB, false>(t, bh, out, lse, qkv, T, C, NH, causal, scale_log2,
+                                    KeyPart{0, 0, nullptr, nullptr});
+}
+
+// Split-KV forward: workgroup (rank, bh) of a grid of nqt * nchunk * BH
+// takes Q tile nqt - 1 - rank / nchunk (heaviest first) and key chunk
+// rank % nchunk (chunk_tiles 64-key tiles); chunks wholly past the tile's
+// last key do nothing.  Each writes its partial output and log-sum-exp into
+// the chunk's slabs of o_parts (nchunk, B, T, C) and lse_parts
+// (nchunk, B, NH, T); merge_kernel combines them per row.
+template <typename E, int HS, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void fwd_part_half_kernel(float* __restrict__ o_parts,
+                                                            float* __restrict__ lse_parts,
+                                                            const uint16_t* __restrict__ qkv,
+                                                            int T, int C, int NH, int causal,
+                                                            float scale_log2, int BH, int nchunk,
+                                                            int chunk_tiles) {
+    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    const int rank = blockIdx.x / BH;
+    const int bh = blockIdx.x - rank * BH;
+    const int tile = nt - 1 - rank / nchunk;
+    const int c = rank - (rank / nchunk) * nchunk;
+    if (tile < 0) return;
+    const int nkt_all = (T + kStream - 1) / kStream;
+    const int nkt_tile = causal ? min(nkt_all, (tile * 64 * QB + 64 * QB - 1) / kStream + 1) : nkt_all;
+    const int lo = c * chunk_tiles;
+    if (lo >= nkt_tile) return;   // whole workgroup: no barrier is reached
+    const size_t B = (size_t)BH / NH;
+    KeyPart part{lo, lo + chunk_tiles, o_parts + (size_t)c * B * T * C,
+                 lse_parts + (size_t)c * BH * T};
+    fwd_half_tile<E, HS, QB, true>(tile, bh, nullptr, nullptr, qkv, T, C, NH, causal, scale_log2,
+                                   part);
 }
 
 template <typename E, int HS, int KB>
@@ -801,7 +887,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int nt = (T + 64 * KB - 1) / (64 * KB);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, false, deal, bh, t);
-    bwd_dkdv_half_tile<E, HS, KB>(t, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale, scale_log2);
+    bwd_dkdv_half_tile<E, HS, KB, false>(t, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale,
+                                         scale_log2, KeyPart{0, 0, nullptr, nullptr});
 }
 
 template <typename E, int HS, int QB>
@@ -813,10 +900,98 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
     const int nt = (T + 64 * QB - 1) / (64 * QB);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
-    bwd_dq_half_tile<E, HS, QB>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal, scale, scale_log2);
+    bwd_dq_half_tile<E, HS, QB, false>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal,
+                                       scale, scale_log2, KeyPart{0, 0, nullptr, nullptr});
+}
+
+// Split backward.  dQ: workgroup (rank, bh) of nqt * nchunk * BH takes Q
+// tile nqt - 1 - rank / nchunk and key chunk rank % nchunk (chunk_tiles
+// 64-key tiles; chunks past the tile's last key do nothing), writing its
+// dq sum to slab c of dq_parts (nchunk, B, T, C).  dK/dV: workgroup (rank,
+// bh) of nkvt * nchunk * BH takes K/V tile rank / nchunk and query chunk
+// rank % nchunk (chunk_tiles 64-row query tiles; chunks wholly before the
+// tile's first query do nothing), writing dk, dv sums to slab c of
+// dkv_parts (nchunk, B, T, 2C).  sum_parts_kernel adds the slabs.
+template <typename E, int HS, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void bwd_dq_part_half_kernel(
+    float* __restrict__ dq_parts, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
+    float scale_log2, int BH, int nchunk, int chunk_tiles) {
+    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    const int rank = blockIdx.x / BH;
+    const int bh = blockIdx.x - rank * BH;
+    const int tile = nt - 1 - rank / nchunk;
+    const int c = rank - (rank / nchunk) * nchunk;
+    if (tile < 0) return;
+    const int nkt_all = (T + kStream - 1) / kStream;
+    const int nkt_tile = causal ? min(nkt_all, (tile * 64 * QB + 64 * QB - 1) / kStream + 1) : nkt_all;
+    const int lo = c * chunk_tiles;
+    if (lo >= nkt_tile) return;   // whole workgroup: no barrier is reached
+    const size_t B = (size_t)BH / NH;
+    KeyPart part{lo, lo + chunk_tiles, dq_parts + (size_t)c * B * T * C, nullptr};
+    bwd_dq_half_tile<E, HS, QB, true>(tile, bh, nullptr, Dws, dout, qkv, out, lse, T, C, NH, causal,
+                                      scale, scale_log2, part);
+}
+
+template <typename E, int HS, int KB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_part_half_kernel(
+    float* __restrict__ dkv_parts, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
+    const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
+    float scale_log2, int BH, int nchunk, int chunk_tiles) {
+    constexpr int BN = 64 * KB;
+    const int nt = (T + BN - 1) / BN;
+    const int rank = blockIdx.x / BH;
+    const int bh = blockIdx.x - rank * BH;
+    const int tile = rank / nchunk;
+    const int c = rank - (rank / nchunk) * nchunk;
+    if (tile >= nt) return;
+    const int nqt_all = (T + kStream - 1) / kStream;
+    const int qt0 = causal ? (tile * BN) / kStream : 0;
+    const int hi = min(nqt_all, (c + 1) * chunk_tiles);
+    if (hi <= qt0) return;        // whole workgroup: no barrier is reached
+    const size_t B = (size_t)BH / NH;
+    KeyPart part{c * chunk_tiles, hi, dkv_parts + (size_t)c * B * T * 2 * C, nullptr};
+    bwd_dkdv_half_tile<E, HS, KB, true>(tile, bh, nullptr, dout, qkv, lse, Dws, T, C, NH, causal,
+                                        scale, scale_log2, part);
+}
+
+// Sum of the partial slabs into one third (part 0: dq, width C) or two
+// thirds (dk, dv, width 2C) of the packed dqkv, rounded once to the 16-bit
+// type.  Row t of the dq slabs has parts c < ceil(kend / chunk) (causal:
+// kend = the end of its Q tile's keys); key row j of the dk/dv slabs has
+// parts c >= first query row of its K/V tile / chunk (causal).  The parts
+// are added in increasing c.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void sum_parts_kernel(uint16_t* __restrict__ dqkv,
+                                                             const float* __restrict__ parts,
+                                                             int P, int B, int T, int C, int width,
+                                                             int col0, int causal, int q_rows,
+                                                             int kv_rows, int chunk, long long n4) {
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= n4) return;
+    const int W4 = width / 4;
+    const long long row = gid / W4;   // b*T + t
+    const int c = (int)(gid - row * W4) * 4;
+    const int t = (int)(row % T);
+    int p0 = 0, p1 = P;
+    if (causal && q_rows > 0) p1 = min(P, (min(T, (t / q_rows + 1) * q_rows) + chunk - 1) / chunk);
+    if (causal && kv_rows > 0) p0 = ((t / kv_rows) * kv_rows) / chunk;
+    const size_t slab = (size_t)B * T * width;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p = p0; p < p1; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(parts + p * slab + (size_t)row * width + c);
+        acc[0] += v.x;
+        acc[1] += v.y;
+        acc[2] += v.z;
+        acc[3] += v.w;
+    }
+    store4<E>(dqkv + (size_t)row * 3 * C + col0 + c, f32x4{acc[0], acc[1], acc[2], acc[3]});
 }
 
 constexpr int kQB = 2;
+static_assert(64 * kQB == kFwdHalfRows, "forward Q tile rows");
 // dK/dV: 32 K/V rows per wave for hs <= 64, 16 for hs = 128 (fewer
 // registers, more resident waves; measured faster on the long-context shape)
 constexpr int kb_for(int hs) { return hs >= 128 ? 1 : 2; }
@@ -831,6 +1006,61 @@ hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Sha
     const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>(kThreads);
     hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
                        qkv, s.T, s.C, s.NH, s.causal, scale_log2, deal);
+    return hipGetLastError();
+}
+
+template <typename E, int HS>
+hipError_t fwd_part_half_hs(float* o_parts, float* lse_parts, const uint16_t* qkv, int chunk_tiles,
+                            const Shape& s, hipStream_t st) {
+    constexpr int BM = 64 * kQB;
+    const int nqt = (s.T + BM - 1) / BM;
+    const int nkt = (s.T + kStream - 1) / kStream;
+    const int nchunk = (nkt + chunk_tiles - 1) / chunk_tiles;
+    const long long BH = (long long)s.B * s.NH;
+    const long long grid = (long long)nqt * nchunk * BH;
+    if (grid < 1 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
+    hipLaunchKernelGGL((fwd_part_half_kernel<E, HS, kQB>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                       o_parts, lse_parts, qkv, s.T, s.C, s.NH, s.causal, scale_log2, (int)BH,
+                       nchunk, chunk_tiles);
+    return hipGetLastError();
+}
+
+template <typename E, int HS>
+hipError_t bwd_split_half_hs(uint16_t* dqkv, float* work, const uint16_t* dout,
+                             const uint16_t* qkv, const uint16_t* out, const float* lse,
+                             int chunk_tiles, const Shape& s, hipStream_t st) {
+    constexpr int KB = kb_for(HS);
+    const long long BH = (long long)s.B * s.NH;
+    const int nt64 = (s.T + kStream - 1) / kStream;
+    const int nchunk = (nt64 + chunk_tiles - 1) / chunk_tiles;
+    const size_t BTC = (size_t)s.B * s.T * s.C;
+    float* D = work;
+    float* dq_parts = work + (((size_t)BH * s.T + 63) & ~(size_t)63);
+    float* dkv_parts = dq_parts + (size_t)nchunk * BTC;
+    const float scale = (float)(1.0 / sqrt((double)HS));
+    const int nqt = (s.T + 64 * kQB - 1) / (64 * kQB);
+    const int nkvt = (s.T + 64 * KB - 1) / (64 * KB);
+    const long long g1 = (long long)nqt * nchunk * BH, g2 = (long long)nkvt * nchunk * BH;
+    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_part_half_kernel<E, HS, kQB>), dim3((unsigned)g1), dim3(kThreads), 0, st,
+                       dq_parts, D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale,
+                       scale * kLog2e, (int)BH, nchunk, chunk_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    long long n4 = (long long)s.B * s.T * (s.C / 4);
+    hipLaunchKernelGGL(sum_parts_kernel<E>, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, st, dqkv, dq_parts, nchunk, s.B, s.T, s.C, s.C, 0, s.causal, 64 * kQB, 0,
+                       64 * chunk_tiles, n4);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_part_half_kernel<E, HS, KB>), dim3((unsigned)g2), dim3(kThreads), 0, st,
+                       dkv_parts, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
+                       (int)BH, nchunk, chunk_tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    n4 = (long long)s.B * s.T * (2 * s.C / 4);
+    hipLaunchKernelGGL(sum_parts_kernel<E>, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, st, dqkv, dkv_parts, nchunk, s.B, s.T, s.C, 2 * s.C, s.C, s.causal, 0,
+                       64 * KB, 64 * chunk_tiles, n4);
     return hipGetLastError();
 }
 
@@ -889,6 +1119,15 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
     hipError_t launch_fwd_##SFX(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,  \
                                 hipStream_t st) {                                                 \
         ATTN_DISPATCH_HS(fwd_half_hs, E, out, lse, qkv, s, st)                                     \
+    }                                                                                              \
+    hipError_t launch_fwd_part_##SFX(float* o_parts, float* lse_parts, const uint16_t* qkv,      \
+                                     int chunk_tiles, const Shape& s, hipStream_t st) {          \
+        ATTN_DISPATCH_HS(fwd_part_half_hs, E, o_parts, lse_parts, qkv, chunk_tiles, s, st)         \
+    }                                                                                              \
+    hipError_t launch_bwd_split_##SFX(uint16_t* dqkv, float* work, const uint16_t* dout,         \
+                                      const uint16_t* qkv, const uint16_t* out, const float* lse, \
+                                      int chunk_tiles, const Shape& s, hipStream_t st) {          \
+        ATTN_DISPATCH_HS(bwd_split_half_hs, E, dqkv, work, dout, qkv, out, lse, chunk_tiles, s, st)\
     }                                                                                              \
     hipError_t launch_prepass_##SFX(float* D, const uint16_t* dout, const uint16_t* out,          \
                                     const Shape& s, hipStream_t st) {                             \
