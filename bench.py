@@ -461,6 +461,34 @@ def run_splitkv(la, torch, steps=20, warmup_ms=100.0):
     return res
 
 
+def run_projections(la, torch, M, C, steps=20, warmup_ms=100.0):
+    """The QKV projection (M x C times C x 3C, + bias) and the output
+    projection (M x C times C x C, + bias + residual) at the workload's
+    activation rows, fp32 and bf16, in TFLOP/s of 2*M*K*N flops against the
+    matrix-core peak of the dtype."""
+    from workloads import randn
+    res = []
+    for dtype in ("f32", "bf16"):
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        for name, N, resid in (("qkv_projection", 3 * C, False), ("out_projection", C, True)):
+            x = randn((M, C), 41, 1.0, dtype).cuda()
+            w = randn((N, C), 42, 0.02, dtype).cuda()
+            b = randn((N,), 43, 0.02, "f32").cuda()
+            y = torch.empty((M, N), dtype=tdt, device="cuda")
+            if resid:
+                r = randn((M, N), 44, 1.0, dtype).cuda()
+                fn = {"f32": la.attn_out_projection, "bf16": la.attn_out_projection_bf16}[dtype]
+                call = lambda fn=fn, x=x, w=w, b=b, r=r, y=y, N=N: fn(y, x, w, b, r, M, C, N)
+            else:
+                fn = {"f32": la.attn_qkv_projection, "bf16": la.attn_qkv_projection_bf16}[dtype]
+                call = lambda fn=fn, x=x, w=w, b=b, y=y, N=N: fn(y, x, w, b, M, C, N)
+            ms = _time_call(torch, call, steps, warmup_ms)
+            tf = 2.0 * M * C * N / (ms * 1e-3) / 1e12
+            res.append({"op": name, "dtype": dtype, "M": M, "K": C, "N": N, "us": round(ms * 1e3, 2),
+                        "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_TFLOPS[dtype], 4)})
+    return res
+
+
 def run_layernorm(la, torch, N, C, dtype, steps=50, warmup=100):
     """Time the LayerNorm forward and backward over N rows of C (the GPT-2
     layer's activations when N = B*T = 8192, C = 768).  Both are HBM-bound:
@@ -733,7 +761,8 @@ def main():
                              run_layernorm(la, torch, w.B * w.T, w.C, "bf16")]
 
     if not args.no_extra:
-        line["splitkv_forward"] = run_splitkv(la, torch)
+        line["splitkv"] = run_splitkv(la, torch)
+        line["projections"] = run_projections(la, torch, w.B * w.T, w.C)
 
     if not args.no_extra:
         line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),

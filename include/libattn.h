@@ -419,6 +419,40 @@ const char* attn_last_error(void);
  * not race with work still queued that uses it (synchronise first). */
 void attn_release(void);
 
+/*
+ * The projections on either side of the attention block, on the matrix
+ * cores with the elementwise steps fused into the product's store (the
+ * kernel fusion of "LLM Systems 10 & 11: Accelerating Transformer Training
+ * and Inference", section 1).  Row-major, fp32 accumulation:
+ *
+ *   attn_qkv_projection:  qkv[m][n] = sum_k x[m][k] w[n][k] + bias[n]
+ *   attn_out_projection:  y[m][n]   = sum_k a[m][k] w[n][k] + bias[n] + residual[m][n]
+ *
+ * The QKV projection is Q = X W_Q, K = X W_K, V = X W_V of "Umakini wa
+ * kujitegemea, kerneli za CUDA na FlashAttention" (section 1) for all heads
+ * at once: with M = B*T rows of x (C = K wide) and w of shape (N = 3C, K)
+ * whose rows are the columns of [W_Q | W_K | W_V] (the layout in which
+ * each output column's weights are contiguous), qkv is the packed
+ * (B, T, 3C) input of attn_forward.  The output projection adds the
+ * residual stream as residual_forward_kernel does ("llm.c 的中文注解-20240423",
+ * section 1.15: out = inp1 + inp2), here in the same pass.
+ *   x, a (M, K); w (N, K); bias (N) fp32; residual, y, qkv (M, N).
+ *   _bf16: x, a, w, residual and the output bf16, bias fp32; the output
+ *   is rounded once (to nearest even) from the fp32 sum.
+ * Errors: ATTN_EINVAL for a null or misaligned pointer, M, K or N < 1,
+ * K not a multiple of 4 (fp32) or 8 (bf16), N not a multiple of 4, K too
+ * large for 32-bit tile offsets, or an output overlapping an input.
+ * Nothing is allocated.
+ */
+int attn_qkv_projection(float* qkv, const float* x, const float* w, const float* bias,
+                        int M, int K, int N);
+int attn_qkv_projection_bf16(uint16_t* qkv, const uint16_t* x, const uint16_t* w,
+                             const float* bias, int M, int K, int N);
+int attn_out_projection(float* y, const float* a, const float* w, const float* bias,
+                        const float* residual, int M, int K, int N);
+int attn_out_projection_bf16(uint16_t* y, const uint16_t* a, const uint16_t* w,
+                             const float* bias, const uint16_t* residual, int M, int K, int N);
+
 #ifdef __cplusplus
 }
 #endif

@@ -412,3 +412,22 @@ def test_backward_splitkv_work_bytes_and_errors():
         q[5] = ctypes.c_void_p(0)
         rc = getattr(lib, name)(*q, B, T, C, NH, 1, 2048)
         assert rc == la.ATTN_EINVAL and b"NULL" in lib.attn_last_error()
+
+
+@pytest.mark.parametrize("name,nptr", [("attn_qkv_projection", 4), ("attn_qkv_projection_bf16", 4),
+                                       ("attn_out_projection", 5), ("attn_out_projection_bf16", 5)])
+def test_projection_argument_errors(name, nptr):
+    lib = la.load()
+    f = getattr(lib, name)
+    kmul = 8 if name.endswith("bf16") else 4
+    assert f(*ptrs(nptr), 0, 64, 64) == la.ATTN_EINVAL
+    assert f(*ptrs(nptr), 64, kmul + 2, 64) == la.ATTN_EINVAL      # K not a multiple
+    assert b"multiple" in lib.attn_last_error()
+    assert f(*ptrs(nptr), 64, 64, 66) == la.ATTN_EINVAL            # N % 4
+    for i in range(nptr):
+        p = ptrs(nptr)
+        p[i] = ctypes.c_void_p(0)
+        assert f(*p, 64, 64, 64) == la.ATTN_EINVAL and b"NULL" in lib.attn_last_error()
+    p = ptrs(nptr)
+    p[0] = ctypes.c_void_p(BASE + 8)
+    assert f(*p, 64, 64, 64) == la.ATTN_EINVAL and b"aligned" in lib.attn_last_error()

@@ -13,6 +13,8 @@ from ._binding import (  # noqa: F401
     attn_forward_splitkv_bf16, attn_forward_splitkv_f16, forward_splitkv,
     attn_backward_splitkv_bytes, attn_backward_splitkv_bf16, attn_backward_splitkv_f16,
     backward_splitkv,
+    attn_qkv_projection, attn_qkv_projection_bf16, attn_out_projection, attn_out_projection_bf16,
+    qkv_projection, out_projection,
     attn_backward_dq, attn_backward_dq_bf16, attn_backward_materialized,
     attn_backward_ds_bytes, attn_backward_dkdv_ds, attn_backward_dq_ds,
     attn_backward_preprocess, attn_backward_preprocess_bf16, attn_decode, attn_decode_bf16, attn_decode_f16,

@@ -39,6 +39,8 @@ EXPORTS = (
     "attn_merge", "attn_merge_bf16", "attn_merge_f16",
     "layernorm_forward", "layernorm_forward_bf16", "layernorm_backward", "layernorm_backward_bf16",
     "layernorm_forward_f16", "layernorm_backward_f16",
+    "attn_qkv_projection", "attn_qkv_projection_bf16",
+    "attn_out_projection", "attn_out_projection_bf16",
     "attn_set_stream", "attn_last_error", "attn_release",
 )
 
@@ -114,6 +116,14 @@ def load(path: str | None = None):
         for name in ("layernorm_backward", "layernorm_backward_bf16", "layernorm_backward_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 8 + [i] * 2
+            fn.restype = i
+        for name in ("attn_qkv_projection", "attn_qkv_projection_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 4 + [i] * 3
+            fn.restype = i
+        for name in ("attn_out_projection", "attn_out_projection_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp] * 5 + [i] * 3
             fn.restype = i
         lib.attn_set_stream.argtypes = [vp]
         lib.attn_set_stream.restype = i
@@ -260,6 +270,57 @@ def attn_backward_splitkv_f16(dqkv, dout, qkv, out, lse, work, B, T, C, NH, caus
                               kv_chunk) -> None:
     _bwd_splitkv("attn_backward_splitkv_f16", torch.float16, dqkv, dout, qkv, out, lse, work,
                  B, T, C, NH, causal, kv_chunk)
+
+
+def attn_qkv_projection(qkv, x, w, bias, M, K, N) -> None:
+    f = torch.float32
+    _call("attn_qkv_projection", _check(qkv, "qkv", f, M * N), _check(x, "x", f, M * K),
+          _check(w, "w", f, N * K), _check(bias, "bias", f, N), int(M), int(K), int(N))
+
+
+def attn_qkv_projection_bf16(qkv, x, w, bias, M, K, N) -> None:
+    h = torch.bfloat16
+    _call("attn_qkv_projection_bf16", _check(qkv, "qkv", h, M * N), _check(x, "x", h, M * K),
+          _check(w, "w", h, N * K), _check(bias, "bias", torch.float32, N),
+          int(M), int(K), int(N))
+
+
+def attn_out_projection(y, a, w, bias, residual, M, K, N) -> None:
+    f = torch.float32
+    _call("attn_out_projection", _check(y, "y", f, M * N), _check(a, "a", f, M * K),
+          _check(w, "w", f, N * K), _check(bias, "bias", f, N),
+          _check(residual, "residual", f, M * N), int(M), int(K), int(N))
+
+
+def attn_out_projection_bf16(y, a, w, bias, residual, M, K, N) -> None:
+    h = torch.bfloat16
+    _call("attn_out_projection_bf16", _check(y, "y", h, M * N), _check(a, "a", h, M * K),
+          _check(w, "w", h, N * K), _check(bias, "bias", torch.float32, N),
+          _check(residual, "residual", h, M * N), int(M), int(K), int(N))
+
+
+def qkv_projection(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor) -> torch.Tensor:
+    """Allocate qkv with torch and run x w^T + bias (x (..., K), w (N, K));
+    fp32 or bf16 by x's dtype, bias fp32."""
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = w.shape[0]
+    out = torch.empty(x.shape[:-1] + (N,), dtype=x.dtype, device=x.device)
+    fn = attn_qkv_projection_bf16 if x.dtype == torch.bfloat16 else attn_qkv_projection
+    fn(out, x, w, bias, M, K, N)
+    return out
+
+
+def out_projection(a: torch.Tensor, w: torch.Tensor, bias: torch.Tensor,
+                   residual: torch.Tensor) -> torch.Tensor:
+    """Allocate y with torch and run a w^T + bias + residual."""
+    K = a.shape[-1]
+    M = a.numel() // K
+    N = w.shape[0]
+    out = torch.empty(a.shape[:-1] + (N,), dtype=a.dtype, device=a.device)
+    fn = attn_out_projection_bf16 if a.dtype == torch.bfloat16 else attn_out_projection
+    fn(out, a, w, bias, residual, M, K, N)
+    return out
 
 
 def attn_backward_ds_bytes(B, T, C, NH, causal) -> int:

@@ -905,3 +905,84 @@ int layernorm_backward_bf16(uint16_t* dinp, float* dweight, float* dbias, const 
 }
 
 }  // extern "C"
+
+// ---- projections ----
+namespace {
+int check_proj(int M, int K, int N, int kmul, const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i)
+        if (!outs[i].p) return fail(ATTN_EINVAL, "%s is NULL", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if (!ins[i].p) return fail(ATTN_EINVAL, "%s is NULL", ins[i].name);
+    if (M < 1 || K < 1 || N < 1)
+        return fail(ATTN_EINVAL, "M, K and N must be >= 1 (got M=%d K=%d N=%d)", M, K, N);
+    if (K % kmul != 0)
+        return fail(ATTN_EINVAL, "K=%d must be a multiple of %d (16-byte rows)", K, kmul);
+    if (N % 4 != 0) return fail(ATTN_EINVAL, "N=%d must be a multiple of 4", N);
+    // a 128-row tile of rows K elements long is addressed with 32-bit byte offsets
+    if ((long long)128 * K * 4 >= (1LL << 31))
+        return fail(ATTN_EINVAL, "K=%d too large for the tile offsets", K);
+    for (int i = 0; i < nout; ++i)
+        if ((uintptr_t)outs[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", outs[i].name);
+    for (int i = 0; i < nin; ++i)
+        if ((uintptr_t)ins[i].p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", ins[i].name);
+    for (int i = 0; i < nout; ++i)
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(ATTN_EINVAL, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    return ATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int attn_qkv_projection(float* qkv, const float* x, const float* w, const float* bias, int M, int K,
+                        int N) {
+    const Span outs[] = {{qkv, nbytes((long long)M * N, 4), "qkv"}};
+    const Span ins[] = {{x, nbytes((long long)M * K, 4), "x"},
+                        {w, nbytes((long long)N * K, 4), "w"},
+                        {bias, nbytes(N, 4), "bias"}};
+    int rc = check_proj(M, K, N, 4, outs, 1, ins, 3);
+    if (rc) return rc;
+    return launched(attn::launch_gemm_f32(qkv, x, w, bias, nullptr, M, N, K, g_stream),
+                    "attn_qkv_projection launch");
+}
+
+int attn_qkv_projection_bf16(uint16_t* qkv, const uint16_t* x, const uint16_t* w, const float* bias,
+                             int M, int K, int N) {
+    const Span outs[] = {{qkv, nbytes((long long)M * N, 2), "qkv"}};
+    const Span ins[] = {{x, nbytes((long long)M * K, 2), "x"},
+                        {w, nbytes((long long)N * K, 2), "w"},
+                        {bias, nbytes(N, 4), "bias"}};
+    int rc = check_proj(M, K, N, 8, outs, 1, ins, 3);
+    if (rc) return rc;
+    return launched(attn::launch_gemm_bf16(qkv, x, w, bias, nullptr, M, N, K, g_stream),
+                    "attn_qkv_projection_bf16 launch");
+}
+
+int attn_out_projection(float* y, const float* a, const float* w, const float* bias,
+                        const float* residual, int M, int K, int N) {
+    const Span outs[] = {{y, nbytes((long long)M * N, 4), "y"}};
+    const Span ins[] = {{a, nbytes((long long)M * K, 4), "a"},
+                        {w, nbytes((long long)N * K, 4), "w"},
+                        {bias, nbytes(N, 4), "bias"},
+                        {residual, nbytes((long long)M * N, 4), "residual"}};
+    int rc = check_proj(M, K, N, 4, outs, 1, ins, 4);
+    if (rc) return rc;
+    return launched(attn::launch_gemm_f32(y, a, w, bias, residual, M, N, K, g_stream),
+                    "attn_out_projection launch");
+}
+
+int attn_out_projection_bf16(uint16_t* y, const uint16_t* a, const uint16_t* w, const float* bias,
+                             const uint16_t* residual, int M, int K, int N) {
+    const Span outs[] = {{y, nbytes((long long)M * N, 2), "y"}};
+    const Span ins[] = {{a, nbytes((long long)M * K, 2), "a"},
+                        {w, nbytes((long long)N * K, 2), "w"},
+                        {bias, nbytes(N, 4), "bias"},
+                        {residual, nbytes((long long)M * N, 2), "residual"}};
+    int rc = check_proj(M, K, N, 8, outs, 1, ins, 4);
+    if (rc) return rc;
+    return launched(attn::launch_gemm_bf16(y, a, w, bias, residual, M, N, K, g_stream),
+                    "attn_out_projection_bf16 launch");
+}
+
+}  // extern "C"

@@ -236,6 +236,13 @@ hipError_t launch_decode_f16(uint16_t* out, float* lse, const uint16_t* qkv, flo
 hipError_t launch_merge_f16(uint16_t* out, float* lse, const float* o_parts,
                             const float* lse_parts, int P, const Shape& s, hipStream_t st);
 
+// projections with fused epilogues (gemm.hip): y = x w^T + bias (+ res),
+// x (M, K), w (N, K), bias (N), res and y (M, N), row-major
+hipError_t launch_gemm_f32(float* y, const float* x, const float* w, const float* bias,
+                           const float* res, int M, int N, int K, hipStream_t st);
+hipError_t launch_gemm_bf16(uint16_t* y, const uint16_t* x, const uint16_t* w, const float* bias,
+                            const uint16_t* res, int M, int N, int K, hipStream_t st);
+
 // LayerNorm over the rows of an (N, C) matrix (layernorm.hip); the backward
 // uses layernorm_workspace_floats(N, C) floats of workspace
 int layernorm_col_chunks(int N, int C, int* rows_per_chunk);
