@@ -204,19 +204,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
 
 // A kStream x HS 16-bit tile held in registers between its global load and
 // its LDS store (row-major, stride LDR); rows >= T are zero.
-template <int HS>
+template <int HS, int NT = kThreads>
 struct TileRegs {
     static constexpr int CH = HS / 8;                        // 16-byte chunks per row
     static constexpr int TOTAL = kStream * CH;
-    static constexpr int N = (TOTAL + kThreads - 1) / kThreads;
-    static constexpr bool FULL = TOTAL % kThreads == 0;      // every thread holds N chunks
+    static constexpr int N = (TOTAL + NT - 1) / NT;
+    static constexpr bool FULL = TOTAL % NT == 0;            // every thread holds N chunks
     uint4 v[N];
     __device__ __forceinline__ void fetch(const uint16_t* base, size_t ld, int row0, int T, int tid) {
         const uint32_t ldb = (uint32_t)(ld * 2);
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, ldb, row0, T, HS * 2);
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const int e = tid + k * kThreads;
+            const int e = tid + k * NT;
             const int row = e / CH, c = e - (e / CH) * CH;
             const uint32_t off = (uint32_t)row * ldb + 16u * (uint32_t)c;
             v[k] = make_uint4(0u, 0u, 0u, 0u);
@@ -229,7 +229,7 @@ struct TileRegs {
     __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const int e = tid + k * kThreads;
+            const int e = tid + k * NT;
             const int row = e / CH, c = e - (e / CH) * CH;
             if (FULL || e < TOTAL) *reinterpret_cast<uint4*>(lds + row * Geom<HS>::LDR + 8 * c) = v[k];
         }
@@ -261,9 +261,6 @@ __device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal 
 }
 
 // ------------------------------------------------------------------ forward
-// Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
-// stream through LDS 64 at a time (one buffer; the next tile's registers
-// are loaded while the current tile is used).
 // Key range of one forward workgroup and, for a split of the keys over
 // workgroups, where its partial result goes.
 struct KeyPart {
@@ -272,6 +269,9 @@ struct KeyPart {
     float* l;              // PART: log-sum-exp over the range, (B, NH, T) slab
 };
 
+// Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
+// stream through LDS 64 at a time (one buffer; the next tile's registers
+// are loaded while the current tile is used).
 template <typename E, int HS, int QB, bool PART>
 __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __restrict__ out,
                                               float* __restrict__ lse,
