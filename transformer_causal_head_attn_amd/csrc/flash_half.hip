@@ -272,7 +272,7 @@ struct KeyPart {
 // Workgroup: a 4*R-row Q tile of one head (R = 16*QB rows per wave); keys
 // stream through LDS 64 at a time (one buffer; the next tile's registers
 // are loaded while the current tile is used).
-template <typename E, int HS, int QB, bool PART>
+template <typename E, int HS, int QB, bool PART, int NW = 4>
 __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __restrict__ out,
                                               float* __restrict__ lse,
                                               const uint16_t* __restrict__ qkv, int T, int C,
@@ -280,7 +280,7 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
                                               KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
-    constexpr int BM = 4 * R;
+    constexpr int BM = NW * R;
     __shared__ uint16_t Ks[kStream * G::LDR];
     __shared__ uint16_t Vs[kStream * G::LDR];
 
@@ -406,7 +406,7 @@ __device__ __forceinline__ void fwd_half_tile(int tile_, int bh_, uint16_t* __re
         }
     };
 
-    TileRegs<HS> rk, rv;
+    TileRegs<HS, 64 * NW> rk, rv;
     {
         f32x4 sc[QB][4];
         rk.fetch(kbase, C3, kt_lo * kStream, T, L.tid);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void prepass_half_kernel(float* __restric
 // PART: the workgroup takes the query tiles [part.kt_lo, part.kt_hi) only
 // (64-row tiles) and writes its fp32 dk (scaled) and dv sums to the partial
 // slab part.o, rows of 2C: [dk | dv] (a later kernel adds the slabs).
-template <typename E, int HS, int KB, bool PART>
+template <typename E, int HS, int KB, bool PART, int NW = 4>
 __device__ __forceinline__ void bwd_dkdv_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
@@ -509,7 +509,7 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
     float scale_log2, KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * KB;
-    constexpr int BN = 4 * R;
+    constexpr int BN = NW * R;
     __shared__ uint16_t Qs[kStream * G::LDR];
     __shared__ uint16_t dOs[kStream * G::LDR];
     __shared__ float Ls[kStream];
@@ -549,7 +549,7 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
     const int nqt_all = (T + kStream - 1) / kStream;
     const int nqt = PART ? min(nqt_all, part.kt_hi) : nqt_all;
     const int qt0 = max(causal ? (kvt * BN) / kStream : 0, PART ? part.kt_lo : 0);
-    TileRegs<HS> rq, rd;
+    TileRegs<HS, 64 * NW> rq, rd;
     float rl = 0.f, rD = 0.f;
     // lse and D of the tile's rows are loaded raw and only transformed when
     // stored, so nothing waits for them before the next step
@@ -682,7 +682,7 @@ __device__ __forceinline__ void bwd_dkdv_half_tile(
 // PART: the workgroup takes the key tiles [part.kt_lo, part.kt_hi) only and
 // writes its fp32 dq sum (scaled) to the partial slab part.o (B, T, C); the
 // workgroup of the first key range also writes D.
-template <typename E, int HS, int QB, bool PART>
+template <typename E, int HS, int QB, bool PART, int NW = 4>
 __device__ __forceinline__ void bwd_dq_half_tile(
     int tile_, int bh_, uint16_t* __restrict__ dqkv, float* __restrict__ Dws,
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ qkv,
@@ -690,7 +690,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     int causal, float scale, float scale_log2, KeyPart part) {
     using G = Geom<HS>;
     constexpr int R = 16 * QB;
-    constexpr int BM = 4 * R;
+    constexpr int BM = NW * R;
     __shared__ uint16_t Ks[kStream * G::LDR];
     __shared__ uint16_t Vs[kStream * G::LDR];
 
@@ -740,7 +740,7 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     const int nkt_tile = causal ? min(nkt_all, (qt * BM + BM - 1) / kStream + 1) : nkt_all;
     const int kt_lo = PART ? part.kt_lo : 0;
     const int nkt = PART ? min(nkt_tile, part.kt_hi) : nkt_tile;
-    TileRegs<HS> rk, rv;
+    TileRegs<HS, 64 * NW> rk, rv;
     rk.fetch(kbase, C3, kt_lo * kStream, T, L.tid);
     rv.fetch(vbase, C3, kt_lo * kStream, T, L.tid);
     wait_global_loads();
@@ -835,17 +835,19 @@ __device__ __forceinline__ void bwd_dq_half_tile(
 // GPT-2, ViT and long-context shapes: 2 beats 1 and 4)
 // ------------------------------------------------------------- kernels
 // Each runs its tile function on the tile deal_tile gives it.
-template <typename E, int HS, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void fwd_half_kernel(uint16_t* __restrict__ out,
+// NW waves per workgroup: 4 (128-row tiles), or 8 (256-row tiles: one tile
+// per head for T <= 256, so the streamed K and V are read once per head)
+template <typename E, int HS, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : NW == 8 ? 4 : 3))) void fwd_half_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, int causal,
                                                             float scale_log2, Deal deal) {
-    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    const int nt = (T + 16 * QB * NW - 1) / (16 * QB * NW);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
-    fwd_half_tile<E, HS, QB, false>(t, bh, out, lse, qkv, T, C, NH, causal, scale_log2,
-                                    KeyPart{0, 0, nullptr, nullptr});
+    fwd_half_tile<E, HS, QB, false, NW>(t, bh, out, lse, qkv, T, C, NH, causal, scale_log2,
+                                        KeyPart{0, 0, nullptr, nullptr});
 }
 
 // Split-KV forward: workgroup (rank, bh) of a grid of nqt * nchunk * BH
@@ -878,30 +880,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 
                                    part);
 }
 
-template <typename E, int HS, int KB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_half_kernel(
+template <typename E, int HS, int KB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_half_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse,
     const float* __restrict__ Dws, int T, int C, int NH, int causal, float scale,
     float scale_log2, Deal deal) {
-    const int nt = (T + 64 * KB - 1) / (64 * KB);
+    const int nt = (T + 16 * KB * NW - 1) / (16 * KB * NW);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, false, deal, bh, t);
-    bwd_dkdv_half_tile<E, HS, KB, false>(t, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal, scale,
-                                         scale_log2, KeyPart{0, 0, nullptr, nullptr});
+    bwd_dkdv_half_tile<E, HS, KB, false, NW>(t, bh, dqkv, dout, qkv, lse, Dws, T, C, NH, causal,
+                                             scale, scale_log2, KeyPart{0, 0, nullptr, nullptr});
 }
 
-template <typename E, int HS, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void bwd_dq_half_kernel(
+template <typename E, int HS, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(HS >= 128 ? 2 : 3))) void bwd_dq_half_kernel(
     uint16_t* __restrict__ dqkv, float* __restrict__ Dws, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
     float scale_log2, Deal deal) {
-    const int nt = (T + 64 * QB - 1) / (64 * QB);
+    const int nt = (T + 16 * QB * NW - 1) / (16 * QB * NW);
     int bh, t;
     deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
-    bwd_dq_half_tile<E, HS, QB, false>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal,
-                                       scale, scale_log2, KeyPart{0, 0, nullptr, nullptr});
+    bwd_dq_half_tile<E, HS, QB, false, NW>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal,
+                                           scale, scale_log2, KeyPart{0, 0, nullptr, nullptr});
 }
 
 // Split backward.  dQ: workgroup (rank, bh) of nqt * nchunk * BH takes Q
@@ -996,17 +998,33 @@ static_assert(64 * kQB == kFwdHalfRows, "forward Q tile rows");
 // registers, more resident waves; measured faster on the long-context shape)
 constexpr int kb_for(int hs) { return hs >= 128 ? 1 : 2; }
 
-template <typename E, int HS>
-hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
+// Short sequences (128 < T <= 256, hs <= 64): the forward runs 8-wave
+// workgroups of 256 rows, one per head, so every K and V row is read once
+// per head instead of once per 128-row tile (ViT-B/16, T = 196: 45.5 ->
+// 39.2 us).  The dQ and dK/dV kernels keep 4 waves: at 8 their register
+// needs leave one workgroup per CU (dQ 63 -> 72 us, dK/dV 74 -> 84 us; dQ
+// held to 4 waves per SIMD spills, 83 us).
+template <int HS>
+bool short_seq(const Shape& s) { return HS <= 64 && s.T <= 256 && s.T > 128; }
+
+template <typename E, int HS, int NW>
+hipError_t fwd_half_nw(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
                        hipStream_t st) {
-    constexpr int BM = 64 * kQB;
+    constexpr int BM = 16 * kQB * NW;
     const int nqt = (s.T + BM - 1) / BM;
     const unsigned grid = (unsigned)(nqt * s.B * s.NH);
     const float scale_log2 = (float)(1.0 / sqrt((double)HS)) * kLog2e;
-    const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB>>(kThreads);
-    hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, out, lse,
-                       qkv, s.T, s.C, s.NH, s.causal, scale_log2, deal);
+    const Deal deal = deal_for<fwd_half_kernel<E, HS, kQB, NW>>(64 * NW);
+    hipLaunchKernelGGL((fwd_half_kernel<E, HS, kQB, NW>), dim3(grid), dim3(64 * NW), 0, st, out,
+                       lse, qkv, s.T, s.C, s.NH, s.causal, scale_log2, deal);
     return hipGetLastError();
+}
+
+template <typename E, int HS>
+hipError_t fwd_half_hs(uint16_t* out, float* lse, const uint16_t* qkv, const Shape& s,
+                       hipStream_t st) {
+    if (short_seq<HS>(s)) return fwd_half_nw<E, HS, 8>(out, lse, qkv, s, st);
+    return fwd_half_nw<E, HS, 4>(out, lse, qkv, s, st);
 }
 
 template <typename E, int HS>
@@ -1075,33 +1093,45 @@ hipError_t prepass_half_hs(float* D, const uint16_t* dout, const uint16_t* out, 
     return hipGetLastError();
 }
 
-template <typename E, int HS>
-hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+template <typename E, int HS, int NW>
+hipError_t dkdv_half_nw(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                         const float* lse, const float* D, const Shape& s, hipStream_t st) {
     constexpr int KB = kb_for(HS);
-    constexpr int BN = 64 * KB;
+    constexpr int BN = 16 * KB * NW;
     const int nt = (s.T + BN - 1) / BN;
     const unsigned grid = (unsigned)(nt * s.B * s.NH);
     const float scale = (float)(1.0 / sqrt((double)HS));
-    const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB>>(kThreads);
-    hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
-                       dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
+    const Deal deal = deal_for<bwd_dkdv_half_kernel<E, HS, KB, NW>>(64 * NW);
+    hipLaunchKernelGGL((bwd_dkdv_half_kernel<E, HS, KB, NW>), dim3(grid), dim3(64 * NW), 0, st,
+                       dqkv, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
                        deal);
+    return hipGetLastError();
+}
+
+template <typename E, int HS>
+hipError_t dkdv_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                        const float* lse, const float* D, const Shape& s, hipStream_t st) {
+    return dkdv_half_nw<E, HS, 4>(dqkv, dout, qkv, lse, D, s, st);
+}
+
+template <typename E, int HS, int NW>
+hipError_t dq_half_nw(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
+                      const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
+    constexpr int BM = 16 * kQB * NW;
+    const int nt = (s.T + BM - 1) / BM;
+    const unsigned grid = (unsigned)(nt * s.B * s.NH);
+    const float scale = (float)(1.0 / sqrt((double)HS));
+    const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB, NW>>(64 * NW);
+    hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB, NW>), dim3(grid), dim3(64 * NW), 0, st,
+                       dqkv, D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale,
+                       scale * kLog2e, deal);
     return hipGetLastError();
 }
 
 template <typename E, int HS>
 hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                       const uint16_t* out, const float* lse, const Shape& s, hipStream_t st) {
-    constexpr int BM = 64 * kQB;
-    const int nt = (s.T + BM - 1) / BM;
-    const unsigned grid = (unsigned)(nt * s.B * s.NH);
-    const float scale = (float)(1.0 / sqrt((double)HS));
-    const Deal deal = deal_for<bwd_dq_half_kernel<E, HS, kQB>>(kThreads);
-    hipLaunchKernelGGL((bwd_dq_half_kernel<E, HS, kQB>), dim3(grid), dim3(kThreads), 0, st, dqkv,
-                       D, dout, qkv, out, lse, s.T, s.C, s.NH, s.causal, scale, scale * kLog2e,
-                       deal);
-    return hipGetLastError();
+    return dq_half_nw<E, HS, 4>(dqkv, D, dout, qkv, out, lse, s, st);
 }
 
 }  // namespace
