@@ -47,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd causal TFLOP/s and % MFMA peak, B8 T1024 C768 NH12"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_causal_head_attn_amd", "csrc")
 KERNEL_SOURCE = {"f32": "flash_f32.hip", "f32_ds": "flash_f32.hip", "bf16": "flash_half.hip", "f16": "flash_half.hip"}
@@ -119,8 +119,9 @@ def device_peaks():
         return {"cus": cus, "max_clock_mhz": clk,
                 "fp32_mfma_tflops": round(cus * clk * 1e6 * 4 * 64 / 1e12, 1),
                 "bf16_mfma_tflops": round(cus * clk * 1e6 * 4 * 1024 / 1e12, 1),
+                "fp8_mfma_tflops": round(cus * clk * 1e6 * 4 * 2048 / 1e12, 1),
                 "source": "rocminfo: compute units x max engine clock x matrix-core flops "
-                          "per clock (fp32 256, bf16/fp16 4096 per CU)"}
+                          "per clock (fp32 256, bf16/fp16 4096, fp8 8192 per CU)"}
     return None
 
 
@@ -461,6 +462,29 @@ def run_splitkv(la, torch, steps=20, warmup_ms=100.0):
     return res
 
 
+def run_fp8_forward(la, torch, keys=(3, 4, 5), steps=20, warmup_ms=100.0):
+    """The fp8 forward (E4M3 q, k, v; bf16 out) on the inputs of workloads
+    `keys` rounded to E4M3, in TFLOP/s of the forward's useful 4*hs*P*B*NH
+    flops against the fp8 matrix-core peak, beside the bf16 forward on the
+    same (E4M3-valued) inputs."""
+    from workloads import WORKLOADS, workload_inputs
+    res = []
+    for key in keys:
+        w = WORKLOADS[key]
+        q8 = workload_inputs(w, "fp8")[0].cuda()
+        qb = q8.to(torch.bfloat16)
+        B, T, C, NH, c = w.B, w.T, w.C, w.NH, int(w.causal)
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+        ms8 = _time_call(torch, lambda: la.attn_forward_fp8(out, lse, q8, B, T, C, NH, c), steps, warmup_ms)
+        msb = _time_call(torch, lambda: la.attn_forward_bf16(out, lse, qb, B, T, C, NH, c), steps, warmup_ms)
+        tf8 = w.flops_fwd / (ms8 * 1e-3) / 1e12
+        res.append({"workload": f"{w.name} {w.label().rsplit(' ', 1)[0]} fp8", "fp8_us": round(ms8 * 1e3, 2),
+                    "tflops": round(tf8, 1), "frac_fp8_mfma_peak": round(tf8 / PEAK_TFLOPS["fp8"], 4),
+                    "bf16_forward_us": round(msb * 1e3, 2)})
+    return res
+
+
 def run_projections(la, torch, M, C, steps=20, warmup_ms=100.0):
     """The QKV projection (M x C times C x 3C, + bias) and the output
     projection (M x C times C x C, + bias + residual) at the workload's
@@ -763,6 +787,7 @@ def main():
     if not args.no_extra:
         line["splitkv"] = run_splitkv(la, torch)
         line["projections"] = run_projections(la, torch, w.B * w.T, w.C)
+        line["fp8_forward"] = run_fp8_forward(la, torch)
 
     if not args.no_extra:
         line["decode"] = [run_decode(la, torch, w, dtype, 50, 200),

@@ -283,6 +283,25 @@ int attn_backward_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t*
                            int B, int T, int C, int NH, int causal);
 
 /*
+ * Fused forward with 8-bit floating-point q, k, v ("LLM Systems 10 & 11:
+ * Accelerating Transformer Training and Inference", section 1.3,
+ * Mixed-precision Calculation, which names FP8 beside FP16 for the forward
+ * and backward).  qkv holds OCP FP8 E4M3 bytes (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; largest finite magnitude 448; 0x7F and 0xFF are
+ * NaN), packed (B, T, 3C) like the other calls.  Every product accumulates
+ * in fp32 and the softmax runs in fp32; the probabilities enter the P V
+ * product rounded to E4M3 (round to nearest even; below 2^-10 of a row's
+ * running maximum they become 0), and the row sums are taken over the same
+ * rounded values.  out is bfloat16 (B, T, C), round to nearest even; lse is
+ * fp32 (B, NH, T) as for attn_forward.  Forward only: the backward runs in
+ * bf16 or fp16 (attn_backward_bf16 / _f16 with a 16-bit copy of qkv).
+ * Requirements and errors as for attn_forward_bf16 (qkv 16-byte aligned).
+ * Nothing is allocated.
+ */
+int attn_forward_fp8(uint16_t* out, float* lse, const uint8_t* qkv,
+                     int B, int T, int C, int NH, int causal);
+
+/*
  * Materialised forward, fp32, as the pages' reference does it: writes the
  * full unscaled preatt = q.k (B,NH,T,T) including masked entries, att
  * (B,NH,T,T) with masked entries exactly 0, and out (B,T,C).

@@ -7,7 +7,16 @@ import torch
 # Tolerances on |gpu - oracle| <= atol + rtol * |oracle|, elementwise.
 # fp16 (not in the stated targets) gets ten of its rounding steps, 2^-11 each:
 # the same margin over one rounding that the bf16 bound leaves over bf16's 2^-8.
-TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2), "f16": (5e-3, 5e-3)}
+# fp8 (forward only, no stated target): q, k, v in E4M3 and P rounded to E4M3
+# (3 mantissa bits, relative step 2^-3) before the P V product, out in bf16.
+# A model of that rounding (P = E4M3(exp(s - max)), normaliser over the
+# rounded P, out rounded to bf16; tests/test_parity_fp8_model.py) errs by at
+# most 0.046 in out and 0.016 in lse on heads of the GPT-2, ViT and
+# long-context workloads; the bounds leave ~2x (out) and ~4x (lse).  The lse
+# bound 0.065 is also log(1 / (1 - 2^-4)): the normaliser's relative error
+# when every weight rounds by the largest E4M3 step in one direction.
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-2), "f16": (5e-3, 5e-3), "fp8": (0.1, 0.1)}
+LSE_ATOL_FP8 = 0.065
 
 
 def assert_close(gpu, ref, dtype: str, what: str):
@@ -41,13 +50,15 @@ def assert_close(gpu, ref, dtype: str, what: str):
 # the rounded P, D from the rounded out) on heads of the GPT-2, ViT and
 # long-context workloads: 0.064 elementwise and 0.020 row-wise
 # (tests/test_parity_power.py).  fp16 rounds 8x finer; its constants are 4x
-# smaller.  Exempt, and held to the stated bound only: the dq rows of causal
+# smaller.  fp8 (forward only): the E4M3 rounding model reaches 0.132
+# elementwise and 0.045 row-wise (tests/test_parity_fp8_model.py); the
+# constants leave 3x and 2.7x.  Exempt, and held to the stated bound only: the dq rows of causal
 # queries with fewer than FEW_KEYS keys.  There sum_j dS[t,j] = 0 (exactly,
 # in exact arithmetic) cancels over a few terms, and the rounding of the
 # normaliser and of out (through D = dout . out) leaves the row with a large
 # relative error: up to 0.27 of its norm in the rounding model, at t = 1
 # (2 keys), and never past t = 2 on the GPT-2 layer's 96 heads.
-ROW_TOL = {"bf16": (0.25, 0.05), "f16": (0.0625, 0.0125)}
+ROW_TOL = {"bf16": (0.25, 0.05), "f16": (0.0625, 0.0125), "fp8": (0.4, 0.12)}
 FEW_KEYS = 16
 # Absolute floor of both checks (per element; sqrt(hs) times it per row), far
 # below any gradient the workloads produce: a head whose reference is exactly

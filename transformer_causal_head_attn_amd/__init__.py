@@ -19,7 +19,7 @@ from ._binding import (  # noqa: F401
     attn_backward_ds_bytes, attn_backward_dkdv_ds, attn_backward_dq_ds,
     attn_backward_preprocess, attn_backward_preprocess_bf16, attn_decode, attn_decode_bf16, attn_decode_f16,
     attn_backward_dkdv_f16, attn_backward_dq_f16, attn_backward_f16,
-    attn_backward_preprocess_f16, attn_forward_f16,
+    attn_backward_preprocess_f16, attn_forward_f16, attn_forward_fp8, forward_fp8,
     attn_forward, attn_forward_bf16, attn_forward_materialized, attn_last_error, attn_merge,
     attn_merge_bf16, attn_merge_f16, attn_release, attn_set_stream, backward, backward_materialized, decode,
     forward, forward_materialized, load, merge,

@@ -29,7 +29,7 @@ EXPORTS = (
     "attn_backward_ds_bytes", "attn_backward_dkdv_ds", "attn_backward_dq_ds",
     "attn_forward_bf16", "attn_backward_bf16",
     "attn_backward_preprocess_bf16", "attn_backward_dkdv_bf16", "attn_backward_dq_bf16",
-    "attn_forward_f16", "attn_backward_f16",
+    "attn_forward_f16", "attn_backward_f16", "attn_forward_fp8",
     "attn_forward_splitkv_chunk", "attn_forward_splitkv_bytes",
     "attn_forward_splitkv_bf16", "attn_forward_splitkv_f16",
     "attn_backward_splitkv_bytes", "attn_backward_splitkv_bf16", "attn_backward_splitkv_f16",
@@ -75,6 +75,7 @@ def load(path: str | None = None):
                            ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
                            ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6),
                            ("attn_forward_f16", 3), ("attn_backward_f16", 5),
+                           ("attn_forward_fp8", 3),
                            ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6)):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * nptr + [i] * 5
@@ -348,6 +349,23 @@ def attn_forward_bf16(out, lse, qkv, B, T, C, NH, causal) -> None:
     h, f = torch.bfloat16, torch.float32
     _call("attn_forward_bf16", _check(out, "out", h, B * T * C), _check(lse, "lse", f, B * NH * T),
           _check(qkv, "qkv", h, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def attn_forward_fp8(out, lse, qkv, B, T, C, NH, causal) -> None:
+    """qkv: torch.float8_e4m3fn (OCP E4M3); out: bfloat16; lse: float32."""
+    _call("attn_forward_fp8", _check(out, "out", torch.bfloat16, B * T * C),
+          _check(lse, "lse", torch.float32, B * NH * T),
+          _check(qkv, "qkv", torch.float8_e4m3fn, B * T * 3 * C), *_dims(B, T, C, NH, causal))
+
+
+def forward_fp8(qkv: torch.Tensor, NH: int, causal: bool = True):
+    """Allocate (out bf16, lse fp32) with torch and run the fp8 forward on a
+    float8_e4m3fn qkv."""
+    B, T, C = _shape(qkv, NH)
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device=qkv.device)
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device=qkv.device)
+    attn_forward_fp8(out, lse, qkv, B, T, C, NH, int(causal))
+    return out, lse
 
 
 def attn_backward_bf16(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> None:

@@ -359,6 +359,17 @@ int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv, int B, int
                     "attn_forward_bf16 launch");
 }
 
+int attn_forward_fp8(uint16_t* out, float* lse, const uint8_t* qkv, int B, int T, int C, int NH,
+                     int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{out, nbytes(BT * C, 2), "out"}, {lse, nbytes(BT * NH, 4), "lse"}};
+    const Span ins[] = {{qkv, nbytes(BT * 3 * C, 1), "qkv"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 2, ins, 1, false);
+    if (rc) return rc;
+    return launched(attn::launch_fwd_fp8(out, lse, qkv, shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_forward_fp8 launch");
+}
+
 int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                        const uint16_t* out, const float* lse, int B, int T, int C, int NH,
                        int causal) {

@@ -128,6 +128,28 @@ __device__ __forceinline__ int snake_block(Deal deal) {
     return idx;
 }
 
+// Causal tiles carry unequal work (tile i of a Q-tile kernel sees i+1 key
+// tiles, tile j of a K/V-tile kernel nt-j query tiles).  Tiles run one per
+// workgroup, heaviest first (the longest-first order of kernel 8 in llm.c's
+// attention_backward.cu), dealt to the CUs like a snake draft: workgroups
+// that are resident together (ids c, c + ncu, c + 2 ncu, ... share a CU when
+// the whole round fits) take the sorted list in alternating directions, so
+// a CU that got one of the heaviest tiles in the first round gets one of the
+// lightest of the second.  The reversal keeps id % 8, the XCD a workgroup
+// is dispatched to, and a wrong guess about placement only costs balance.
+// Workgroups beyond the resident rounds take the lighter tiles as slots
+// free.  (Running tiles i and nt-1-i back to back in one workgroup, which
+// equalises the work, measured no better on the GPT-2 layer and 2% slower
+// at long context.)  Consecutive workgroup ids walk the heads, so all tiles
+// of a head land on one XCD (one L2) whenever B*NH is a multiple of 8.
+__device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal deal, int& bh,
+                                          int& tile) {
+    const int idx = snake_block(deal);
+    const int rank = idx / BH;
+    bh = idx - rank * BH;
+    tile = heavy_high ? nt - 1 - rank : rank;
+}
+
 // CUs and resident workgroups per CU of `threads`-thread workgroups for a
 // kernel (one occupancy query per kernel and device, cached; host threads may
 // race to fill an entry, all with the same value).  A failed query is
@@ -212,6 +234,9 @@ hipError_t launch_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t*
                            const float* lse, const float* D, const Shape& s, hipStream_t st);
 hipError_t launch_dq_f16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                          const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
+// fp8 forward (OCP E4M3 q, k, v as raw bytes; bfloat16 out, fp32 lse)
+hipError_t launch_fwd_fp8(uint16_t* out, float* lse, const uint8_t* qkv, const Shape& s,
+                          hipStream_t st);
 // materialised fp32 path
 hipError_t launch_fwd_materialized(float* out, float* preatt, float* att, const float* qkv,
                                    const Shape& s, hipStream_t st);

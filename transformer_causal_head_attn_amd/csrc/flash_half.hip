@@ -238,28 +238,6 @@ struct TileRegs {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// Causal tiles carry unequal work (tile i of a Q-tile kernel sees i+1 key
-// tiles, tile j of a K/V-tile kernel nt-j query tiles).  Tiles run one per
-// workgroup, heaviest first (the longest-first order of kernel 8 in llm.c's
-// attention_backward.cu), dealt to the CUs like a snake draft: workgroups
-// that are resident together (ids c, c + ncu, c + 2 ncu, ... share a CU when
-// the whole round fits) take the sorted list in alternating directions, so
-// a CU that got one of the heaviest tiles in the first round gets one of the
-// lightest of the second.  The reversal keeps id % 8, the XCD a workgroup
-// is dispatched to, and a wrong guess about placement only costs balance.
-// Workgroups beyond the resident rounds take the lighter tiles as slots
-// free.  (Running tiles i and nt-1-i back to back in one workgroup, which
-// equalises the work, measured no better on the GPT-2 layer and 2% slower
-// at long context.)  Consecutive workgroup ids walk the heads, so all tiles
-// of a head land on one XCD (one L2) whenever B*NH is a multiple of 8.
-__device__ __forceinline__ void deal_tile(int BH, int nt, bool heavy_high, Deal deal, int& bh,
-                                          int& tile) {
-    const int idx = snake_block(deal);
-    const int rank = idx / BH;
-    bh = idx - rank * BH;
-    tile = heavy_high ? nt - 1 - rank : rank;
-}
-
 // ------------------------------------------------------------------ forward
 // Key range of one forward workgroup and, for a split of the keys over
 // workgroups, where its partial result goes.

@@ -9,8 +9,8 @@ Recipe (the same bytes go to the GPU and to the oracle):
     with ``torch.Generator('cpu').manual_seed(seed)`` and ``torch.randn`` in
     float32, dout then multiplied by its standard deviation (1 or 0.1);
   * the bf16 workloads round those float32 samples to bfloat16 (and the fp16
-    runs to IEEE half) with torch's round-to-nearest-even cast; the oracle
-    then sees the rounded values;
+    runs to IEEE half, the fp8 runs to OCP FP8 E4M3) with torch's
+    round-to-nearest-even cast; the oracle then sees the rounded values;
   * seeds are 1000 + k for qkv and 2000 + k for dout, for workload k.
 
 The shapes are the ones the pages use: the GPT-2 small attention layer of the
@@ -72,7 +72,7 @@ WORKLOADS = {
 
 def randn(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tensor:
     """float32 N(0, std^2) samples from a seeded CPU generator, optionally
-    rounded to bfloat16 or float16 (round to nearest even)."""
+    rounded to bfloat16, float16 or float8 E4M3 (round to nearest even)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
@@ -82,6 +82,8 @@ def randn(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> torch.Tenso
         return x.to(torch.bfloat16)
     if dtype == "f16":
         return x.to(torch.float16)
+    if dtype == "fp8":
+        return x.to(torch.float8_e4m3fn)
     if dtype != "f32":
         raise ValueError(dtype)
     return x
@@ -97,7 +99,8 @@ def randn_device(shape, seed: int, std: float = 1.0, dtype: str = "f32",
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
     if std != 1.0:
         x = x * std
-    return x.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype])
+    return x.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+                 "fp8": torch.float8_e4m3fn}[dtype])
 
 
 def make_inputs(B: int, T: int, C: int, dtype: str = "f32", seed: int = 0,
