@@ -24,13 +24,13 @@
 //    from a row-major LDS tile (ds_read_b64); Q stays in registers.
 //  * O^T = V^T P^T: P comes straight from the score accumulators (lane
 //    group g holds keys 16n + 4g + i, blocks n = 2t, 2t + 1 per 32-key step)
-//    and the matching V operand is two 4-byte reads of a transposed V tile
-//    (V^T, one row per head dimension) that the tile store writes byte by
-//    byte, so no transposed read is needed.
+//    and the matching V operand is one ds_read_b64_tr_b8 transposed read of
+//    a row-major V tile whose 16-byte groups are swizzled per row.
 //  * Every wave owns 32 query rows (two 16-row blocks), four waves a
 //    128-row Q tile; keys stream through LDS 64 at a time, the next tile
 //    loaded into registers while the current one is used.
 #include "common.hpp"
+
 
 namespace attn {
 namespace {
@@ -50,7 +50,17 @@ __device__ __forceinline__ f32x4 mfma8(fp8x8 a, fp8x8 b, f32x4 c) {
 template <int HS>
 struct Geom8 {
     static constexpr int LDK = HS + 8;         // K tile row stride (bytes): 16 rows -> 16 bank pairs
-    static constexpr int LDV = kStream + 4;    // V^T tile row stride (bytes): odd word stride
+    static constexpr int LDV = HS;             // V tile row stride (bytes): dense, swizzled
+    // V rows: 16-byte group q of row r is stored at group q ^ fv(r); the
+    // eight rows one transposed read touches (4g + 0..3 and 16 + 4g + 0..3
+    // of a 32-key step) then fall on eight different bank groups (hs = 16
+    // has one group per row and keeps a two-way conflict)
+    static __device__ __forceinline__ int fv(int r) {
+        if constexpr (HS >= 128) return (r & 3) | (((r >> 4) & 1) << 2);
+        else if constexpr (HS == 64) return ((r >> 1) & 1) | (((r >> 4) & 1) << 1);
+        else if constexpr (HS == 32) return (r >> 4) & 1;
+        else return 0;
+    }
     static constexpr int KSTEPS = HS >= 32 ? HS / 32 : 1;
     static constexpr int MB = HS / 16;
     static constexpr int CH = HS / 16;         // 16-byte chunks per global row
@@ -108,19 +118,14 @@ struct Tile8 {
             }
         }
     }
-    // transposed V tile: byte d of the chunk (head dimension 16c + d of key
-    // `row`) goes to V^T[16c + d][row]
-    __device__ __forceinline__ void store_transposed(uint8_t* lds, int tid) const {
+    // swizzled row-major V tile (one 16-byte store per chunk)
+    __device__ __forceinline__ void store_swizzled(uint8_t* lds, int tid) const {
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             const int e = tid + k * kThreads;
             const int row = e / G::CH, c = e - row * G::CH;
-            if (FULL || e < TOTAL) {
-                const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-                uint8_t* p = lds + (16 * c) * G::LDV + row;
-#pragma unroll
-                for (int d = 0; d < 16; ++d) p[d * G::LDV] = (uint8_t)(w[d >> 2] >> (8 * (d & 3)));
-            }
+            if (FULL || e < TOTAL)
+                *reinterpret_cast<uint4*>(lds + row * G::LDV + 16 * (c ^ G::fv(row))) = v[k];
         }
     }
 };
@@ -133,6 +138,31 @@ __device__ __forceinline__ fp8x8 pack8(const f32x4& x, const f32x4& y) {
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hi, true);
     return (fp8x8)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// The V^T operand of step t (keys 32t .. 32t + 31), head dimensions 16mb ..
+// 16mb + 15, from the swizzled row-major V tile with one transposed read.
+// ds_read_b64_tr_b8 (lane layout probed on the GPU): within each 16-lane
+// group, lane j receives byte j % 8 of the 8-byte blocks addressed by lanes
+// 2e + j / 8 (e = 0..3) and 8 + 2(e - 4) + j / 8 (e = 4..7).  So lane L of
+// the group addresses key row key(L / 2) at bytes 16mb + 8(L % 2) .. + 7,
+// and lane j ends with V[key(e)][16mb + j] in byte e, where key(e) is the
+// score accumulators' key order: 32t + 4g + e for e < 4, 32t + 16 + 4g +
+// e - 4 for e >= 4 (g = lane / 16).
+template <int HS>
+__device__ __forceinline__ fp8x8 v_operand(const uint8_t* Vs, int t, int mb) {
+    using G = Geom8<HS>;
+    const int lane = threadIdx.x & 63;
+    const int L = lane & 15, g = lane >> 4;
+    const int e = L >> 1;
+    const int row = 32 * t + 4 * g + (e & 3) + 16 * (e >> 2);
+    const uint8_t* p = Vs + row * G::LDV + 16 * (mb ^ G::fv(row)) + 8 * (L & 1);
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+    uint64_t u;
+    __builtin_memcpy(&u, &r, 8);
+    return (fp8x8)u;
 }
 
 // fp32 -> bfloat16 bits, round to nearest even (finite inputs)
@@ -152,7 +182,7 @@ __device__ __forceinline__ void fwd_fp8_tile(int qt, int bh, uint16_t* __restric
     using G = Geom8<HS>;
     constexpr int R = 16 * kQB;
     __shared__ __attribute__((aligned(16))) uint8_t Ks[kStream * G::LDK];
-    __shared__ __attribute__((aligned(16))) uint8_t Vt[HS * G::LDV];
+    __shared__ __attribute__((aligned(16))) uint8_t Vs[kStream * G::LDV];
 
     const int tid = threadIdx.x;
     const int r16 = l & 15, g = l >> 4;
@@ -199,7 +229,7 @@ __device__ __forceinline__ void fwd_fp8_tile(int qt, int bh, uint16_t* __restric
     for (int j = 0; j < nkt; ++j) {
         __syncthreads();
         rk.store_rows(Ks, tid);
-        rv.store_transposed(Vt, tid);
+        rv.store_swizzled(Vs, tid);
         __syncthreads();
         if (j + 1 < nkt) {
             rk.fetch(kbase, C3, (j + 1) * kStream, T, tid);
@@ -210,6 +240,10 @@ __device__ __forceinline__ void fwd_fp8_tile(int qt, int bh, uint16_t* __restric
         // S^T = K Q^T: sc[qb][n][i] is the score of key 16n + 4g + i with
         // query r0 + 16qb + r16
         f32x4 sc[kQB][4];
+        // hs = 128: the score products run at raised issue priority, as in
+        // the 16-bit forward (long-context forward 222 -> 208 us; at hs = 64
+        // 3% slower, so only there)
+        if constexpr (HS >= 128) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int np = 0; np < 4; np += 2) {
 #pragma unroll
@@ -228,6 +262,7 @@ __device__ __forceinline__ void fwd_fp8_tile(int qt, int bh, uint16_t* __restric
             }
         }
 
+        if constexpr (HS >= 128) __builtin_amdgcn_s_setprio(0);
         const int k0 = j * kStream;
         const bool edge = (k0 + kStream > T) || (causal && k0 + kStream - 1 > r0);
 #pragma unroll
@@ -276,10 +311,7 @@ __device__ __forceinline__ void fwd_fp8_tile(int qt, int bh, uint16_t* __restric
             }
 #pragma unroll
             for (int mb = 0; mb < G::MB; ++mb) {
-                const uint8_t* vr = Vt + (16 * mb + r16) * G::LDV + 32 * t + 4 * g;
-                const uint32_t a = *reinterpret_cast<const uint32_t*>(vr);
-                const uint32_t c = *reinterpret_cast<const uint32_t*>(vr + 16);
-                const fp8x8 vop = (fp8x8)(((uint64_t)c << 32) | (uint64_t)a);
+                const fp8x8 vop = v_operand<HS>(Vs, t, mb);
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) o[qb][mb] = mfma8(vop, pb[qb], o[qb][mb]);
             }
