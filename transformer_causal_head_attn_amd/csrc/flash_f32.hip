@@ -43,6 +43,7 @@
 //    more than writing dS once and reading it back.
 #include "common.hpp"
 
+
 namespace attn {
 namespace {
 
@@ -740,8 +741,11 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
     }
 }
 
+// hs <= 64 without the dS store: three workgroups per CU (162 VGPRs; the
+// compiler's own choice was 174, two per CU): GPT-2 layer dK/dV 220 -> 214
+// us, same bits.  With the store the same cap spills.
 template <int HS, bool STORE_DS>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
+__global__ __launch_bounds__(kThreads, HS >= 128 || STORE_DS ? 1 : 3) void bwd_dkdv_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
     const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
     int T, int C, int NH, int causal, float scale, float scale_log2, int paired, Deal deal) {
