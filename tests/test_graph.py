@@ -111,3 +111,30 @@ def test_captured_fused_backward_survives_workspace_growth(la, dtype):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(dqkv, ref), f"replay {r} after growth differs from the eager result"
+
+
+def test_fp8_forward_graph_replays(la):
+    """attn_forward_fp8 allocates nothing and clears nothing, so it can be
+    captured; three replays with eager work in between give the eager bits."""
+    B, T, C, NH = 2, 150, 256, 4
+    print(f"\n[case] graph replay fp8 forward B{B} T{T} C{C} NH{NH}", flush=True)
+    q8 = make_inputs(B, T, C, "fp8", seed=74)[0].cuda()
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, NH, T), device="cuda")
+    la.attn_forward_fp8(out, lse, q8, B, T, C, NH, 1)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.attn_forward_fp8(out, lse, q8, B, T, C, NH, 1)
+    other = make_inputs(B, 300, C, "fp8", seed=75)[0].cuda()
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), f"replay {r}: out"
+        assert torch.equal(lse, ref[1]), f"replay {r}: lse"
+        la.forward_fp8(other, NH, True)
+        torch.cuda.synchronize()
