@@ -54,3 +54,23 @@ def test_offsets_past_32_bits(la, oracle_mod, dtype):
         assert_close(dec_lse[b, h].cpu(), rl[0, 0, T - 1], dtype, f"decode lse head {(b, h)}")
     del qkv, dout, out, lse, dqkv
     torch.cuda.empty_cache()
+
+
+def test_fp8_forward_offsets_past_32_bits(la, oracle_mod):
+    """fp8 qkv of more than 2^32 bytes (one byte per element): the last
+    sequences' offsets need 64-bit arithmetic in the fp8 forward too."""
+    from helpers import LSE_ATOL_FP8, assert_close_scaled
+    B, T, C, NH = 1850, 1024, 768, 12        # B*T*3C = 4.4e9 bytes
+    print(f"\n[case] fp8 forward B{B} T{T} C{C} NH{NH}", flush=True)
+    assert B * T * 3 * C > 2 ** 32
+    qkv = randn_device((B, T, 3 * C), 93, 1.0, "fp8")
+    out, lse = la.forward_fp8(qkv, NH, True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (1299, 7), (B - 1, NH - 1)]:
+        qs = _head(qkv, b, h, NH, True)
+        ro, rl = oracle_mod.forward(qs, 1, True)
+        assert_close_scaled(_head(out, b, h, NH, False), ro, "fp8", f"out head {(b, h)}", 1, "rows")
+        err = np.abs(lse[b:b + 1, h:h + 1].cpu().double().numpy() - rl).max()
+        assert err <= LSE_ATOL_FP8, f"lse head {(b, h)}: {err}"
+    del qkv, out, lse
+    torch.cuda.empty_cache()
