@@ -179,7 +179,15 @@ def kernel_flops(w, dtype):
                 "dq": u}            # dQ = dS K from the stored dS
     return {"fwd": 2 * u,
             "dkdv": 4 * u,          # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
-            "dq": 3 * u}            # S, dP, dQ = dS K (plus the D = dO.O row sums)
+            "dq": 3 * u,            # S, dP, dQ = dS K (plus the D = dO.O row sums)
+            "bwd_short": 5 * u}     # one kernel: S, dP, dV, dK, dQ (dS kept in LDS)
+
+
+def short_backward(w, dtype):
+    """Whether the library's fused 16-bit backward runs its one-workgroup-
+    per-head kernel for this shape (the rule of bwd_short_applies in
+    csrc/common.hpp); the step then times attn_backward_* as one stage."""
+    return dtype in ("bf16", "f16") and w.hs <= 64 and w.T <= 256 and (w.T > 128 or w.hs == 16)
 
 
 def source_sha(dtype):
@@ -242,6 +250,10 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0, warmup_ms=150.0):
                   ("dkdv", lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D,
                                                             B, T, C, NH, c)),
                   ("dq", lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c))]
+    elif short_backward(w, dtype):
+        bwd = getattr(la, "attn_backward" + sfx)
+        stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
+                  ("bwd_short", lambda: bwd(dqkv, dout, qkv, out, lse, B, T, C, NH, c))]
     else:
         stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
                   ("dq", lambda: dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c)),

@@ -46,7 +46,8 @@
  * Results are deterministic: no atomics, fixed reduction order.
  *
  * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need
- * B*NH*T floats of scratch for D, attn_decode* room for their partial
+ * B*NH*T floats of scratch for D (the 16-bit ones not for the shapes they
+ * run as one kernel, see attn_backward_bf16), attn_decode* room for their partial
  * results (4*B*NH*(hs+1)*ceil(T/128) bytes at most), layernorm_backward*
  * room for column partial sums.  libattn keeps one grow-only buffer per
  * device, allocated with hipMalloc on first need.  A call that needs more
@@ -184,6 +185,12 @@ int attn_backward_dq_ds(float* dqkv, const float* dS, const float* qkv,
  * Accelerating Transformer Training and Inference", section 1: low-precision
  * operands, higher-precision accumulation).  lse stays fp32.  Probabilities
  * and dS are rounded to bf16 only as matrix-core operands.
+ * attn_backward_bf16 (and attn_backward_f16) runs the dQ stage, which writes
+ * D to the workspace, then the dK/dV stage; for short sequences (T <= 256
+ * with hs = 16, 128 < T <= 256 with hs = 32 or 64) it runs instead one
+ * kernel with one workgroup per head that keeps the head's dS on chip, forms
+ * D itself and uses no workspace.  Both give the same quantities to within
+ * the rounding of dS and of the fp32 sums; each is deterministic.
  */
 int attn_forward_bf16(uint16_t* out, float* lse, const uint16_t* qkv,
                       int B, int T, int C, int NH, int causal);

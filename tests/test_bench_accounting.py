@@ -19,8 +19,22 @@ def test_kernel_flops_add_up_to_the_step(key, dtype):
     kf = bench.kernel_flops(w, dtype)
     unit = w.hs * w.pairs * w.B * w.NH
     assert w.flops_fwd + w.flops_bwd == 14 * unit
-    assert sum(kf.values()) == (14 if dtype == "f32_ds" else 18) * unit
+    staged = {k: v for k, v in kf.items() if k != "bwd_short"}
+    assert sum(staged.values()) == (14 if dtype == "f32_ds" else 18) * unit
     assert kf["fwd"] == w.flops_fwd
+    if dtype == "bf16":   # the one-kernel short-sequence backward: five contractions
+        assert kf["bwd_short"] == w.flops_bwd == 10 * unit
+
+
+def test_short_backward_rule():
+    """The step times the fused 16-bit backward as one stage exactly for the
+    shapes where the library runs its one-workgroup-per-head kernel."""
+    assert bench.short_backward(WORKLOADS[4], "bf16")          # ViT-B/16, T = 196, hs = 64
+    assert not bench.short_backward(WORKLOADS[3], "bf16")      # GPT-2 layer, T = 1024
+    assert not bench.short_backward(WORKLOADS[5], "bf16")      # long context, hs = 128
+    assert not bench.short_backward(WORKLOADS[4], "f32")       # 16-bit kernels only
+    assert bench.short_backward(WORKLOADS[2], "bf16")          # T = 256, hs = 64
+    assert bench.short_backward(WORKLOADS[1], "bf16")          # T = 64, hs = 16
 
 
 def test_compulsory_bytes_by_hand():

@@ -31,19 +31,23 @@ def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
                 lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH),
                 lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D, B, T, C, NH, c),
                 lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c)]
+    if dtype == "bf16_fused":   # T <= 256: the one-workgroup-per-head backward
+        return [lambda: la.attn_forward_bf16(out, lse, qkv, B, T, C, NH, c),
+                lambda: la.attn_backward_bf16(dqkv, dout, qkv, out, lse, B, T, C, NH, c)]
     return [lambda: la.attn_forward_bf16(out, lse, qkv, B, T, C, NH, c),
             lambda: la.attn_backward_dq_bf16(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c),
             lambda: la.attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16", "bf16_fused"])
 def test_graph_replays_equal_eager(la, dtype):
     B, T, C, NH, c = 2, 150, 256, 4, 1
     print(f"\n[case] graph replay {dtype} B{B} T{T} C{C} NH{NH}", flush=True)
     sys.stdout.flush()
-    qkv_c, dout_c = make_inputs(B, T, C, "bf16" if dtype == "bf16" else "f32", seed=71)
+    half = dtype.startswith("bf16")
+    qkv_c, dout_c = make_inputs(B, T, C, "bf16" if half else "f32", seed=71)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = torch.bfloat16 if half else torch.float32
     out = torch.empty((B, T, C), dtype=tdt, device="cuda")
     lse = torch.empty((B, NH, T), device="cuda")
     D = torch.empty((B, NH, T), device="cuda")
@@ -80,8 +84,8 @@ def test_captured_fused_backward_survives_workspace_growth(la, dtype):
     """A captured fused backward keeps the workspace address it saw; a later
     eager call at a larger shape grows the workspace, which must retire the
     old buffer without freeing it, so the graph's replays still give the
-    eager bits."""
-    B, T, C, NH, c = 2, 150, 256, 4, 1
+    eager bits.  (T = 300: shorter 16-bit sequences need no workspace.)"""
+    B, T, C, NH, c = 2, 300, 256, 4, 1
     print(f"\n[case] workspace growth under a captured {dtype} attn_backward", flush=True)
     torch.cuda.synchronize()
     la.attn_release()           # start from no workspace: the first call sizes it

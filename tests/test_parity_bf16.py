@@ -117,11 +117,12 @@ def test_single_token_exact(la):
 
 
 def test_stages_equal_fused_backward(la):
-    """dq (which writes D) then dkdv equals attn_backward_bf16; the standalone
-    pre-pass gives the same D, and dkdv run from it (before dq) gives the
-    same dk and dv.  (The fp32 stages: test_parity_f32.py.)"""
+    """dq (which writes D) then dkdv equals attn_backward_bf16 (T = 300: the
+    fused call runs these two kernels); the standalone pre-pass gives the
+    same D, and dkdv run from it (before dq) gives the same dk and dv.  (The
+    fp32 stages: test_parity_f32.py.)"""
     for dtype in ("bf16",):
-        B, T, C, NH = 2, 190, 256, 4
+        B, T, C, NH = 2, 300, 256, 4
         qkv_c, dout_c = make_inputs(B, T, C, dtype, seed=33)
         qkv, dout = qkv_c.cuda(), dout_c.cuda()
         out, lse = la.forward(qkv, NH, True)
@@ -142,3 +143,42 @@ def test_stages_equal_fused_backward(la):
         tol = 1e-2 if dtype == "bf16" else 1e-5   # bf16: one rounding step
         torch.testing.assert_close(g2[:, :, C:].float(), ref[:, :, C:].float(),
                                    rtol=tol, atol=tol)
+
+
+SHORT_SHAPES = [
+    (2, 196, 768, 12),   # hs 64, ViT length: one workgroup per head
+    (3, 200, 256, 16),   # hs 16
+    (2, 129, 512, 16),   # hs 32, one row past 128
+    (1, 256, 256, 4),    # hs 64, the longest such sequence
+    (2, 100, 256, 4),    # hs 64 at T <= 128: the two kernels
+    (2, 64, 128, 8),     # hs 16, exactly one query tile
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", SHORT_SHAPES)
+def test_short_sequence_backward_paths(la, oracle_mod, shape, causal, dtype):
+    """For T <= 256 the fused backward runs one workgroup per head, with the
+    head's dS kept in LDS; the stage calls keep the dQ and dK/dV kernels.
+    Both are checked against the oracle on the same inputs."""
+    B, T, C, NH = shape
+    _case(f"{dtype} short-sequence backward B{B} T{T} C{C} NH{NH} causal={causal}")
+    qkv_c, dout_c = make_inputs(B, T, C, dtype, seed=1200 + T)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    sfx = "_" + dtype
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    c = int(causal)
+    out = torch.empty((B, T, C), dtype=tdt, device="cuda")
+    lse = torch.empty((B, NH, T), device="cuda")
+    getattr(la, "attn_forward" + sfx)(out, lse, qkv, B, T, C, NH, c)
+    fused = torch.full_like(qkv, float("nan"))
+    getattr(la, "attn_backward" + sfx)(fused, dout, qkv, out, lse, B, T, C, NH, c)
+    D = torch.full((B, NH, T), float("nan"), device="cuda")
+    staged = torch.full_like(qkv, float("nan"))
+    getattr(la, "attn_backward_dq" + sfx)(staged, D, dout, qkv, out, lse, B, T, C, NH, c)
+    getattr(la, "attn_backward_dkdv" + sfx)(staged, dout, qkv, lse, D, B, T, C, NH, c)
+    torch.cuda.synchronize()
+    rd = oracle_mod.backward(qkv_c, dout_c, NH, causal)
+    assert_close(fused.cpu(), rd, dtype, "dqkv (fused)")
+    assert_close(staged.cpu(), rd, dtype, "dqkv (stages)")

@@ -103,7 +103,7 @@ def test_single_token_exact(la):
 def test_stages_equal_fused_backward(la):
     """dq (which writes D) then dkdv equals attn_backward_f16; the standalone
     pre-pass gives the same D."""
-    B, T, C, NH = 2, 190, 256, 4
+    B, T, C, NH = 2, 300, 256, 4
     qkv_c, dout_c = make_inputs(B, T, C, "f16", seed=43)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
     out, lse = la.forward(qkv, NH, True)

@@ -381,10 +381,13 @@ int attn_backward_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv
                         {lse, nbytes(BT * NH, 4), "lse"}};
     int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
     if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    if (attn::bwd_short_applies(s))   // one fused kernel, no workspace
+        return launched(attn::launch_bwd_short_bf16(dqkv, dout, qkv, out, lse, s, g_stream),
+                        "attn_backward_bf16 launch");
     float* D = nullptr;
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
-    const attn::Shape s = shape_of(B, T, C, NH, causal);
     hipError_t e = attn::launch_dq_bf16(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_bf16(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward_bf16 launch");
@@ -633,10 +636,13 @@ int attn_backward_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                         {lse, nbytes(BT * NH, 4), "lse"}};
     int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
     if (rc) return rc;
+    const attn::Shape s = shape_of(B, T, C, NH, causal);
+    if (attn::bwd_short_applies(s))   // one fused kernel, no workspace
+        return launched(attn::launch_bwd_short_f16(dqkv, dout, qkv, out, lse, s, g_stream),
+                        "attn_backward_f16 launch");
     float* D = nullptr;
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
-    const attn::Shape s = shape_of(B, T, C, NH, causal);
     hipError_t e = attn::launch_dq_f16(dqkv, D, dout, qkv, out, lse, s, g_stream);
     if (e == hipSuccess) e = attn::launch_dkdv_f16(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward_f16 launch");

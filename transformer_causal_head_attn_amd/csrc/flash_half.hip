@@ -809,6 +809,267 @@ __device__ __forceinline__ void bwd_dq_half_tile(
     }
 }
 
+// ------------------------------------------- backward, short sequences
+// One workgroup per head for T <= 256 (hs <= 64), so a head's dQ sums over
+// keys stay inside one workgroup.  Eight waves each own 32 key rows (K and V
+// in registers, dK and dV accumulated), as in the dK/dV kernel, and the
+// head's queries stream through LDS 64 at a time.  Per query tile each wave
+// also leaves its block of dS^T in LDS; after a barrier the workgroup forms
+// the tile's dQ = scale * dS K from it over all the head's keys, with K^T
+// (kept in LDS from the start) as the other operand.  So S and dP are formed
+// once per score (five products instead of the two kernels' seven), the dS
+// never reaches memory, D = dO . O comes from the streamed tiles, and q, k,
+// v, out, dout and lse are each read once.
+constexpr int kShortT = 256;     // keys per workgroup: 8 waves of 32
+constexpr int kShortWaves = 8;
+
+// Column operand with the k order of a row read: lane (j, g) receives
+// tile[base + 8g + e][col0 + j], e = 0..7 (the two transpose reads address
+// rows base + 8g + i/4 and base + 8g + 4 + i/4; see col_operand for the
+// lane mapping of ds_read_b64_tr_b16).
+template <typename E>
+__device__ __forceinline__ V8<E> col_operand_seq(const uint16_t* tile, int ld, int base, int col0,
+                                                 int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    const uint16_t* p = tile + (base + 8 * g + (j >> 2)) * ld + col0 + 4 * (j & 3);
+    const s16x4 a = tr_read(p);
+    const s16x4 b = tr_read(p + 4 * ld);
+    V8<E> r;
+    __builtin_memcpy(&r, &a, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+    return r;
+}
+
+template <typename E, int HS>
+__device__ __forceinline__ void bwd_short_half_head(
+    int bh, uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
+    float scale_log2) {
+    using G = Geom<HS>;
+    constexpr int NW = kShortWaves, NT = 64 * NW;
+    constexpr int KB = 2, R = 16 * KB;
+    static_assert(NW * R == kShortT, "one key row per workgroup slot");
+    // K^T row stride: 672 bytes, the same bank offset from row to row (160
+    // mod 256) as the hs + 16 stride of the row-major tiles (a 528-byte
+    // stride measured 2% slower); dS^T rows: 144 bytes
+    constexpr int KTR = kShortT + 80;
+    constexpr int DSR = kStream + 8;
+    constexpr int PB = G::MB >= 2 ? G::MB / 2 : 1;   // dQ output blocks per wave
+    constexpr int CH = HS / 8;                       // 16-byte chunks per row
+    static_assert(TileRegs<HS, NT>::N == 1, "one chunk per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[kStream * G::LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t dOs[kStream * G::LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t KT[HS * KTR];
+    __shared__ __attribute__((aligned(16))) uint16_t dST[kShortT * DSR];
+    __shared__ float Ls[kStream];
+    __shared__ __attribute__((aligned(16))) float Dl[kStream];   // -D per query row
+
+    const Lane L;
+    const int b = bh / NH, h = bh - (bh / NH) * NH;
+    const size_t C3 = 3 * (size_t)C;
+    const uint16_t* qbase = qkv + (size_t)b * T * C3 + (size_t)h * HS;
+    const uint16_t* kbase = qbase + C;
+    const uint16_t* vbase = qbase + 2 * (size_t)C;
+    const uint16_t* dobase = dout + (size_t)b * T * C + (size_t)h * HS;
+    const uint16_t* obase = out + (size_t)b * T * C + (size_t)h * HS;
+    const float* lrow = lse + (size_t)bh * T;
+
+    const int c0 = L.w * R;   // this wave's first key row
+    V8<E> kreg[KB][G::KSTEPS], vreg[KB][G::KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int kv = c0 + 16 * kb + L.r16;
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+            kreg[kb][s] = row_chunk_global<E, HS>(kbase + (size_t)kv * C3, kv < T, s, L.g);
+            vreg[kb][s] = row_chunk_global<E, HS>(vbase + (size_t)kv * C3, kv < T, s, L.g);
+        }
+    }
+    f32x4 dk[KB][G::MB], dv[KB][G::MB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb) {
+            dk[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dv[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int nqt = (T + kStream - 1) / kStream;
+    TileRegs<HS, NT> rq, rd, ro;
+    float rl = 0.f;
+    auto fetch = [&](int qt) {
+        rq.fetch(qbase, C3, qt * kStream, T, L.tid);
+        rd.fetch(dobase, (size_t)C, qt * kStream, T, L.tid);
+        ro.fetch(obase, (size_t)C, qt * kStream, T, L.tid);
+        if (L.tid < kStream) rl = lrow[min(qt * kStream + L.tid, T - 1)];
+    };
+    fetch(0);
+    // K^T: lane (key c0 + 16kb + r16, g) holds dims 32s + 8g .. +7 (zeros
+    // for keys >= T)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+            const int d0 = 32 * s + 8 * L.g;
+            if (d0 < HS) {
+                uint16_t u[8];
+                __builtin_memcpy(u, &kreg[kb][s], 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) KT[(d0 + e) * KTR + c0 + 16 * kb + L.r16] = u[e];
+            }
+        }
+    wait_global_loads();
+
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int q0 = qt * kStream;
+        __syncthreads();   // the previous tile's reads of Qs, dOs and dST are done
+        rq.store(Qs, L.tid);
+        rd.store(dOs, L.tid);
+        {   // D = dO . O per query row: the thread's chunk, then the CH threads of the row
+            float acc = 0.f;
+            if (L.tid < kStream * CH) {
+                const uint32_t av[4] = {rd.v[0].x, rd.v[0].y, rd.v[0].z, rd.v[0].w};
+                const uint32_t ov[4] = {ro.v[0].x, ro.v[0].y, ro.v[0].z, ro.v[0].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc = fmaf(E::bits_to_f32(av[q]), E::bits_to_f32(ov[q]), acc);
+                    acc = fmaf(E::bits_to_f32(av[q] >> 16), E::bits_to_f32(ov[q] >> 16), acc);
+                }
+            }
+#pragma unroll
+            for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+            const int row = L.tid / CH;
+            if (L.tid < kStream * CH && L.tid % CH == 0) Dl[row] = q0 + row < T ? -acc : 0.f;
+        }
+        if (L.tid < kStream) Ls[L.tid] = q0 + L.tid < T ? rl * kLog2e : INFINITY;   // +inf -> P = 0
+        __syncthreads();
+        if (qt + 1 < nqt) fetch(qt + 1);
+
+        // This wave's keys against the tile's queries (skipped when every
+        // query precedes every key, or no key row of the wave is below T):
+        // dV^T += dO^T P, dK^T += Q^T dS, and dS^T into LDS.
+        if (c0 < T && !(causal && q0 + kStream - 1 < c0)) {
+            const bool mask = (causal && q0 < c0 + R - 1) || c0 + R > T;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (t == 1 && q0 + 32 >= T) break;   // the tile's last 32 queries all lie past T
+                f32x4 p[KB][2], ds[KB][2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int n = 2 * t + u;
+                    // s[kb][i], dp[kb][i] for q = q0 + 16n + 4g + i, kv = c0 + 16kb + r16
+                    const f32x4 dneg = *reinterpret_cast<const f32x4*>(Dl + 16 * n + 4 * L.g);
+                    f32x4 s[KB], dp[KB];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        dp[kb] = dneg;
+                    }
+#pragma unroll
+                    for (int st = 0; st < G::KSTEPS; ++st) {
+                        const V8<E> qc = row_chunk_lds<E, HS>(Qs, 16 * n + L.r16, st, L.g);
+                        const V8<E> dc = row_chunk_lds<E, HS>(dOs, 16 * n + L.r16, st, L.g);
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) {
+                            s[kb] = E::mfma(qc, kreg[kb][st], s[kb]);
+                            dp[kb] = E::mfma(dc, vreg[kb][st], dp[kb]);
+                        }
+                    }
+                    if (mask) {   // key kv stays iff kv < T and (causal) kv <= q
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const int kv = c0 + 16 * kb + L.r16;
+                            const int d = causal ? kv - (q0 + 16 * n + 4 * L.g) : -4;
+                            const bool in = kv < T;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[kb][i] = (in && i >= d) ? s[kb][i] : -INFINITY;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float l2 = Ls[16 * n + 4 * L.g + i];
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const float pv = fast_exp2(fmaf(s[kb][i], scale_log2, -l2));
+                            p[kb][u][i] = pv;
+                            ds[kb][u][i] = pv * dp[kb][i];
+                        }
+                    }
+                }
+                V8<E> pb[KB], sb[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    pb[kb] = pack_pair<E>(p[kb][0], p[kb][1]);
+                    sb[kb] = pack_pair<E>(ds[kb][0], ds[kb][1]);
+                    // dS^T rows: the packed halves are queries 32t + 4g .. +3 and 32t + 16 + 4g .. +3
+                    uint4 raw;
+                    __builtin_memcpy(&raw, &sb[kb], 16);
+                    uint16_t* drow = dST + (c0 + 16 * kb + L.r16) * DSR + 32 * t + 4 * L.g;
+                    *reinterpret_cast<uint2*>(drow) = make_uint2(raw.x, raw.y);
+                    *reinterpret_cast<uint2*>(drow + 16) = make_uint2(raw.z, raw.w);
+                }
+#pragma unroll
+                for (int mb = 0; mb < G::MB; ++mb) {
+                    const V8<E> dop = col_operand<E, HS>(dOs, 32 * t, 16 * mb, L.l);
+                    const V8<E> qop = col_operand<E, HS>(Qs, 32 * t, 16 * mb, L.l);
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        dv[kb][mb] = E::mfma(dop, pb[kb], dv[kb][mb]);
+                        dk[kb][mb] = E::mfma(qop, sb[kb], dk[kb][mb]);
+                    }
+                }
+            }
+        }
+        __syncthreads();   // the tile's dS^T is complete
+
+        // dQ^T = K^T dS^T for the tile: wave w takes query block w/2 and PB
+        // of the MB column blocks (hs = 16: waves 0..3, one block each);
+        // keys up to the tile's last query (causal) or T, 32 at a time.
+        {
+            const int qb = G::MB >= 2 ? (L.w >> 1) : L.w;
+            const int mb0 = G::MB >= 2 ? (L.w & 1) * PB : 0;
+            if (qb < 4 && q0 + 16 * qb < T) {
+                const int klim = causal ? min(T, q0 + kStream) : T;
+                const int nks = (klim + 31) / 32;
+                f32x4 acc[PB];
+#pragma unroll
+                for (int pp = 0; pp < PB; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < nks; ++ks) {
+                    const V8<E> sop = col_operand_seq<E>(dST, DSR, 32 * ks, 16 * qb, L.l);
+#pragma unroll
+                    for (int pp = 0; pp < PB; ++pp) {
+                        const V8<E> kop = as_v8<E>(*reinterpret_cast<const uint4*>(
+                            KT + (16 * (mb0 + pp) + L.r16) * KTR + 32 * ks + 8 * L.g));
+                        acc[pp] = E::mfma(kop, sop, acc[pp]);
+                    }
+                }
+                const int q = q0 + 16 * qb + L.r16;
+                if (q < T) {
+                    uint16_t* dqrow = dqkv + ((size_t)b * T + q) * C3 + (size_t)h * HS;
+#pragma unroll
+                    for (int pp = 0; pp < PB; ++pp)
+                        store4<E>(dqrow + 16 * (mb0 + pp) + 4 * L.g, acc[pp] * scale);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int kv = c0 + 16 * kb + L.r16;
+        if (kv < T) {
+            uint16_t* dkrow = dqkv + ((size_t)b * T + kv) * C3 + C + (size_t)h * HS;
+            uint16_t* dvrow = dkrow + C;
+#pragma unroll
+            for (int mb = 0; mb < G::MB; ++mb) {
+                store4<E>(dkrow + 16 * mb + 4 * L.g, dk[kb][mb] * scale);
+                store4<E>(dvrow + 16 * mb + 4 * L.g, dv[kb][mb]);
+            }
+        }
+    }
+}
+
 // 16-row blocks per wave in the forward and dQ kernels (measured on the
 // GPT-2, ViT and long-context shapes: 2 beats 1 and 4)
 // ------------------------------------------------------------- kernels
@@ -882,6 +1143,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(HS >= 1
     deal_tile(gridDim.x / nt, nt, causal != 0, deal, bh, t);
     bwd_dq_half_tile<E, HS, QB, false, NW>(t, bh, dqkv, Dws, dout, qkv, out, lse, T, C, NH, causal,
                                            scale, scale_log2, KeyPart{0, 0, nullptr, nullptr});
+}
+
+// Short-sequence backward: workgroup bh takes head bh.
+template <typename E, int HS>
+__global__ __launch_bounds__(64 * kShortWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_short_half_kernel(
+    uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int T, int C, int NH, int causal, float scale,
+    float scale_log2) {
+    bwd_short_half_head<E, HS>(blockIdx.x, dqkv, dout, qkv, out, lse, T, C, NH, causal, scale,
+                               scale_log2);
 }
 
 // Split backward.  dQ: workgroup (rank, bh) of nqt * nchunk * BH takes Q
@@ -981,7 +1253,9 @@ constexpr int kb_for(int hs) { return hs >= 128 ? 1 : 2; }
 // per head instead of once per 128-row tile (ViT-B/16, T = 196: 45.5 ->
 // 39.2 us).  The dQ and dK/dV kernels keep 4 waves: at 8 their register
 // needs leave one workgroup per CU (dQ 63 -> 72 us, dK/dV 74 -> 84 us; dQ
-// held to 4 waves per SIMD spills, 83 us).
+// held to 4 waves per SIMD spills, 83 us).  The fused backward of such
+// shapes runs bwd_short_half_kernel instead (ViT-B/16: dQ + dK/dV 136 us,
+// fused 123 us).
 template <int HS>
 bool short_seq(const Shape& s) { return HS <= 64 && s.T <= 256 && s.T > 128; }
 
@@ -1112,6 +1386,22 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
     return dq_half_nw<E, HS, 4>(dqkv, D, dout, qkv, out, lse, s, st);
 }
 
+template <typename E, int HS>
+hipError_t bwd_short_half_hs(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
+                             const uint16_t* out, const float* lse, const Shape& s,
+                             hipStream_t st) {
+    if constexpr (HS > 64) {
+        return hipErrorInvalidValue;
+    } else {
+        if (!bwd_short_applies(s)) return hipErrorInvalidValue;
+        const float scale = (float)(1.0 / sqrt((double)HS));
+        hipLaunchKernelGGL((bwd_short_half_kernel<E, HS>), dim3((unsigned)(s.B * s.NH)),
+                           dim3(64 * kShortWaves), 0, st, dqkv, dout, qkv, out, lse, s.T, s.C, s.NH,
+                           s.causal, scale, scale * kLog2e);
+        return hipGetLastError();
+    }
+}
+
 }  // namespace
 
 #define ATTN_DISPATCH_HS(fn, E, ...)                      \
@@ -1150,6 +1440,11 @@ hipError_t dq_half_hs(uint16_t* dqkv, float* D, const uint16_t* dout, const uint
                                const uint16_t* qkv, const uint16_t* out, const float* lse,        \
                                const Shape& s, hipStream_t st) {                                  \
         ATTN_DISPATCH_HS(dq_half_hs, E, dqkv, D, dout, qkv, out, lse, s, st)                       \
+    }                                                                                              \
+    hipError_t launch_bwd_short_##SFX(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,  \
+                                      const uint16_t* out, const float* lse, const Shape& s,      \
+                                      hipStream_t st) {                                            \
+        ATTN_DISPATCH_HS(bwd_short_half_hs, E, dqkv, dout, qkv, out, lse, s, st)                   \
     }
 
 ATTN_HALF_LAUNCHERS(bf16, BF16)
