@@ -16,18 +16,18 @@
 // Accelerating Transformer Training and Inference" (section 1): the
 // elementwise passes never read or write the (M, N) matrix again.
 //
-// gfx950 mapping.  A workgroup of 4 waves computes a 128 x 128 tile of y
-// (rows m, columns n); each wave a 64 x 64 quarter as 4 x 4 blocks of 16 x
-// 16 accumulators.  The products are arranged as y^T = w x^T: w rows (k
+// gfx950 mapping.  The products are arranged as y^T = w x^T: w rows (k
 // contiguous) are the first matrix-core operand and x rows (k contiguous)
-// the second, both read from row-major LDS tiles with 16-byte loads, and a
-// lane ends with 4 consecutive n of one row m, so bias, residual and the
-// output move 4 columns per lane.  Tiles of w and x stream through LDS in
-// steps of BK = 64 (bf16, v_mfma_f32_16x16x32_bf16) or 32 (fp32,
-// v_mfma_f32_16x16x4_f32) k-values; the next step's tiles are loaded into
-// registers while the current one is used.  Rows past M or N come back as
-// zeros from buffer loads bounded by the tile's rows; k-chunks past K are
-// predicated (K is a multiple of the 16-byte chunk).
+// the second, both read from LDS tiles with 16-byte loads, and a lane ends
+// with 4 consecutive n of one row m, so bias, residual and the output move
+// 4 columns per lane.  fp32 (v_mfma_f32_16x16x4_f32): a workgroup of 4
+// waves computes a 128 x 128 tile of y, each wave a 64 x 64 quarter as 4 x 4
+// blocks of 16 x 16 accumulators; tiles of w and x stream through LDS in
+// steps of 32 k-values, the next step's loaded into registers while the
+// current one is used.  bf16 (v_mfma_f32_16x16x32_bf16): 128 x 64 tiles
+// with two LDS stages filled by direct loads (below).  Rows past M or N come
+// back as zeros from buffer loads bounded by the tile's rows; k-chunks past
+// K are predicated or read as zeros (K is a multiple of the 16-byte chunk).
 #include "common.hpp"
 
 namespace attn {
@@ -93,71 +93,140 @@ struct GLane {
 typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 
 // bf16 operands, fp32 accumulation, bf16 output (round to nearest even);
-// bias fp32, residual bf16.
+// bias fp32, residual bf16.  A workgroup computes a 128 (m) x 64 (n) tile
+// of y; wave w takes rows 64 (w >> 1) .. +63 and columns 32 (w & 1) .. +31.
+// k steps by 64 through two LDS stages that are filled straight from global
+// memory (buffer_load_dwordx4 ... lds: one wave instruction moves 64 lanes x
+// 16 bytes into 1 KB of consecutive LDS, lane l into bytes 16l .. 16l + 15),
+// so the next step's tiles load while the current one is used, with no
+// staging registers and one barrier per step.
+constexpr int kBM = 128, kBN = 64, kBK = 64;
+constexpr int kBWaves = kBM / 32;              // waves: kBM / 64 along m, 2 along n
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kWNB = kBN / 32;   // 16-column blocks per wave
+
+// LDS rows are 128 bytes (64 bf16 of k); chunk c of row r sits at chunk
+// position c ^ swz(r).  The LDS has 64 four-byte banks (256 bytes), so two
+// rows share a bank period: sixteen lanes reading chunk c of rows r .. r + 15
+// (one ds_read_b128 pass) land on sixteen distinct 16-byte bank groups when
+// the even rows, and the odd rows, take eight distinct positions each.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Tile of workgroup blockIdx.x.  Workgroups go to the 8 XCDs round robin by
+// id; when the row-block count is a multiple of 8, XCD x takes row blocks x,
+// x + 8, x + 16, ... with every column block, so each row block of x is
+// fetched into one XCD's L2 only (otherwise consecutive tiles of one row
+// block land on 8 different XCDs and each pulls it from memory).
+__device__ __forceinline__ void xcd_tile(int ntn, int ntm, int& tn, int& tm) {
+    const int id = blockIdx.x;
+    if (ntm % 8 == 0) {
+        const int loc = id >> 3;
+        tm = (id & 7) + 8 * (loc / ntn);
+        tn = loc - (loc / ntn) * ntn;
+    } else {
+        tn = id % ntn;
+        tm = id / ntn;
+    }
+}
+
+// k bytes kb0 .. kb0 + 127 of rows 0 .. ROWS - 1 of the descriptor's rows
+// (rows past its record limit read as zeros) into a ROWS x 128-byte tile;
+// chunks at or past kbytes get an offset past every record limit, so they
+// are zeros too.  The 4 waves share the ROWS / 8 wave loads.
+template <int ROWS>
+__device__ __forceinline__ void dma_stage(char* tile, __amdgpu_buffer_rsrc_t r, uint32_t ld, int kb0,
+                                          int kbytes, int w, int l) {
+    constexpr int NI = ROWS / 8;
+    static_assert(NI % kBWaves == 0, "whole wave loads per wave");
+#pragma unroll
+    for (int k = 0; k < NI / kBWaves; ++k) {
+        const int q = w + kBWaves * k;
+        const int row = 8 * q + (l >> 3);
+        const int kb = kb0 + 16 * ((l & 7) ^ swz(row));
+        const uint32_t off = kb < kbytes ? (uint32_t)row * ld + (uint32_t)kb : 0x7FFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(tile + 1024 * q), 16, (int)off, 0, 0, 0);
+    }
+}
+
 template <bool RES>
-__global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kBThreads) void gemm_bf16_kernel(uint16_t* __restrict__ y,
                                                               const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ w,
                                                               const float* __restrict__ bias,
                                                               const uint16_t* __restrict__ res,
                                                               int M, int N, int K) {
-    constexpr int BK = 64;               // k per step (128 bytes of a row)
-    constexpr int LDB = (BK + 8) * 2;    // LDS row stride in bytes (16 bytes of padding)
-    __shared__ __attribute__((aligned(16))) char Ws[kGN * LDB];
-    __shared__ __attribute__((aligned(16))) char Xs[kGM * LDB];
+    // two stages in separate arrays, each indexed only by constants: with one
+    // array indexed by the step's parity the compiler would wait for the
+    // loads in flight before every LDS read
+    // a stage: the x tile, then the w tile
+    __shared__ __attribute__((aligned(16))) char S0[(kBM + kBN) * 128];
+    __shared__ __attribute__((aligned(16))) char S1[(kBM + kBN) * 128];
     const GLane L;
-    const int ntn = (N + kGN - 1) / kGN;
-    const int tn = blockIdx.x % ntn, tm = blockIdx.x / ntn;
-    const int n0 = tn * kGN, m0 = tm * kGM;
-    const size_t ldb = (size_t)K * 2;
-    const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w, ldb, n0, kGN, N);
-    const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, ldb, m0, kGM, M);
+    const int ntn = (N + kBN - 1) / kBN;
+    int tn, tm;
+    xcd_tile(ntn, (M + kBM - 1) / kBM, tn, tm);
+    const int n0 = tn * kBN, m0 = tm * kBM;
+    const uint32_t ldb = (uint32_t)K * 2;
+    const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w, ldb, n0, kBN, N);
+    const __amdgpu_buffer_rsrc_t rx = rows_rsrc(x, ldb, m0, kBM, M);
+    const int kbytes = K * 2;
+    const int nsteps = (K + kBK - 1) / kBK;
 
-    f32x4 acc[4][4];
+    f32x4 acc[kWNB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWNB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Stage sw, sx;
-    const int kbytes = K * 2;
-    sw.fetch(rw, ldb, 0, kbytes, L.tid);
-    sx.fetch(rx, ldb, 0, kbytes, L.tid);
-    wait_global_loads();
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();
-        sw.store<LDB>(Ws, L.tid);
-        sx.store<LDB>(Xs, L.tid);
-        __syncthreads();
-        if (k0 + BK < K) {
-            sw.fetch(rw, ldb, (k0 + BK) * 2, kbytes, L.tid);
-            sx.fetch(rx, ldb, (k0 + BK) * 2, kbytes, L.tid);
-        }
+    auto load = [&](int s, char* Sn) {
+        dma_stage<kBM>(Sn, rx, ldb, s * 2 * kBK, kbytes, L.w, L.l);
+        dma_stage<kBN>(Sn + kBM * 128, rw, ldb, s * 2 * kBK, kbytes, L.w, L.l);
+    };
+    auto compute = [&](const char* Sc) {
+        const char* Xc = Sc;
+        const char* Wc = Sc + kBM * 128;
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            gbf16x8 a[4], b[4];
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            const int c = 4 * ks + L.g;
+            gbf16x8 a[kWNB], b[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 va = *reinterpret_cast<const uint4*>(
-                    Ws + (64 * L.wn + 16 * i + L.r16) * LDB + (32 * ks + 8 * L.g) * 2);
-                const uint4 vb = *reinterpret_cast<const uint4*>(
-                    Xs + (64 * L.wm + 16 * i + L.r16) * LDB + (32 * ks + 8 * L.g) * 2);
-                __builtin_memcpy(&a[i], &va, 16);
-                __builtin_memcpy(&b[i], &vb, 16);
+            for (int i = 0; i < kWNB; ++i) {
+                const int row = (kBN / 2) * L.wn + 16 * i + L.r16;
+                const uint4 v = *reinterpret_cast<const uint4*>(Wc + row * 128 + 16 * (c ^ swz(row)));
+                __builtin_memcpy(&a[i], &v, 16);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) {
+                const int row = 64 * L.wm + 16 * j + L.r16;
+                const uint4 v = *reinterpret_cast<const uint4*>(Xc + row * 128 + 16 * (c ^ swz(row)));
+                __builtin_memcpy(&b[j], &v, 16);
+            }
+#pragma unroll
+            for (int i = 0; i < kWNB; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+    };
+    auto step = [&](int s, const char* Sc, char* Sn) {
+        wait_global_loads();   // this wave's loads of step s (the only ones in flight)
+        __syncthreads();       // every wave's loads of step s have landed; step s - 1 is read
+        if (s + 1 < nsteps) load(s + 1, Sn);
+        compute(Sc);
+    };
+    load(0, S0);
+    for (int s = 0; s < nsteps; s += 2) {
+        step(s, S0, S1);
+        if (s + 1 < nsteps) step(s + 1, S1, S0);
     }
 
     // acc[i][j] register q: y[m][n], m = m0 + 64 wm + 16 j + r16,
-    // n = n0 + 64 wn + 16 i + 4 g + q
+    // n = n0 + (kBN / 2) wn + 16 i + 4 g + q
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int n = n0 + 64 * L.wn + 16 * i + 4 * L.g;
+    for (int i = 0; i < kWNB; ++i) {
+        const int n = n0 + (kBN / 2) * L.wn + 16 * i + 4 * L.g;
         if (n >= N) continue;   // N % 4 == 0: the four columns are all in or all out
         const float4 bb = *reinterpret_cast<const float4*>(bias + n);
 #pragma unroll
@@ -196,7 +265,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_f32_kernel(float* __restrict__
     __shared__ __attribute__((aligned(16))) float Xs[kGM * LDF];
     const GLane L;
     const int ntn = (N + kGN - 1) / kGN;
-    const int tn = blockIdx.x % ntn, tm = blockIdx.x / ntn;
+    int tn, tm;
+    xcd_tile(ntn, (M + kGM - 1) / kGM, tn, tm);
     const int n0 = tn * kGN, m0 = tm * kGM;
     const size_t ldb = (size_t)K * 4;
     const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w, ldb, n0, kGN, N);
@@ -293,13 +363,13 @@ hipError_t launch_gemm_f32(float* y, const float* x, const float* w, const float
 
 hipError_t launch_gemm_bf16(uint16_t* y, const uint16_t* x, const uint16_t* w, const float* bias,
                             const uint16_t* res, int M, int N, int K, hipStream_t st) {
-    const long long grid = gemm_grid(M, N);
+    const long long grid = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
     if (grid < 1 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (res)
-        hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kGThreads), 0, st, y, x,
+        hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kBThreads), 0, st, y, x,
                            w, bias, res, M, N, K);
     else
-        hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(kGThreads), 0, st, y, x,
+        hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(kBThreads), 0, st, y, x,
                            w, bias, res, M, N, K);
     return hipGetLastError();
 }
