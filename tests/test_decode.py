@@ -164,3 +164,30 @@ def test_decode_calls_in_a_row(la, oracle_mod):
     assert_close(a2[0].cpu(), ro, "f32", "decode out")
     ro, rl = _decode_ref(oracle_mod, qb, 8)
     assert_close(b2[0].cpu(), ro, "f32", "decode out")
+
+
+def test_decode_graph_replays(la):
+    """A captured decode (range kernel and merge kernel) replayed three
+    times, with eager decodes of another shape in between, gives the eager
+    bits each time."""
+    _case("decode under graph capture")
+    qa, _ = make_inputs(4, 700, 256, "bf16", seed=85)
+    qb, _ = make_inputs(2, 300, 512, "bf16", seed=86)
+    qa_, qb_ = qa.cuda(), qb.cuda()
+    out = torch.empty((4, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((4, 4), device="cuda")
+    la.attn_decode_bf16(out, lse, qa_, 4, 700, 256, 4)   # eager: sizes the workspace
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.attn_decode_bf16(out, lse, qa_, 4, 700, 256, 4)
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {r}"
+        la.decode(qb_, 8)
+        torch.cuda.synchronize()
