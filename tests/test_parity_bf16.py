@@ -152,6 +152,8 @@ SHORT_SHAPES = [
     (1, 256, 256, 4),    # hs 64, the longest such sequence
     (2, 100, 256, 4),    # hs 64 at T <= 128: the two kernels
     (2, 64, 128, 8),     # hs 16, exactly one query tile
+    (2, 256, 128, 8),    # hs 16, every wave's keys below T
+    (1, 256, 512, 16),   # hs 32, four full query tiles
 ]
 
 
