@@ -185,8 +185,9 @@ def kernel_flops(w, dtype):
 
 def short_backward(w, dtype):
     """Whether the library's fused 16-bit backward runs its one-workgroup-
-    per-head kernel for this shape (the rule of bwd_short_applies in
-    csrc/common.hpp); the step then times attn_backward_* as one stage."""
+    per-head kernel for this shape (the rule of tiles::bwd_short_applies in
+    csrc/tiles.hpp, checked against this one by tests/test_tiles.py); the
+    step then times attn_backward_* as one stage."""
     return dtype in ("bf16", "f16") and w.hs <= 64 and w.T <= 256 and (w.T > 128 or w.hs == 16)
 
 

@@ -58,3 +58,43 @@ def test_apply_grid_and_decode_agree(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.startswith("ok ")
+
+
+RULE = r"""
+#include <cstdio>
+#include "tiles.hpp"
+int main() {
+    const int hss[] = {16, 32, 64, 128};
+    for (int hs : hss)
+        for (int T = 1; T <= 300; ++T) std::printf("%d %d %d\n", hs, T, (int)attn::tiles::bwd_short_applies(T, hs));
+    return 0;
+}
+"""
+
+
+def test_short_backward_rule_matches_bench(tmp_path):
+    """bench.py times the fused 16-bit backward as one stage exactly where the
+    library's dispatch (tiles::bwd_short_applies) runs the one-kernel
+    backward: the two agree for every hs and T up to 300."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "rule.cpp"
+    exe = tmp_path / "rule"
+    src.write_text(RULE)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", CSRC, "-o", str(exe),
+                    str(src)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, check=True)
+
+    class W:
+        pass
+    n = 0
+    for line in res.stdout.split("\n"):
+        if not line:
+            continue
+        hs, T, lib = (int(v) for v in line.split())
+        w = W()
+        w.hs, w.T = hs, T
+        assert bench.short_backward(w, "bf16") == bool(lib), (hs, T)
+        n += 1
+    assert n == 4 * 300

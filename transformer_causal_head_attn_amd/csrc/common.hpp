@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include "tiles.hpp"
 
 namespace attn {
 
@@ -235,12 +236,8 @@ hipError_t launch_dkdv_f16(uint16_t* dqkv, const uint16_t* dout, const uint16_t*
 hipError_t launch_dq_f16(uint16_t* dqkv, float* D, const uint16_t* dout, const uint16_t* qkv,
                          const uint16_t* out, const float* lse, const Shape& s, hipStream_t st);
 // Fused 16-bit backward of short sequences (one workgroup per head), used by
-// the fused backward entry points for T <= 256 and hs <= 64: at hs = 64 and
-// 32 only above T = 128 (at or below it the dQ and dK/dV kernels, one
-// workgroup per head each, measured 4-5% faster), at hs = 16 for every T.
-inline bool bwd_short_applies(const Shape& s) {
-    return s.hs <= 64 && s.T <= 256 && (s.T > 128 || s.hs == 16);
-}
+// the fused backward entry points where tiles::bwd_short_applies says so.
+inline bool bwd_short_applies(const Shape& s) { return tiles::bwd_short_applies(s.T, s.hs); }
 hipError_t launch_bwd_short_bf16(uint16_t* dqkv, const uint16_t* dout, const uint16_t* qkv,
                                  const uint16_t* out, const float* lse, const Shape& s,
                                  hipStream_t st);

@@ -1,9 +1,9 @@
-// tiles.hpp -- integer tiling arithmetic of the materialised product kernel
-// (apply_kernel in materialized.hip), shared by the kernel and its launchers
-// so the grid and the workgroup -> (head, row tile) decode cannot drift
-// apart.  Only constexpr integer functions: they compile for the device and
-// the host alike and need no HIP header, so the host tests check them with
-// a plain C++ compiler.
+// tiles.hpp -- integer tiling and dispatch arithmetic shared by kernels and
+// their launchers: the materialised product kernel's grid and workgroup ->
+// (head, row tile) decode (apply_kernel in materialized.hip), and which
+// 16-bit backward the fused entry points run.  Only constexpr integer
+// functions: they compile for the device and the host alike and need no HIP
+// header, so the host tests check them with a plain C++ compiler.
 #pragma once
 
 namespace attn {
@@ -33,6 +33,14 @@ constexpr TileId apply_tile(long long block, int BH, int T, bool heavy_first) {
     const int rank = (int)(block / BH);
     const int bh = (int)(block - (long long)rank * BH);
     return TileId{bh, heavy_first ? nrt - 1 - rank : rank, true};
+}
+
+// The fused 16-bit backward runs one kernel with one workgroup per head
+// (bwd_short_half_kernel) for T <= 256 and hs <= 64: at hs = 64 and 32 only
+// above T = 128 (at or below it the dQ and dK/dV kernels, one workgroup per
+// head each, measured 4-5% faster), at hs = 16 for every T.
+constexpr bool bwd_short_applies(int T, int hs) {
+    return hs <= 64 && T <= 256 && (T > 128 || hs == 16);
 }
 
 }  // namespace tiles
