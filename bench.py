@@ -83,6 +83,9 @@ def parse_args():
     p.add_argument("--fp8-only", action="store_true",
                    help="only time the fp8 forward (and the bf16 forward on the same values) on "
                         "the GPT-2, ViT and long-context inputs and print them as one JSON line")
+    p.add_argument("--projections-only", action="store_true",
+                   help="only time the QKV and output projections over the workload's "
+                        "activation rows (fp32 and bf16) and print them as one JSON line")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes (3 times), "
                         "to calibrate the HBM byte counters of a profiler run")
@@ -658,7 +661,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
-    peaks = device_peaks() if not (args.calibrate_copy or args.layernorm_only or args.fp8_only) else None
+    peaks = (device_peaks() if not (args.calibrate_copy or args.layernorm_only or args.fp8_only
+                                    or args.projections_only) else None)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
@@ -678,6 +682,10 @@ def main():
         return
     if args.fp8_only:
         print(json.dumps({"fp8_forward": run_fp8_forward(la, torch, steps=args.steps)}), flush=True)
+        return
+    if args.projections_only:
+        print(json.dumps({"projections": run_projections(la, torch, w.B * w.T, w.C, steps=args.steps)}),
+              flush=True)
         return
     dtype = args.dtype or w.dtype
     total_ms, graph_ms, wall_ms, per_kernel, stats = run_gpu(la, torch, w, dtype, args.steps,
