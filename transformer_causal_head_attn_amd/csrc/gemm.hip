@@ -65,16 +65,8 @@ struct Stage {
             }
         }
     }
-    // LDS row stride LDB bytes
-    template <int LDB>
-    __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = tid + kGThreads * j;
-            const int row = e >> 3, c = e & 7;
-            *reinterpret_cast<uint4*>(lds + row * LDB + 16 * c) = v[j];
-        }
-    }
+    // dense 128-byte LDS rows, chunk c of row r at chunk position c ^ swz(r)
+    __device__ __forceinline__ void store_swz(char* lds, int tid) const;
 };
 
 struct GLane {
@@ -111,6 +103,15 @@ constexpr int kWNB = kBN / 32;   // 16-column blocks per wave
 // (one ds_read_b128 pass) land on sixteen distinct 16-byte bank groups when
 // the even rows, and the odd rows, take eight distinct positions each.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void Stage::store_swz(char* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kGThreads * j;
+        const int row = e >> 3, c = e & 7;
+        *reinterpret_cast<uint4*>(lds + row * 128 + 16 * (c ^ swz(row))) = v[j];
+    }
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_f32_kernel(float* __restrict__
                                                              const float* __restrict__ res, int M,
                                                              int N, int K) {
     constexpr int BK = 32;               // k per step (128 bytes of a row)
-    constexpr int LDF = BK + 4;          // LDS row stride in floats
+    constexpr int LDF = BK;              // dense 128-byte rows, chunks swizzled
     __shared__ __attribute__((aligned(16))) float Ws[kGN * LDF];
     __shared__ __attribute__((aligned(16))) float Xs[kGM * LDF];
     const GLane L;
@@ -290,8 +291,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_f32_kernel(float* __restrict__
     wait_global_loads();
     for (int k0 = 0; k0 < K; k0 += BK) {
         __syncthreads();
-        sw.store<LDF * 4>(reinterpret_cast<char*>(Ws), L.tid);
-        sx.store<LDF * 4>(reinterpret_cast<char*>(Xs), L.tid);
+        sw.store_swz(reinterpret_cast<char*>(Ws), L.tid);
+        sx.store_swz(reinterpret_cast<char*>(Xs), L.tid);
         __syncthreads();
         if (k0 + BK < K) {
             sw.fetch(rw, ldb, (k0 + BK) * 4, kbytes, L.tid);
@@ -300,12 +301,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_f32_kernel(float* __restrict__
         float a[4][8], b[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float* pa = Ws + (64 * L.wn + 16 * i + L.r16) * LDF + 8 * L.g;
-            const float* pb = Xs + (64 * L.wm + 16 * i + L.r16) * LDF + 8 * L.g;
+            const int ra = 64 * L.wn + 16 * i + L.r16, rb = 64 * L.wm + 16 * i + L.r16;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const float4 va = *reinterpret_cast<const float4*>(pa + 4 * h);
-                const float4 vb = *reinterpret_cast<const float4*>(pb + 4 * h);
+                const float4 va = *reinterpret_cast<const float4*>(
+                    Ws + ra * LDF + 4 * ((2 * L.g + h) ^ swz(ra)));
+                const float4 vb = *reinterpret_cast<const float4*>(
+                    Xs + rb * LDF + 4 * ((2 * L.g + h) ^ swz(rb)));
                 a[i][4 * h + 0] = va.x;
                 a[i][4 * h + 1] = va.y;
                 a[i][4 * h + 2] = va.z;
