@@ -50,7 +50,8 @@ METRIC = "attention fwd+bwd causal TFLOP/s and % MFMA peak, B8 T1024 C768 NH12"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_causal_head_attn_amd", "csrc")
-KERNEL_SOURCE = {"f32": "flash_f32.hip", "f32_ds": "flash_f32.hip", "bf16": "flash_half.hip", "f16": "flash_half.hip"}
+KERNEL_SOURCE = {"f32": "flash_f32.hip", "f32_ds": "flash_f32.hip", "f32_rc": "flash_f32.hip",
+                 "bf16": "flash_half.hip", "f16": "flash_half.hip"}
 
 
 def parse_args():
@@ -156,7 +157,7 @@ def compulsory_bytes(w, dtype):
     """Compulsory HBM bytes of one forward and one backward: the forward
     reads qkv once and writes out and lse; the backward reads qkv, out, dout
     and lse, writes and reads D, and writes dqkv."""
-    esz = 4 if dtype in ("f32", "f32_ds") else 2
+    esz = 4 if dtype.startswith("f32") else 2
     io = w.B * w.T * w.C * esz
     rows = 4 * w.B * w.NH * w.T
     return 3 * io + io + rows, 3 * io + 2 * io + rows + 2 * rows + 3 * io
@@ -175,11 +176,17 @@ def kernel_flops(w, dtype):
     """Algorithmic flops of each kernel for one launch: 2*hs per unmasked
     (query, key) pair per contraction it performs."""
     u = 2 * w.hs * w.pairs * w.B * w.NH
-    if dtype == "f32_ds":           # the fp32 dS block store order
+    if dtype == "f32":              # attn_backward: pre-pass, then dK, dV and dQ in one kernel
         return {"fwd": 2 * u,       # S = Q K^T, O = P V
+                "prepass": 0,       # D = dO.O per row, dQ cleared (HBM-bound)
+                "dkdvdq": 5 * u}    # S, dV, dP, dK, dQ = dS K (added with atomics)
+    if dtype == "f32_ds":           # the fp32 dS block store order
+        return {"fwd": 2 * u,
                 "prepass": 0,       # D = dO.O per row (HBM-bound)
                 "dkdv": 4 * u,      # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q (+ dS stored)
                 "dq": u}            # dQ = dS K from the stored dS
+    # the recompute order: the 16-bit attn_backward_* and the fp32 stages
+    # attn_backward_dq + attn_backward_dkdv ("f32_rc")
     return {"fwd": 2 * u,
             "dkdv": 4 * u,          # S, dV = P^T dO, dP = dO V^T, dK = dS^T Q
             "dq": 3 * u,            # S, dP, dQ = dS K (plus the D = dO.O row sums)
@@ -233,7 +240,7 @@ def warm_up(torch, stages, warmup, warmup_ms):
 
 def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0, warmup_ms=150.0):
     from workloads import workload_inputs
-    qkv_c, dout_c = workload_inputs(w, "f32" if dtype == "f32_ds" else dtype)
+    qkv_c, dout_c = workload_inputs(w, "f32" if dtype.startswith("f32") else dtype)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
     B, T, C, NH = w.B, w.T, w.C, w.NH
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
@@ -241,7 +248,7 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0, warmup_ms=150.0):
     lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
     dqkv = torch.empty_like(qkv)
     D = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
-    sfx = "" if dtype in ("f32", "f32_ds") else "_" + dtype
+    sfx = "" if dtype.startswith("f32") else "_" + dtype
     fwd = getattr(la, "attn_forward" + sfx)
     dkdv = getattr(la, "attn_backward_dkdv" + sfx)
     dq = getattr(la, "attn_backward_dq" + sfx)
@@ -254,6 +261,12 @@ def run_gpu(la, torch, w, dtype, steps, warmup, flush_mb=0, warmup_ms=150.0):
                   ("dkdv", lambda: la.attn_backward_dkdv_ds(dqkv, dS, dout, qkv, lse, D,
                                                             B, T, C, NH, c)),
                   ("dq", lambda: la.attn_backward_dq_ds(dqkv, dS, qkv, B, T, C, NH, c))]
+    elif dtype == "f32":
+        # attn_backward's two stages: D and a cleared dQ, then dK, dV, dQ
+        stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
+                  ("prepass", lambda: la.attn_backward_prepare(dqkv, D, dout, out, B, T, C, NH)),
+                  ("dkdvdq", lambda: la.attn_backward_dkdvdq(dqkv, dout, qkv, lse, D,
+                                                             B, T, C, NH, c))]
     elif short_backward(w, dtype):
         bwd = getattr(la, "attn_backward" + sfx)
         stages = [("fwd", lambda: fwd(out, lse, qkv, B, T, C, NH, c)),
@@ -702,8 +715,9 @@ def main():
         if kf[name]:
             rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
             rec["frac_peak"] = round(rec["tflops"] / peak, 4)
-        else:   # the D pre-pass: reads out and dout, writes D
-            nb = 2 * w.B * w.T * w.C * (4 if dtype == "f32" else 2) + 4 * w.B * w.NH * w.T
+        else:   # the D pre-pass: reads out and dout, writes D (and clears dQ in fp32)
+            nb = (2 * w.B * w.T * w.C * (4 if dtype == "f32" else 2) + 4 * w.B * w.NH * w.T
+                  + (4 * w.B * w.T * w.C if dtype == "f32" else 0))
             rec["gbs"] = round(nb / (ms * 1e-3) / 1e9, 1)
             rec["frac_hbm_peak"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
         kernels[name] = rec
@@ -730,8 +744,11 @@ def main():
         "timing": "ms_per_step and kernels: the C-ABI calls launched one by one, each kernel "
                   "between HIP events; graph_ms_per_step: K replays of the step captured in "
                   "one HIP graph",
-        "backward": "attn_backward's order: dQ (recomputes S and dP from lse, forms D), "
-                    "then dK/dV (recomputes P, reads D); scratch B*NH*T floats",
+        "backward": ("attn_backward: pre-pass (D = dO.O, dQ cleared), then one kernel per "
+                     "key tile forming dV, dK and adding dQ = scale dS K with float atomics; "
+                     "scratch B*NH*T floats" if dtype == "f32" else
+                     "attn_backward's order: dQ (recomputes S and dP from lse, forms D), "
+                     "then dK/dV (recomputes P, reads D); scratch B*NH*T floats"),
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3),
         "wall_ms_per_step": round(wall_ms, 5),
@@ -745,9 +762,23 @@ def main():
     }
 
     if not args.no_extra and dtype == "f32":
+        # the atomic-free recompute order through its stage calls (dQ kernel
+        # recomputing S and dP, then dK/dV): bitwise reproducible dq
+        r_total, r_graph, _, r_kernels, r_stats = run_gpu(la, torch, w, "f32_rc", args.steps,
+                                                          args.warmup, 0, args.warmup_ms)
+        r_val = flops / (r_total * 1e-3) / 1e12
+        rkf = kernel_flops(w, "f32_rc")
+        line["fp32_recompute_order"] = {
+            "order": "dQ (recomputes S and dP, forms D), then dK/dV; no atomics",
+            "ms_per_step": round(r_total, 5), "tflops": round(r_val, 3),
+            "frac_mfma_peak": round(r_val / PEAK_TFLOPS["f32"], 4),
+            "graph_ms_per_step": round(r_graph, 5), "step_stats": r_stats,
+            "kernels": {k: {"ms": round(v, 5),
+                            "frac_peak": round(rkf[k] / (v * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4)}
+                        for k, v in r_kernels.items()}}
+    if not args.no_extra and dtype == "f32":
         # the fp32 dS block store order through the stage calls, with a
-        # caller-owned store of O(T^2) floats (beside the headline, which
-        # runs attn_backward's recompute order)
+        # caller-owned store of O(T^2) floats
         d_total, d_graph, _, d_kernels, d_stats = run_gpu(la, torch, w, "f32_ds", args.steps,
                                                           args.warmup, 0, args.warmup_ms)
         d_val = flops / (d_total * 1e-3) / 1e12

@@ -38,12 +38,18 @@
  * Pointers.  Every tensor pointer is a DEVICE pointer on the current HIP
  * device, 16-byte aligned, owned by the caller; libattn never frees it.
  * bf16 tensors are passed as uint16_t bit patterns (bfloat16, round to
- * nearest even on output).  Outputs are overwritten (=), never accumulated.
- * An output may not overlap any input or another output.
+ * nearest even on output).  Outputs are overwritten (=), never accumulated,
+ * except the dq third of dqkv in attn_backward_dkdvdq, which that stage adds
+ * to.  An output may not overlap any input or another output.
  *
  * Streams.  Calls enqueue work on the calling thread's libattn stream
  * (attn_set_stream; default: the null stream) and return without waiting.
- * Results are deterministic: no atomics, fixed reduction order.
+ * Results are deterministic (fixed reduction order), with one exception: the
+ * dq third of the fp32 attn_backward, attn_backward_noalloc and
+ * attn_backward_dkdvdq is summed with float atomics, so its last bits may
+ * differ from run to run (dk, dv and everything else are bitwise
+ * reproducible; the stages attn_backward_dq + attn_backward_dkdv give a
+ * reproducible fp32 dq).
  *
  * Workspace.  attn_backward, attn_backward_bf16 and attn_backward_f16 need
  * B*NH*T floats of scratch for D (the 16-bit ones not for the shapes they
@@ -98,14 +104,17 @@ int attn_forward(float* out, float* lse, const float* qkv,
 
 /*
  * Fused backward, fp32.  Reads dout (B,T,C), qkv, and the forward's out and
- * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  It runs a dQ kernel that
- * recomputes the probabilities from lse and the products dP = dout V^T
- * itself and also forms D = rowsum(dout*out), then a dK/dV kernel that
- * recomputes the probabilities again and reads D (the stages
- * attn_backward_dq and attn_backward_dkdv below).  Memory is O(B*NH*T): the
- * only scratch is D in the library workspace.  (The dS block store stages
- * further below trade O(T^2) caller-owned memory for two of the dQ
- * kernel's three contractions.)
+ * lse; writes dqkv (B,T,3C) = [dq | dk | dv].  It runs a pre-pass that
+ * forms D = rowsum(dout*out) and clears the dq third, then one kernel per
+ * 64-key tile that recomputes the probabilities from lse, forms dV, dP, dS
+ * = P*(dP - D) and dK, and adds the tile's share of dq = scale * dS K into
+ * the dq third with float atomics (the stages attn_backward_prepare and
+ * attn_backward_dkdvdq below; dq's last bits vary with the order of those
+ * additions).  Memory is O(B*NH*T): the only scratch is D in the library
+ * workspace.  The stages attn_backward_dq + attn_backward_dkdv compute the
+ * same result without atomics, recomputing the probabilities and dP a
+ * second time for dq; the dS block store stages further below trade O(T^2)
+ * caller-owned memory for that recompute.
  */
 int attn_backward(float* dqkv, const float* dout, const float* qkv,
                   const float* out, const float* lse,
@@ -114,8 +123,9 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv,
 /*
  * attn_backward without any allocation, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, hosts
- * that forbid hipMalloc.  Same arguments, kernels and result (bit for bit)
- * as attn_backward; its D scratch (B*NH*T floats) lives in a fixed device
+ * that forbid hipMalloc.  Same arguments, kernels and result as
+ * attn_backward (bit for bit for dk and dv; dq up to the order of its
+ * atomic additions); its D scratch (B*NH*T floats) lives in a fixed device
  * array of 4194304 floats (16 MiB) that each GPU the library runs on holds
  * from library load until the process ends.  Shapes with B*NH*T above
  * that return ATTN_EINVAL before any HIP call.  The first call on a device
@@ -131,16 +141,32 @@ int attn_backward_noalloc(float* dqkv, const float* dout, const float* qkv,
 
 /*
  * The stages of attn_backward, for callers that want to time, order or
- * overlap them, or to own the D buffer (these calls allocate nothing):
- *   attn_backward_dq: writes D (B,NH,T) fp32 = dout . out per row and head
- *       (D[t] = sum_j att[t,j] datt[t,j], the row term of the closed-form
- *       softmax gradient) and the dq third of dqkv;
+ * overlap them, or to own the D buffer (these calls allocate nothing).
+ * D (B,NH,T) fp32 = dout . out per row and head (D[t] = sum_j att[t,j]
+ * datt[t,j], the row term of the closed-form softmax gradient of
+ * softmax_autoregressive_backward_kernel7 in llm.c
+ * dev/cuda/attention_backward.cu); dq_t = scale * sum_j dS[t,j] k_j is the
+ * dq product of attention_backward_cpu there.
+ *   attn_backward_prepare: writes D and sets the dq third of dqkv to 0
+ *       (the dk and dv thirds are not touched);
+ *   attn_backward_dkdvdq: reads D, writes the dk and dv thirds of dqkv and
+ *       ADDS each key tile's share of dq into the dq third (float atomics,
+ *       so dq's last bits depend on their order).  The dq third must hold
+ *       zeros, as attn_backward_prepare leaves it, or the dq to add to.
+ * attn_backward runs prepare then dkdvdq on the same stream.  The recompute
+ * order, deterministic and free of atomics:
+ *   attn_backward_dq: writes D and the dq third of dqkv (it recomputes the
+ *       probabilities and dP itself);
  *   attn_backward_dkdv: reads that D, writes the dk and dv thirds of dqkv.
- * attn_backward runs dq then dkdv on the same stream.
- * attn_backward_preprocess computes D alone (the same value attn_backward_dq
- * writes, up to summation order), for callers that run dkdv first or need D
+ * attn_backward_preprocess computes D alone (the same value the other calls
+ * write, up to summation order), for callers that run dkdv first or need D
  * by itself.
  */
+int attn_backward_prepare(float* dqkv, float* D, const float* dout, const float* out,
+                          int B, int T, int C, int NH);
+int attn_backward_dkdvdq(float* dqkv, const float* dout, const float* qkv,
+                         const float* lse, const float* D,
+                         int B, int T, int C, int NH, int causal);
 int attn_backward_preprocess(float* D, const float* dout, const float* out,
                              int B, int T, int C, int NH);
 int attn_backward_dq(float* dqkv, float* D, const float* dout, const float* qkv,

@@ -1,8 +1,10 @@
 """bench.py's accounting on the CPU: the per-kernel flop counts add up to
-18 * hs * pairs * B * NH for the step attn_backward runs in every dtype
-(whose dQ kernel recomputes S and dP: 4 + 8 + 6) and to the useful
-14 * hs * pairs * B * NH for the fp32 dS block store order (whose dQ kernel
-reads the stored dS: 4 + 8 + 2), and the compulsory HBM bytes
+the useful 14 * hs * pairs * B * NH for the fp32 attn_backward (one kernel
+for dK, dV and dQ: 4 + 10) and for the fp32 dS block store order (whose dQ
+kernel reads the stored dS: 4 + 8 + 2), and to 18 * hs * pairs * B * NH
+for the recompute order that the 16-bit attn_backward_* and the fp32
+stages attn_backward_dq + attn_backward_dkdv run (whose dQ kernel
+recomputes S and dP: 4 + 8 + 6), and the compulsory HBM bytes
 match the figures worked out by hand for the five workloads (forward: qkv
 read, out and lse written; backward: qkv, out, dout, lse read, D written and
 read, dqkv written)."""
@@ -13,14 +15,14 @@ from workloads import WORKLOADS
 
 
 @pytest.mark.parametrize("key", sorted(WORKLOADS))
-@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "f32_rc", "bf16"])
 def test_kernel_flops_add_up_to_the_step(key, dtype):
     w = WORKLOADS[key]
     kf = bench.kernel_flops(w, dtype)
     unit = w.hs * w.pairs * w.B * w.NH
     assert w.flops_fwd + w.flops_bwd == 14 * unit
     staged = {k: v for k, v in kf.items() if k != "bwd_short"}
-    assert sum(staged.values()) == (14 if dtype == "f32_ds" else 18) * unit
+    assert sum(staged.values()) == (14 if dtype in ("f32", "f32_ds") else 18) * unit
     assert kf["fwd"] == w.flops_fwd
     if dtype == "bf16":   # the one-kernel short-sequence backward: five contractions
         assert kf["bwd_short"] == w.flops_bwd == 10 * unit

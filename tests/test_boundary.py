@@ -72,9 +72,9 @@ ENTRY = [("attn_forward", 3), ("attn_backward", 5), ("attn_backward_noalloc", 5)
          ("attn_forward_f16", 3), ("attn_backward_f16", 5),
          ("attn_backward_dkdv_f16", 5), ("attn_backward_dq_f16", 6),
          ("attn_backward_dkdv_ds", 6), ("attn_backward_dq_ds", 3),
-         ("attn_forward_fp8", 3)]
+         ("attn_backward_dkdvdq", 5), ("attn_forward_fp8", 3)]
 STAGE0 = [("attn_backward_preprocess", 3), ("attn_backward_preprocess_bf16", 3),
-          ("attn_backward_preprocess_f16", 3)]
+          ("attn_backward_preprocess_f16", 3), ("attn_backward_prepare", 4)]
 
 
 @pytest.mark.parametrize("name,nptr", ENTRY)

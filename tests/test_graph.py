@@ -2,12 +2,14 @@
 backward, replayed several times with eager work and synchronisations in
 between, gives bitwise the results of the same calls made eagerly (the
 kernels are deterministic, and none of these calls allocates or clears
-memory with a memset)."""
+memory with a memset; the fp32 dq that attn_backward_dkdvdq sums with
+atomics is compared up to the order of those sums)."""
 import sys
 
 import pytest
 import torch
 
+from helpers import assert_atomic_dq_equal
 from workloads import make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -26,6 +28,10 @@ def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
         return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
                 lambda: la.attn_backward_dq(dqkv, D, dout, qkv, out, lse, B, T, C, NH, c),
                 lambda: la.attn_backward_dkdv(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
+    if dtype == "f32_fused":    # what attn_backward runs
+        return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
+                lambda: la.attn_backward_prepare(dqkv, D, dout, out, B, T, C, NH),
+                lambda: la.attn_backward_dkdvdq(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
     if dtype == "f32_ds":
         return [lambda: la.attn_forward(out, lse, qkv, B, T, C, NH, c),
                 lambda: la.attn_backward_preprocess(D, dout, out, B, T, C, NH),
@@ -39,7 +45,7 @@ def _stages(la, dtype, qkv, dout, out, lse, D, dS, dqkv, B, T, C, NH, c):
             lambda: la.attn_backward_dkdv_bf16(dqkv, dout, qkv, lse, D, B, T, C, NH, c)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f32_ds", "bf16", "bf16_fused"])
+@pytest.mark.parametrize("dtype", ["f32", "f32_fused", "f32_ds", "bf16", "bf16_fused"])
 def test_graph_replays_equal_eager(la, dtype):
     B, T, C, NH, c = 2, 150, 256, 4, 1
     print(f"\n[case] graph replay {dtype} B{B} T{T} C{C} NH{NH}", flush=True)
@@ -72,6 +78,9 @@ def test_graph_replays_equal_eager(la, dtype):
         torch.cuda.synchronize()
         got = (out.clone(), lse.clone(), dqkv.clone())
         for name, a, b in zip(("out", "lse", "dqkv"), got, ref):
+            if dtype == "f32_fused" and name == "dqkv":
+                assert_atomic_dq_equal(a, b, C, f"replay {r}")
+                continue
             assert torch.equal(a, b), f"replay {r}: {name} differs from the eager result"
         # eager work between replays, on the same library state
         o2, l2 = la.forward(other, NH, True)
@@ -114,7 +123,10 @@ def test_captured_fused_backward_survives_workspace_growth(la, dtype):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(dqkv, ref), f"replay {r} after growth differs from the eager result"
+        if dtype == "f32":    # dq summed with atomics
+            assert_atomic_dq_equal(dqkv, ref, C, f"replay {r} after growth")
+        else:
+            assert torch.equal(dqkv, ref), f"replay {r} after growth differs from the eager result"
 
 
 def test_fp8_forward_graph_replays(la):

@@ -5,7 +5,7 @@ import sys
 import pytest
 import torch
 
-from helpers import assert_close, gpu_fwd_bwd
+from helpers import assert_atomic_dq_equal, assert_close, gpu_fwd_bwd
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -80,18 +80,40 @@ def test_gpt2_layer_all_heads(la, oracle_mod):
     assert_close(dqkv, rd, "f32", "dqkv")
 
 
+def _recompute_backward(la, qkv, dout, out, lse, NH, causal):
+    """dqkv from the atomic-free stages (dQ kernel that recomputes S and dP,
+    then dK/dV): bitwise reproducible."""
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    D = torch.empty((B, NH, T), device="cuda")
+    g = torch.empty_like(qkv)
+    la.attn_backward_dq(g, D, dout, qkv, out, lse, B, T, C, NH, int(causal))
+    la.attn_backward_dkdv(g, dout, qkv, lse, D, B, T, C, NH, int(causal))
+    return g
+
+
 def test_deterministic(la):
-    """Two runs on the same inputs are bitwise identical (no atomics)."""
+    """Two runs on the same inputs: out, lse, dk and dv bitwise identical,
+    dq equal up to the order of its atomic sums; the recompute stages
+    (no atomics) bitwise identical."""
     qkv, dout = make_inputs(2, 300, 256, "f32", seed=5)
     a = gpu_fwd_bwd(la, qkv, dout, 4, True)
     b = gpu_fwd_bwd(la, qkv, dout, 4, True)
-    for x, y in zip(a, b):
-        assert torch.equal(x, y)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert_atomic_dq_equal(a[2], b[2], 256)
+    q, d = qkv.cuda(), dout.cuda()
+    out, lse = la.forward(q, 4, True)
+    r1 = _recompute_backward(la, q, d, out, lse, 4, True)
+    r2 = _recompute_backward(la, q, d, out, lse, 4, True)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
 
 
 def test_causality(la):
     """Changing k and v at positions >= t0 leaves out, lse and dq of rows
-    < t0 bitwise unchanged (masked probabilities are exactly 0)."""
+    < t0 unchanged (masked probabilities are exactly 0): bitwise for out,
+    lse and the recompute stages' dq, up to the order of its atomic sums for
+    attn_backward's dq."""
     B, T, C, NH = 2, 250, 256, 4
     t0 = 97
     qkv, dout = make_inputs(B, T, C, "f32", seed=6)
@@ -101,7 +123,14 @@ def test_causality(la):
     o2, l2, d2 = gpu_fwd_bwd(la, qkv2, dout, NH, True)
     assert torch.equal(o1[:, :t0], o2[:, :t0])
     assert torch.equal(l1[:, :, :t0], l2[:, :, :t0])
-    assert torch.equal(d1[:, :t0, :C], d2[:, :t0, :C])
+    a, b = d1[:, :t0, :C], d2[:, :t0, :C]
+    assert (a - b).abs().max().item() <= 1e-5 * a.abs().max().item()
+    r = []
+    for q in (qkv, qkv2):
+        qg, dg = q.cuda(), dout.cuda()
+        out, lse = la.forward(qg, NH, True)
+        r.append(_recompute_backward(la, qg, dg, out, lse, NH, True).cpu())
+    assert torch.equal(r[0][:, :t0, :C], r[1][:, :t0, :C])
 
 
 def test_first_row_and_single_token_exact(la):
@@ -148,18 +177,24 @@ def test_respects_torch_stream(la, oracle_mod):
 
 
 def test_stages_equal_fused_backward(la):
-    """attn_backward (fp32) is the dQ kernel that recomputes S and dP and
-    writes D, then dK/dV: the two stage calls give the same bits.  The dS
-    block store order (pre-pass D, dK/dV writing dS, dQ from dS) agrees up
-    to fp32 summation order, and its dK/dV gives the same dk and dv bits as
-    the plain dK/dV kernel run from the same D."""
-    B, T, C, NH = 2, 190, 256, 4
+    """attn_backward (fp32) is the pre-pass (D, dq cleared) then the kernel
+    that forms dK, dV and adds dQ: the two stage calls give its dk and dv
+    bits and its dq up to the order of the atomic sums.  The dK/dV part of
+    that kernel is the plain dK/dV kernel's arithmetic: from the same D it
+    gives the same dk and dv bits.  The recompute stages (dQ kernel forming
+    its own D, then dK/dV) and the dS block store order (pre-pass D, dK/dV
+    writing dS, dQ from dS) agree up to fp32 summation order."""
+    B, T, C, NH = 2, 300, 256, 4
     _case(f"f32 stages B{B} T{T} C{C} NH{NH}")
     qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=33)
     qkv, dout = qkv_c.cuda(), dout_c.cuda()
     out, lse = la.forward(qkv, NH, True)
     ref = la.backward(dout, qkv, out, lse, NH, True)
     nan = float("nan")
+    D1 = torch.full((B, NH, T), nan, device="cuda")
+    g1 = torch.full_like(qkv, nan)
+    la.attn_backward_prepare(g1, D1, dout, out, B, T, C, NH)
+    la.attn_backward_dkdvdq(g1, dout, qkv, lse, D1, B, T, C, NH, 1)
     D2 = torch.full((B, NH, T), nan, device="cuda")
     g2 = torch.full_like(qkv, nan)
     la.attn_backward_dq(g2, D2, dout, qkv, out, lse, B, T, C, NH, 1)
@@ -173,10 +208,35 @@ def test_stages_equal_fused_backward(la):
     g3 = torch.full_like(qkv, nan)
     la.attn_backward_dkdv(g3, dout, qkv, lse, D, B, T, C, NH, 1)
     torch.cuda.synchronize()
-    assert torch.equal(g2, ref)
-    torch.testing.assert_close(D2, D, rtol=1e-5, atol=1e-5)
-    torch.testing.assert_close(g, ref, rtol=1e-5, atol=1e-5)
+    assert_atomic_dq_equal(g1, ref, C, "prepare + dkdvdq")
+    assert torch.equal(D1, D)                      # the same pre-pass kernel
+    assert torch.equal(g3[:, :, C:], ref[:, :, C:])
     assert torch.equal(g3[:, :, C:], g[:, :, C:])
+    torch.testing.assert_close(D2, D, rtol=1e-5, atol=1e-5)
+    torch.testing.assert_close(g2, ref, rtol=1e-5, atol=1e-5)
+    torch.testing.assert_close(g, ref, rtol=1e-5, atol=1e-5)
+
+
+def test_dkdvdq_adds_into_dq(la, oracle_mod):
+    """attn_backward_dkdvdq adds its dq into the dq third and overwrites dk
+    and dv: run twice after one attn_backward_prepare, dq is twice the
+    gradient and dk, dv are unchanged; on a ragged non-causal shape whose
+    last key tile runs past T."""
+    B, T, C, NH = 2, 161, 256, 4
+    _case(f"f32 dkdvdq accumulation B{B} T{T} C{C} NH{NH}")
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=34)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    out, lse = la.forward(qkv, NH, False)
+    D = torch.empty((B, NH, T), device="cuda")
+    g = torch.full_like(qkv, float("nan"))
+    la.attn_backward_prepare(g, D, dout, out, B, T, C, NH)
+    la.attn_backward_dkdvdq(g, dout, qkv, lse, D, B, T, C, NH, 0)
+    once = g.clone()
+    la.attn_backward_dkdvdq(g, dout, qkv, lse, D, B, T, C, NH, 0)
+    torch.cuda.synchronize()
+    assert_close(once, oracle_mod.backward(qkv_c, dout_c, NH, False), "f32", "dqkv")
+    assert torch.equal(g[:, :, C:], once[:, :, C:])
+    torch.testing.assert_close(g[:, :, :C], 2 * once[:, :, :C], rtol=1e-5, atol=1e-5)
 
 
 RECOMPUTE_SHAPES = [(1, 1, 64, 4), (2, 65, 128, 2), (1, 100, 96, 3), (1, 129, 512, 4),

@@ -9,7 +9,8 @@ if it cannot.
 from ._binding import (  # noqa: F401
     ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_OK, EXPORTS, LIB_PATH, AttnError,
     attn_backward, attn_backward_bf16, attn_backward_dkdv, attn_backward_dkdv_bf16,
-    attn_backward_noalloc, attn_forward_splitkv_chunk, attn_forward_splitkv_bytes,
+    attn_backward_noalloc, attn_backward_prepare, attn_backward_dkdvdq,
+    attn_forward_splitkv_chunk, attn_forward_splitkv_bytes,
     attn_forward_splitkv_bf16, attn_forward_splitkv_f16, forward_splitkv,
     attn_backward_splitkv_bytes, attn_backward_splitkv_bf16, attn_backward_splitkv_f16,
     backward_splitkv,

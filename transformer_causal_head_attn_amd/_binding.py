@@ -25,6 +25,7 @@ ATTN_EHIP = -3
 
 EXPORTS = (
     "attn_forward", "attn_backward", "attn_backward_noalloc",
+    "attn_backward_prepare", "attn_backward_dkdvdq",
     "attn_backward_preprocess", "attn_backward_dkdv", "attn_backward_dq",
     "attn_backward_ds_bytes", "attn_backward_dkdv_ds", "attn_backward_dq_ds",
     "attn_forward_bf16", "attn_backward_bf16",
@@ -73,6 +74,7 @@ def load(path: str | None = None):
                            ("attn_forward_materialized", 4),
                            ("attn_backward_materialized", 6),
                            ("attn_backward_dkdv", 5), ("attn_backward_dq", 6),
+                           ("attn_backward_dkdvdq", 5),
                            ("attn_backward_dkdv_bf16", 5), ("attn_backward_dq_bf16", 6),
                            ("attn_forward_f16", 3), ("attn_backward_f16", 5),
                            ("attn_forward_fp8", 3),
@@ -86,6 +88,8 @@ def load(path: str | None = None):
             fn = getattr(lib, name)
             fn.argtypes = [vp] * 3 + [i] * 4
             fn.restype = i
+        lib.attn_backward_prepare.argtypes = [vp] * 4 + [i] * 4
+        lib.attn_backward_prepare.restype = i
         lib.attn_forward_splitkv_chunk.argtypes = [i] * 5
         lib.attn_forward_splitkv_chunk.restype = i
         lib.attn_forward_splitkv_bytes.argtypes = [i] * 6
@@ -183,6 +187,21 @@ def attn_backward_noalloc(dqkv, dout, qkv, out, lse, B, T, C, NH, causal) -> Non
     _call("attn_backward_noalloc", _check(dqkv, "dqkv", f, B * T * 3 * C),
           _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
           _check(out, "out", f, B * T * C), _check(lse, "lse", f, B * NH * T),
+          *_dims(B, T, C, NH, causal))
+
+
+def attn_backward_prepare(dqkv, D, dout, out, B, T, C, NH) -> None:
+    f = torch.float32
+    _call("attn_backward_prepare", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(D, "D", f, B * NH * T), _check(dout, "dout", f, B * T * C),
+          _check(out, "out", f, B * T * C), int(B), int(T), int(C), int(NH))
+
+
+def attn_backward_dkdvdq(dqkv, dout, qkv, lse, D, B, T, C, NH, causal) -> None:
+    f = torch.float32
+    _call("attn_backward_dkdvdq", _check(dqkv, "dqkv", f, B * T * 3 * C),
+          _check(dout, "dout", f, B * T * C), _check(qkv, "qkv", f, B * T * 3 * C),
+          _check(lse, "lse", f, B * NH * T), _check(D, "D", f, B * NH * T),
           *_dims(B, T, C, NH, causal))
 
 

@@ -226,14 +226,15 @@ int attn_backward(float* dqkv, const float* dout, const float* qkv, const float*
                         {lse, nbytes(BT * NH, 4), "lse"}};
     int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
     if (rc) return rc;
-    // the recompute order: dQ (recomputes S and dP, forms D = dO . O per
-    // row), then dK/dV (reads D); the only workspace is D, B*NH*T floats
+    // the pre-pass (D = dO . O per row, dQ slot cleared), then one kernel
+    // for dK, dV and dQ (dQ added with atomics); the only workspace is D,
+    // B*NH*T floats
     float* D = nullptr;
     rc = workspace(nbytes(BT * NH, 4), &D);
     if (rc) return rc;
     const attn::Shape s = shape_of(B, T, C, NH, causal);
-    hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
-    if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
+    hipError_t e = attn::launch_prepare_f32(dqkv, D, dout, out, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdvdq_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward launch");
 }
 
@@ -251,14 +252,14 @@ int attn_backward_noalloc(float* dqkv, const float* dout, const float* qkv, cons
         return fail(ATTN_EINVAL,
                     "attn_backward_noalloc: B*NH*T = %lld exceeds the fixed scratch of %zu floats",
                     BT * NH, kNoAllocScratchFloats);
-    // D lives in the fixed scratch: written in full by the dQ kernel before
-    // the dK/dV kernel reads it, so nothing needs clearing
+    // D lives in the fixed scratch: written in full by the pre-pass before
+    // the dK/dV/dQ kernel reads it, so nothing needs clearing
     float* D = nullptr;
     rc = scratch_for_device(&D);
     if (rc) return rc;
     const attn::Shape s = shape_of(B, T, C, NH, causal);
-    hipError_t e = attn::launch_dq_f32(dqkv, D, dout, qkv, out, lse, s, g_stream);
-    if (e == hipSuccess) e = attn::launch_dkdv_f32(dqkv, dout, qkv, lse, D, s, g_stream);
+    hipError_t e = attn::launch_prepare_f32(dqkv, D, dout, out, s, g_stream);
+    if (e == hipSuccess) e = attn::launch_dkdvdq_f32(dqkv, dout, qkv, lse, D, s, g_stream);
     return launched(e, "attn_backward_noalloc launch");
 }
 
@@ -316,6 +317,33 @@ int attn_backward_preprocess(float* D, const float* dout, const float* out, int 
     if (rc) return rc;
     return launched(attn::launch_prepass_f32(D, dout, out, shape_of(B, T, C, NH, 0), g_stream),
                     "attn_backward_preprocess launch");
+}
+
+int attn_backward_prepare(float* dqkv, float* D, const float* dout, const float* out, int B,
+                          int T, int C, int NH) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}, {D, nbytes(BT * NH, 4), "D"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"}, {out, nbytes(BT * C, 4), "out"}};
+    int rc = check_args(B, T, C, NH, 0, outs, 2, ins, 2, false);
+    if (rc) return rc;
+    return launched(attn::launch_prepare_f32(dqkv, D, dout, out, shape_of(B, T, C, NH, 0),
+                                             g_stream),
+                    "attn_backward_prepare launch");
+}
+
+int attn_backward_dkdvdq(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                         const float* D, int B, int T, int C, int NH, int causal) {
+    const long long BT = (long long)B * T;
+    const Span outs[] = {{dqkv, nbytes(BT * 3 * C, 4), "dqkv"}};
+    const Span ins[] = {{dout, nbytes(BT * C, 4), "dout"},
+                        {qkv, nbytes(BT * 3 * C, 4), "qkv"},
+                        {lse, nbytes(BT * NH, 4), "lse"},
+                        {D, nbytes(BT * NH, 4), "D"}};
+    int rc = check_args(B, T, C, NH, causal, outs, 1, ins, 4, false);
+    if (rc) return rc;
+    return launched(attn::launch_dkdvdq_f32(dqkv, dout, qkv, lse, D,
+                                            shape_of(B, T, C, NH, causal), g_stream),
+                    "attn_backward_dkdvdq launch");
 }
 
 int attn_backward_dkdv(float* dqkv, const float* dout, const float* qkv, const float* lse,

@@ -191,6 +191,12 @@ hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, con
                            const float* D, const Shape& s, hipStream_t st);
 hipError_t launch_dq_f32(float* dqkv, float* D, const float* dout, const float* qkv,
                          const float* out, const float* lse, const Shape& s, hipStream_t st);
+// the pre-pass that also clears dqkv's dQ slot, and one dK/dV kernel that
+// also adds dQ into that slot with atomics
+hipError_t launch_prepare_f32(float* dqkv, float* D, const float* dout, const float* out,
+                             const Shape& s, hipStream_t st);
+hipError_t launch_dkdvdq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                             const float* D, const Shape& s, hipStream_t st);
 // dS block store variant of the fp32 backward: dK/dV also writes dS, dQ reads it
 size_t ds_store_floats(const Shape& s);
 hipError_t launch_dkdv_ds_f32(float* dqkv, float* dS, const float* dout, const float* qkv,

@@ -306,11 +306,14 @@ __device__ __forceinline__ void fwd_f32_tile(int tile_, int bh_, float* __restri
 // ------------------------------------------------------ backward pre-pass
 // D[b,h,t] = sum_i dout[b,t,h*hs+i] * out[b,t,h*hs+i], one group of HS/4
 // lanes per (b,t,h) row, rows in memory order.
+// With dq non-null it also clears the dQ slot of the same row of dqkv (row
+// stride 3C), where the fused backward then adds its dQ contributions.
 template <int HS>
 __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict__ D,
                                                                const float* __restrict__ dout,
                                                                const float* __restrict__ out,
-                                                               int T, int NH, long long rows) {
+                                                               int T, int NH, long long rows,
+                                                               float* __restrict__ dq) {
     constexpr int G = HS / 4;
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
     const long long row = gid / G;
@@ -320,6 +323,12 @@ __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict
         const float4 a = *reinterpret_cast<const float4*>(dout + row * HS + 4 * part);
         const float4 c = *reinterpret_cast<const float4*>(out + row * HS + 4 * part);
         acc = a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+        if (dq) {
+            const long long bt = row / NH;
+            const int h = (int)(row - bt * NH);
+            *reinterpret_cast<float4*>(dq + bt * 3 * NH * HS + h * HS + 4 * part) =
+                make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
 #pragma unroll
     for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -338,7 +347,16 @@ __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict
 // dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS (scale applied at the end).
 // With STORE_DS it also writes each 64x64 block of dS (unscaled) to the dS
 // block store, for the dQ kernel that consumes it (bwd_dq_ds_f32_tile).
-template <int HS, bool STORE_DS>
+// With DQ it also forms dQ: each Q tile's dS block goes through LDS (dSt,
+// query rows), and during the next Q tile's step every wave multiplies its
+// 16 query rows of it by the key tile (Kt, held transposed and scaled for
+// the whole loop) and adds the 16 x HS result into dqkv's dQ slot with
+// global float atomics.  The slot must be cleared first (the pre-pass does
+// it), and the order of the additions, hence dQ's last bits, varies from run
+// to run.  The atomics of a step are issued before the next Q tile's
+// prefetch: the compiler makes the wait for those loads also cover every
+// store issued before them, which then has a whole step to complete.
+template <int HS, bool STORE_DS, bool DQ = false>
 __device__ __forceinline__ void bwd_dkdv_f32_tile(
     int tile_, int bh_, float* __restrict__ dqkv, float* __restrict__ dsw,
     const float* __restrict__ dout, const float* __restrict__ qkv, const float* __restrict__ lse,
@@ -357,6 +375,14 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     // per-wave 16 x 16 transpose scratch for the dS store (kTrLd floats a row)
     constexpr int kTrLd = 20, kTrWave = 16 * kTrLd;
     __shared__ __attribute__((aligned(16))) float Tr[STORE_DS ? 4 * kTrWave : 4];
+    // DQ: dS of the last Q tile by query row, and the key tile transposed
+    // (row = head dimension) and multiplied by scale; rows of 64 keys padded
+    // to 68 floats, so the 16 rows of one 16-byte read pass fall on
+    // distinct bank groups
+    constexpr int LDT = kTile + 4;
+    __shared__ __attribute__((aligned(16))) float dSt[DQ ? kTile * LDT : 4];
+    __shared__ __attribute__((aligned(16))) float Kt[DQ ? HS * LDT : 4];
+    static_assert(!(DQ && STORE_DS), "one dQ route at a time");
 
     const Lane L;
     const int nt = (T + kTile - 1) / kTile;
@@ -374,6 +400,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     float kreg[KS], vreg[KS];
     load_row_part<HS>(kreg, kbase + (size_t)kvrow * C3, kvrow < T, L.g);
     load_row_part<HS>(vreg, vbase + (size_t)kvrow * C3, kvrow < T, L.g);
+    if constexpr (DQ) {   // read by the first dQ product, after the loop's barriers
+#pragma unroll
+        for (int k = 0; k < KS; ++k) Kt[(KS * L.g + k) * LDT + 16 * L.w + L.r16] = kreg[k] * scale;
+    }
     // K enters only S: scaled once by scale*log2e, S comes out in the log2
     // domain of the exponent
 #pragma unroll
@@ -408,6 +438,41 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     [[maybe_unused]] const int ds_lane = 64 * (L.r16 >> 2) + 4 * (L.r16 & 3);
     [[maybe_unused]] const bool kv_in = kvrow < T;
     [[maybe_unused]] const bool kv_full = (kt + 1) * kTile <= T;   // no key of the tile past T
+    // DQ: dQ rows qtp*64 + 16w + 4g + i, columns 16mb + r16 from dSt and Kt
+    // (the contraction runs over the tile's keys 16g + 4c + j in lane group g)
+    [[maybe_unused]] float* dqbase = dqkv + (size_t)b * T * C3 + (size_t)h * HS;
+    [[maybe_unused]] auto dq_product = [&](int qtp) {
+        f32x4 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* ar = dSt + (16 * L.w + L.r16) * LDT + 16 * L.g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 a4 = *reinterpret_cast<const float4*>(ar + 4 * c);
+            float4 b4[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                b4[mb] = *reinterpret_cast<const float4*>(Kt + (16 * mb + L.r16) * LDT + 16 * L.g +
+                                                          4 * c);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.x, b4[mb].x, acc[mb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.y, b4[mb].y, acc[mb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.z, b4[mb].z, acc[mb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.w, b4[mb].w, acc[mb]);
+        }
+        const int q0 = qtp * kTile + 16 * L.w + 4 * L.g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (q0 + i < T) {
+                float* row = dqbase + (size_t)(q0 + i) * C3 + L.r16;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) unsafeAtomicAdd(row + 16 * mb, acc[mb][i]);
+            }
+        }
+    };
     for (int qt = qt0; qt < nt; ++qt) {
         __syncthreads();
         rq.template store<LDK>(Qs, L.tid);
@@ -417,8 +482,16 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
             Ls[L.tid] = in ? -rl * kLog2e : -INFINITY;   // -inf -> P = 0
             Dl[L.tid] = in ? -rD : 0.f;
         }
-        __syncthreads();
-        if (qt + 1 < nt) fetch(qt + 1);
+        if constexpr (DQ) {
+            // the previous Q tile's dS is complete (first barrier); this
+            // step's dS writes come after the second barrier
+            if (qt > qt0) dq_product(qt - 1);
+            if (qt + 1 < nt) fetch(qt + 1);
+            __syncthreads();
+        } else {
+            __syncthreads();
+            if (qt + 1 < nt) fetch(qt + 1);
+        }
         const bool diag = causal && (qt == kt);
 
 #pragma unroll
@@ -485,6 +558,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 // it back; with the hint on both sides the step is ~1% faster)
                 __builtin_nontemporal_store(f32x4{y.x, y.y, y.z, y.w}, reinterpret_cast<f32x4*>(blk));
             }
+            if constexpr (DQ) {   // entry (query 16n + 4g + i, key 16w + r16)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dSt[(16 * n + 4 * L.g + i) * LDT + 16 * L.w + L.r16] = ds[i];
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ql = 16 * n + 4 * L.g + i;
@@ -499,6 +576,10 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
         }
     }
 
+    if constexpr (DQ) {
+        __syncthreads();
+        dq_product(nt - 1);
+    }
     if (kvrow < T) {
         float* dkrow = dqkv + ((size_t)b * T + kvrow) * C3 + C + (size_t)h * HS;
         float* dvrow = dkrow + C;
@@ -744,19 +825,19 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
 // hs <= 64 without the dS store: three workgroups per CU (162 VGPRs; the
 // compiler's own choice was 174, two per CU): GPT-2 layer dK/dV 220 -> 214
 // us, same bits.  With the store the same cap spills.
-template <int HS, bool STORE_DS>
-__global__ __launch_bounds__(kThreads, HS >= 128 || STORE_DS ? 1 : 3) void bwd_dkdv_f32_kernel(
+template <int HS, bool STORE_DS, bool DQ = false>
+__global__ __launch_bounds__(kThreads, HS >= 128 || STORE_DS ? 1 : (DQ ? 2 : 3)) void bwd_dkdv_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
     const float* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ Dws,
     int T, int C, int NH, int causal, float scale, float scale_log2, int paired, Deal deal) {
     const int nt = (T + kTile - 1) / kTile;
     int bh, ta, tb;
     pair_of_block(gridDim.x / grid_tiles(nt, paired), nt, paired, false, deal, bh, ta, tb);
-    bwd_dkdv_f32_tile<HS, STORE_DS>(ta, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
+    bwd_dkdv_f32_tile<HS, STORE_DS, DQ>(ta, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
                                     scale, scale_log2);
     if (tb >= 0) {
         __syncthreads();
-        bwd_dkdv_f32_tile<HS, STORE_DS>(tb, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
+        bwd_dkdv_f32_tile<HS, STORE_DS, DQ>(tb, bh, dqkv, dsw, dout, qkv, lse, Dws, T, C, NH, causal,
                                         scale, scale_log2);
     }
 }
@@ -806,12 +887,12 @@ hipError_t fwd_f32_hs(float* out, float* lse, const float* qkv, const Shape& s, 
 
 template <int HS>
 hipError_t prepass_f32_hs(float* D, const float* dout, const float* out, const Shape& s,
-                          hipStream_t st) {
+                          hipStream_t st, float* dq = nullptr) {
     const long long rows = (long long)s.B * s.T * s.NH;
     const long long threads = rows * (HS / 4);
     const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(prepass_f32_kernel<HS>, dim3(grid), dim3(kThreads), 0, st, D, dout, out,
-                       s.T, s.NH, rows);
+                       s.T, s.NH, rows, dq);
     return hipGetLastError();
 }
 
@@ -836,6 +917,23 @@ hipError_t dkdv_f32_hs(float* dqkv, float* dsw, const float* dout, const float* 
                            dqkv, dsw, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
                            scale * kLog2e, (int)paired,
                            deal_for<bwd_dkdv_f32_kernel<HS, false>>(kThreads));
+    return hipGetLastError();
+}
+
+// One kernel for dK, dV and dQ (bwd_dkdv_f32_tile with DQ): 5 contractions
+// per score instead of the recompute order's 7.  D and a cleared dQ slot
+// come from the pre-pass (prepass_f32_hs with dq).
+template <int HS>
+hipError_t dkdvdq_f32_hs(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                         const float* D, const Shape& s, hipStream_t st) {
+    const int nt = (s.T + kTile - 1) / kTile;
+    const bool paired = false;   // heaviest first, as the dK/dV kernel
+    const unsigned grid = (unsigned)(grid_tiles(nt, paired) * s.B * s.NH);
+    const float scale = (float)(1.0 / sqrt((double)HS));
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HS, false, true>), dim3(grid), dim3(kThreads), 0, st,
+                       dqkv, nullptr, dout, qkv, lse, D, s.T, s.C, s.NH, s.causal, scale,
+                       scale * kLog2e, (int)paired,
+                       deal_for<bwd_dkdv_f32_kernel<HS, false, true>>(kThreads));
     return hipGetLastError();
 }
 
@@ -893,6 +991,16 @@ hipError_t launch_dkdv_f32(float* dqkv, const float* dout, const float* qkv, con
 hipError_t launch_dkdv_ds_f32(float* dqkv, float* dS, const float* dout, const float* qkv,
                               const float* lse, const float* D, const Shape& s, hipStream_t st) {
     ATTN_DISPATCH_HS(dkdv_f32_hs, dqkv, dS, dout, qkv, lse, D, s, st)
+}
+
+hipError_t launch_prepare_f32(float* dqkv, float* D, const float* dout, const float* out,
+                             const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(prepass_f32_hs, D, dout, out, s, st, dqkv)
+}
+
+hipError_t launch_dkdvdq_f32(float* dqkv, const float* dout, const float* qkv, const float* lse,
+                             const float* D, const Shape& s, hipStream_t st) {
+    ATTN_DISPATCH_HS(dkdvdq_f32_hs, dqkv, dout, qkv, lse, D, s, st)
 }
 
 hipError_t launch_dq_ds_f32(float* dqkv, const float* dS, const float* qkv, const Shape& s,
