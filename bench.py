@@ -10,7 +10,7 @@ The fp32 dS block store order (the D pre-pass, a dK/dV kernel that also
 stores dS, a dQ kernel that reads it; O(T^2) caller-owned memory) is timed
 beside it as fp32_ds_store_order.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16]
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--dtype f32|bf16|f16|f32_rc|f32_ds]
 
 value = useful fwd+bwd TFLOP/s = (4 + 10) * hs * pairs * B * NH / step time,
 pairs = T(T+1)/2 for causal (masked pairs are not counted; the backward's
@@ -66,7 +66,9 @@ def parse_args():
                         "speed only after ~30 ms (fp32) to ~70 ms (bf16) of work, whatever "
                         "the step count")
     p.add_argument("--workload", type=int, default=3)
-    p.add_argument("--dtype", choices=["f32", "bf16", "f16"], default=None)
+    # f32_rc / f32_ds: the fp32 step through the recompute-order or the dS
+    # block store stage calls instead of attn_backward's
+    p.add_argument("--dtype", choices=["f32", "f32_rc", "f32_ds", "bf16", "f16"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="CPU seconds the oracle baseline may spend on its sample")
@@ -706,7 +708,7 @@ def main():
                                                              args.warmup_ms)
     flops = w.flops_fwd + w.flops_bwd
     value = flops / (total_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[dtype]
+    peak = PEAK_TFLOPS[dtype.split("_")[0]]
 
     kf = kernel_flops(w, dtype)
     kernels = {}
@@ -716,8 +718,8 @@ def main():
             rec["tflops"] = round(kf[name] / (ms * 1e-3) / 1e12, 2)
             rec["frac_peak"] = round(rec["tflops"] / peak, 4)
         else:   # the D pre-pass: reads out and dout, writes D (and clears dQ in fp32)
-            nb = (2 * w.B * w.T * w.C * (4 if dtype == "f32" else 2) + 4 * w.B * w.NH * w.T
-                  + (4 * w.B * w.T * w.C if dtype == "f32" else 0))
+            nb = (2 * w.B * w.T * w.C * (4 if dtype.startswith("f32") else 2)
+                  + 4 * w.B * w.NH * w.T + (4 * w.B * w.T * w.C if dtype == "f32" else 0))
             rec["gbs"] = round(nb / (ms * 1e-3) / 1e9, 1)
             rec["frac_hbm_peak"] = round(rec["gbs"] / PEAK_HBM_GBS, 4)
         kernels[name] = rec
@@ -747,7 +749,9 @@ def main():
         "backward": ("attn_backward: pre-pass (D = dO.O, dQ cleared), then one kernel per "
                      "key tile forming dV, dK and adding dQ = scale dS K with float atomics; "
                      "scratch B*NH*T floats" if dtype == "f32" else
-                     "attn_backward's order: dQ (recomputes S and dP from lse, forms D), "
+                     "dS block store stages: pre-pass D, dK/dV also storing dS, dQ = scale dS K "
+                     "from the store; O(T^2) caller-owned floats" if dtype == "f32_ds" else
+                     "the recompute order: dQ (recomputes S and dP from lse, forms D), "
                      "then dK/dV (recomputes P, reads D); scratch B*NH*T floats"),
         "graph_ms_per_step": round(graph_ms, 5),
         "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3),
