@@ -153,6 +153,10 @@ int attn_backward_noalloc(float* dqkv, const float* dout, const float* qkv,
  *       ADDS each key tile's share of dq into the dq third (float atomics,
  *       so dq's last bits depend on their order).  The dq third must hold
  *       zeros, as attn_backward_prepare leaves it, or the dq to add to.
+ *       dqkv must be ordinary device memory of the GPU the call runs on
+ *       (hipMalloc, as torch allocates it): the hardware float atomics are
+ *       not defined on host-mapped or fine-grained memory.  The same holds
+ *       for attn_backward and attn_backward_noalloc.
  * attn_backward runs prepare then dkdvdq on the same stream.  The recompute
  * order, deterministic and free of atomics:
  *   attn_backward_dq: writes D and the dq third of dqkv (it recomputes the
