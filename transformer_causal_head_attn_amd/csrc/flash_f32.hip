@@ -34,13 +34,15 @@
 //  * the forward raises a row's running maximum only when a tile's maximum
 //    exceeds it by more than 2^kLazyMax (log2 domain), as the 16-bit forward
 //    does, and folds the scale into the exponent's FMA;
-//  * the fused backward (attn_backward) runs the dQ kernel that recomputes
-//    S and dP and also forms D = dO . O (bwd_dq_f32_tile), then dK/dV,
-//    keeping memory O(B*NH*T).  A second order, for callers that own an
-//    O(T^2) buffer, lets dK/dV store dS (bwd_dkdv_f32_tile<HS, true>) so
-//    that the dQ kernel (bwd_dq_ds_f32_tile) performs one contraction
-//    instead of three: on the fp32 matrix cores recomputing S and dP costs
-//    more than writing dS once and reading it back.
+//  * the fused backward (attn_backward) runs a pre-pass that forms
+//    D = dO . O and clears dQ, then one dK/dV kernel that also forms dQ and
+//    adds it with float atomics (bwd_dkdv_f32_tile with DQ): five
+//    contractions per score, memory O(B*NH*T).  Two atomic-free orders stay
+//    available as stage calls: the dQ kernel that recomputes S and dP and
+//    forms D (bwd_dq_f32_tile), then dK/dV; and, for callers that own an
+//    O(T^2) buffer, dK/dV storing dS (bwd_dkdv_f32_tile<HS, true>) so that
+//    the dQ kernel (bwd_dq_ds_f32_tile) performs one contraction instead
+//    of three.
 #include "common.hpp"
 
 
@@ -824,7 +826,8 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
 
 // hs <= 64 without the dS store: three workgroups per CU (162 VGPRs; the
 // compiler's own choice was 174, two per CU): GPT-2 layer dK/dV 220 -> 214
-// us, same bits.  With the store the same cap spills.
+// us, same bits.  With the store the same cap spills.  With DQ the LDS
+// (68.5 KB at hs = 64) allows two per CU, and 218 VGPRs fit that.
 template <int HS, bool STORE_DS, bool DQ = false>
 __global__ __launch_bounds__(kThreads, HS >= 128 || STORE_DS ? 1 : (DQ ? 2 : 3)) void bwd_dkdv_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
