@@ -217,6 +217,26 @@ def test_stages_equal_fused_backward(la):
     torch.testing.assert_close(g, ref, rtol=1e-5, atol=1e-5)
 
 
+def test_prepare_clears_dq_only(la):
+    """attn_backward_prepare writes D (the same bits attn_backward_preprocess
+    writes) and zeros over the dq third of dqkv, and leaves the dk and dv
+    thirds as they were."""
+    B, T, C, NH = 2, 97, 128, 2
+    _case(f"f32 prepare B{B} T{T} C{C} NH{NH}")
+    qkv_c, dout_c = make_inputs(B, T, C, "f32", seed=35)
+    qkv, dout = qkv_c.cuda(), dout_c.cuda()
+    out, _ = la.forward(qkv, NH, True)
+    g = torch.full_like(qkv, float("nan"))
+    D = torch.full((B, NH, T), float("nan"), device="cuda")
+    D2 = torch.full((B, NH, T), float("nan"), device="cuda")
+    la.attn_backward_prepare(g, D, dout, out, B, T, C, NH)
+    la.attn_backward_preprocess(D2, dout, out, B, T, C, NH)
+    torch.cuda.synchronize()
+    assert torch.equal(D, D2)
+    assert torch.equal(g[:, :, :C], torch.zeros_like(g[:, :, :C]))
+    assert torch.isnan(g[:, :, C:]).all()
+
+
 def test_dkdvdq_adds_into_dq(la, oracle_mod):
     """attn_backward_dkdvdq adds its dq into the dq third and overwrites dk
     and dv: run twice after one attn_backward_prepare, dq is twice the
