@@ -350,14 +350,15 @@ __global__ __launch_bounds__(kThreads) void prepass_f32_kernel(float* __restrict
 // With STORE_DS it also writes each 64x64 block of dS (unscaled) to the dS
 // block store, for the dQ kernel that consumes it (bwd_dq_ds_f32_tile).
 // With DQ it also forms dQ: each Q tile's dS block goes through LDS (dSt,
-// query rows), and during the next Q tile's step every wave multiplies its
-// 16 query rows of it by the key tile (Kt, held transposed and scaled for
-// the whole loop) and adds the 16 x HS result into dqkv's dQ slot with
-// global float atomics.  The slot must be cleared first (the pre-pass does
-// it), and the order of the additions, hence dQ's last bits, varies from run
-// to run.  The atomics of a step are issued before the next Q tile's
-// prefetch: the compiler makes the wait for those loads also cover every
-// store issued before them, which then has a whole step to complete.
+// query rows), and at the start of the next Q tile's step every wave
+// multiplies its 16 query rows of it by the key tile (Kt, held transposed
+// and scaled for the whole loop); it adds the 16 x HS result into dqkv's dQ
+// slot with global float atomics spread over that step's 16-query blocks
+// (~1% faster than issuing them together).  The slot must be cleared first
+// (the pre-pass does it), and the order of the additions, hence dQ's last
+// bits, varies from run to run.  The compiler makes the wait for the next
+// tile's prefetched loads also cover every store issued before it; the last
+// atomics of a step leave a 16-query block of work before that wait.
 template <int HS, bool STORE_DS, bool DQ = false>
 __device__ __forceinline__ void bwd_dkdv_f32_tile(
     int tile_, int bh_, float* __restrict__ dqkv, float* __restrict__ dsw,
@@ -441,12 +442,13 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
     [[maybe_unused]] const bool kv_in = kvrow < T;
     [[maybe_unused]] const bool kv_full = (kt + 1) * kTile <= T;   // no key of the tile past T
     // DQ: dQ rows qtp*64 + 16w + 4g + i, columns 16mb + r16 from dSt and Kt
-    // (the contraction runs over the tile's keys 16g + 4c + j in lane group g)
+    // (the contraction runs over the tile's keys 16g + 4c + j in lane group
+    // g) into dacc; dq_add then adds row group i of it to dqkv
     [[maybe_unused]] float* dqbase = dqkv + (size_t)b * T * C3 + (size_t)h * HS;
-    [[maybe_unused]] auto dq_product = [&](int qtp) {
-        f32x4 acc[MB];
+    [[maybe_unused]] f32x4 dacc[MB];
+    [[maybe_unused]] auto dq_product = [&]() {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < MB; ++mb) dacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         const float* ar = dSt + (16 * L.w + L.r16) * LDT + 16 * L.g;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -457,22 +459,21 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
                 b4[mb] = *reinterpret_cast<const float4*>(Kt + (16 * mb + L.r16) * LDT + 16 * L.g +
                                                           4 * c);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.x, b4[mb].x, acc[mb]);
+            for (int mb = 0; mb < MB; ++mb) dacc[mb] = mfma_f32(a4.x, b4[mb].x, dacc[mb]);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.y, b4[mb].y, acc[mb]);
+            for (int mb = 0; mb < MB; ++mb) dacc[mb] = mfma_f32(a4.y, b4[mb].y, dacc[mb]);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.z, b4[mb].z, acc[mb]);
+            for (int mb = 0; mb < MB; ++mb) dacc[mb] = mfma_f32(a4.z, b4[mb].z, dacc[mb]);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_f32(a4.w, b4[mb].w, acc[mb]);
+            for (int mb = 0; mb < MB; ++mb) dacc[mb] = mfma_f32(a4.w, b4[mb].w, dacc[mb]);
         }
-        const int q0 = qtp * kTile + 16 * L.w + 4 * L.g;
+    };
+    [[maybe_unused]] auto dq_add = [&](int qtp, int i) {
+        const int q = qtp * kTile + 16 * L.w + 4 * L.g + i;
+        if (q < T) {
+            float* row = dqbase + (size_t)q * C3 + L.r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (q0 + i < T) {
-                float* row = dqbase + (size_t)(q0 + i) * C3 + L.r16;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) unsafeAtomicAdd(row + 16 * mb, acc[mb][i]);
-            }
+            for (int mb = 0; mb < MB; ++mb) unsafeAtomicAdd(row + 16 * mb, dacc[mb][i]);
         }
     };
     for (int qt = qt0; qt < nt; ++qt) {
@@ -487,7 +488,7 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
         if constexpr (DQ) {
             // the previous Q tile's dS is complete (first barrier); this
             // step's dS writes come after the second barrier
-            if (qt > qt0) dq_product(qt - 1);
+            if (qt > qt0) dq_product();
             if (qt + 1 < nt) fetch(qt + 1);
             __syncthreads();
         } else {
@@ -563,6 +564,15 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
             if constexpr (DQ) {   // entry (query 16n + 4g + i, key 16w + r16)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dSt[(16 * n + 4 * L.g + i) * LDT + 16 * L.w + L.r16] = ds[i];
+                // the previous Q tile's dQ atomics, spread over this step
+                // (the last two groups after its third 16-query block)
+                if (qt > qt0) {
+                    if (n < 2) dq_add(qt - 1, n);
+                    if (n == 2) {
+                        dq_add(qt - 1, 2);
+                        dq_add(qt - 1, 3);
+                    }
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -580,7 +590,9 @@ __device__ __forceinline__ void bwd_dkdv_f32_tile(
 
     if constexpr (DQ) {
         __syncthreads();
-        dq_product(nt - 1);
+        dq_product();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dq_add(nt - 1, i);
     }
     if (kvrow < T) {
         float* dkrow = dqkv + ((size_t)b * T + kvrow) * C3 + C + (size_t)h * HS;
@@ -827,7 +839,7 @@ __global__ __launch_bounds__(kThreads, HS >= 128 ? 2 : 3) void fwd_f32_kernel(fl
 // hs <= 64 without the dS store: three workgroups per CU (162 VGPRs; the
 // compiler's own choice was 174, two per CU): GPT-2 layer dK/dV 220 -> 214
 // us, same bits.  With the store the same cap spills.  With DQ the LDS
-// (68.5 KB at hs = 64) allows two per CU, and 218 VGPRs fit that.
+// (68.5 KB at hs = 64) allows two per CU, and 216 VGPRs fit that.
 template <int HS, bool STORE_DS, bool DQ = false>
 __global__ __launch_bounds__(kThreads, HS >= 128 || STORE_DS ? 1 : (DQ ? 2 : 3)) void bwd_dkdv_f32_kernel(
     float* __restrict__ dqkv, float* __restrict__ dsw, const float* __restrict__ dout,
