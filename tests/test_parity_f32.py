@@ -65,6 +65,26 @@ def test_ragged_shapes(la, oracle_mod, shape, causal):
     assert_close(dqkv, rd, "f32", "dqkv")
 
 
+TILE_EDGE_SHAPES = [(1, 64, 64, 4), (1, 128, 512, 4), (2, 192, 64, 4), (1, 256, 512, 4),
+                    (1, 191, 256, 4), (1, 257, 64, 1)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", TILE_EDGE_SHAPES)
+def test_tile_edge_lengths(la, oracle_mod, shape, causal):
+    """T at and next to multiples of the 64-row tile (the last tile full,
+    one row short, one row over), hs = 16, 64 and 128."""
+    B, T, C, NH = shape
+    _case(f"f32 tile edge B{B} T{T} C{C} NH{NH} causal={causal}")
+    qkv, dout = make_inputs(B, T, C, "f32", seed=300 + T)
+    out, lse, dqkv = gpu_fwd_bwd(la, qkv, dout, NH, causal)
+    ro, rl = oracle_mod.forward(qkv, NH, causal)
+    rd = oracle_mod.backward(qkv, dout, NH, causal)
+    assert_close(out, ro, "f32", "out")
+    assert_close(lse, rl, "f32", "lse")
+    assert_close(dqkv, rd, "f32", "dqkv")
+
+
 def test_gpt2_layer_all_heads(la, oracle_mod):
     """The benchmark's workload (B8 T1024 C768 NH12, causal, fp32) in the
     benchmark's launch configuration; every element of every head is
