@@ -30,6 +30,10 @@ SHAPES = [
     (1, 200, 256, 4),   # hs 64, ragged
     (2, 150, 256, 2),   # hs 128, ragged
     (1, 260, 512, 4),   # hs 128, five tiles
+    (1, 384, 256, 4),   # hs 64, three full 128-row forward tiles (two-kernel backward)
+    (1, 383, 512, 4),   # hs 128, one row short of them
+    (1, 385, 256, 4),   # hs 64, one row over
+    (1, 512, 128, 8),   # hs 16, four full forward tiles
 ]
 
 
