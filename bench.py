@@ -65,10 +65,12 @@ def parse_args():
                         "time has passed since the first one: the kernels reach their steady "
                         "speed only after ~30 ms (fp32) to ~70 ms (bf16) of work, whatever "
                         "the step count")
-    p.add_argument("--workload", type=int, default=3)
-    # f32_rc / f32_ds: the fp32 step through the recompute-order or the dS
-    # block store stage calls instead of attn_backward's
-    p.add_argument("--dtype", choices=["f32", "f32_rc", "f32_ds", "bf16", "f16"], default=None)
+    p.add_argument("--workload", type=int, default=3,
+                   help="workload key in workloads.py (3: the GPT-2 layer, the headline)")
+    p.add_argument("--dtype", choices=["f32", "f32_rc", "f32_ds", "bf16", "f16"], default=None,
+                   help="the step's dtype (default: the workload's); f32_rc and f32_ds time the "
+                        "fp32 step through the recompute-order or the dS block store stage calls "
+                        "instead of attn_backward's")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="CPU seconds the oracle baseline may spend on its sample")
